@@ -1,0 +1,18 @@
+"""CPU oracle for low-rank-KV decode attention (float64 NumPy + decimal brute force).
+
+TEST INFRASTRUCTURE.  Only `tests/`, `__graft_entry__.smoke()` and the
+benchmark's CPU-baseline leg may import anything under `oracle/`.  The product
+path (the HIP library and its Python binding) never imports it and has no CPU
+fallback.
+
+Modules
+  lowrank_decode  the plain definition: dequantize, rebuild K and V
+                  explicitly, dense softmax attention, in float64
+  brute           the same definition in 40-digit decimal, nested loops,
+                  for tiny inputs
+
+Parity status: every function is pinned (see the CPU tests); none is
+"parity unpinned".
+"""
+from .lowrank_decode import (as_float64, attend, decode, decode_absorbed,  # noqa: F401
+                             decode_rows, dequantize, rebuild)
