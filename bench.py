@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark over a per-head low-rank KV cache on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config gqa_vlm]
+
+One step = one lrattn_decode call (partition kernel + combine kernel) over
+one batch: every query head of every sequence attends to its whole cached
+context once, i.e. one decode token per sequence for one attention layer.
+Inputs are seeded synthetic tensors with the workload's shapes and value
+distributions, resident in HBM before timing starts.
+
+Printed: one JSON line.  `value` = decode tokens/s = B * K / (wall time of K
+steps), bracketed by device synchronization.  `roofline` describes the
+dominant (partition) kernel: algorithmic bytes per launch / mean launch time
+measured with HIP events on the launch stream.  `cpu_baseline` times the fp64
+CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X published HBM3E bandwidth
+ROTATE_BYTES = 1 << 30       # rotate input copies so the 256 MB MALL cannot hold them
+WORKLOAD_TEXT = {
+    "tiny": "tiny: B=1 H=4 d=64 r=16 T=256 fp32",
+    "llm7b": "7B-LLM-like decode: B=8 H=32 d=128 r=32 T=4096 bf16",
+    "gqa_vlm": "GQA VLM long prompt: B=16 Hq=32 Hkv=8 d=128 r=64 T=16384 (576 image + text) bf16",
+    "int8": "int8 latents: B=32 H=32 d=128 r=32 T=8192, fp32 per-token scales, bf16 q/factors",
+    "ragged": "ragged long context: B=4 H=40 d=128 r=48 T<=131072 bf16",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="gqa_vlm",
+                    choices=["tiny", "llm7b", "gqa_vlm", "int8", "ragged"])
+    ap.add_argument("--num-splits", type=int, default=0, help="0 = library heuristic")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe", action="store_true",
+                    help="also run the HBM read/copy probe kernels (calibration)")
+    return ap.parse_args()
+
+
+def device_tensors(w, torch, copies):
+    import numpy as np
+
+    def t(a, tag):
+        if tag == "bf16":
+            x = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+        else:
+            x = torch.from_numpy(np.ascontiguousarray(a))
+        return x.cuda()
+
+    base = dict(q=t(w.q, w.q_dtype), B_K=t(w.B_K, w.factor_dtype), B_V=t(w.B_V, w.factor_dtype),
+                seq_lens=torch.from_numpy(w.seq_lens.astype(np.int32)).cuda())
+    sets = []
+    lk = t(w.L_K, w.latent_dtype)
+    lv = t(w.L_V, w.latent_dtype)
+    sc = None if w.scales is None else torch.from_numpy(w.scales).cuda()
+    for i in range(copies):
+        if i == 0:
+            sets.append((lk, lv, sc))
+        else:
+            sets.append((lk.clone(), lv.clone(), None if sc is None else sc.clone()))
+    return base, sets
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for name in ("lrattn_kernels.hip", "lrattn_internal.hpp"):
+        with open(os.path.join(ROOT, "rank_kv_cache_head_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(config: str, per_launch_alg: float):
+    """HBM bytes per partition launch from committed rocprofv3 counter runs.
+
+    Null when no counter file exists for this workload or the kernel source has
+    changed since the counters were taken.
+    """
+    path = os.path.join(ROOT, "profiles", f"partition_{config}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha") != kernel_source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, gpu_out, seconds: float):
+    """Time the fp64 oracle on whole sequences of the workload until `seconds` pass."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = ",".join(sorted({i.get("internal_api", "?") for i in threadpool_info()}))
+    except Exception:  # pragma: no cover
+        threads, blas = os.cpu_count(), "?"
+    q = oracle.as_float64(w.q, w.q_dtype)
+    BK = oracle.as_float64(w.B_K, w.factor_dtype)
+    BV = oracle.as_float64(w.B_V, w.factor_dtype)
+    G = w.group
+    done = 0
+    err = 0.0
+    t0 = time.perf_counter()
+    for b in range(w.batch):
+        n = int(w.seq_lens[b])
+        for g in range(w.num_kv_heads):
+            LK = oracle.as_float64(w.L_K[b:b + 1, g:g + 1, :n], w.latent_dtype)
+            LV = oracle.as_float64(w.L_V[b:b + 1, g:g + 1, :n], w.latent_dtype)
+            sc = None if w.scales is None else w.scales[:, b:b + 1, g:g + 1, :n].astype(np.float64)
+            rows = [(0, h) for h in range(G)]
+            ref = oracle.decode_rows(q[b:b + 1, g * G:(g + 1) * G], LK, LV, BK[g:g + 1],
+                                     BV[g:g + 1], np.array([n]), rows, scales=sc)
+            got = gpu_out[b, g * G:(g + 1) * G]
+            e = np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)
+            err = max(err, float(e.max()))
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=done / dt, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{done} of {w.batch} sequences (all {w.num_q_heads} heads each), "
+                       f"fp64 NumPy rebuild-then-attend, {dt:.1f} s, BLAS {blas}",
+                seconds=dt, max_rel_err_vs_gpu=err)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path is "
+              "single-GPU, sharding across GPUs is described in the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import workloads
+    import rank_kv_cache_head_amd as lr
+
+    lr.lib()  # fail loudly if the library is missing
+    t_gen = time.perf_counter()
+    w = workloads.make(args.config)
+    ab = w.algorithmic_bytes()
+    gen_s = time.perf_counter() - t_gen
+    lat_bytes = ab["latents"] + ab["scales"]
+    copies = max(1, min(8, math.ceil(ROTATE_BYTES / max(1, lat_bytes))))
+    base, sets = device_tensors(w, torch, copies)
+    p = lr.params_for(base["q"], sets[0][0], base["B_K"], num_splits=args.num_splits)
+    P, S = lr.plan(p)
+    ws = torch.empty(lr.workspace_size(p), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        lk, lv, sc = sets[i % copies]
+        lr.decode(base["q"], lk, lv, base["B_K"], base["B_V"], base["seq_lens"], sc,
+                  out=out, workspace=ws, num_splits=args.num_splits)
+
+    def part(i):
+        lk, lv, sc = sets[i % copies]
+        lr.partition(base["q"], lk, lv, base["B_K"], base["seq_lens"], sc, workspace=ws,
+                     num_splits=args.num_splits)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole decode steps
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    gpu_out = out.cpu().numpy().astype(np.float64)
+
+    # ---- dominant kernel alone: K partition launches, HIP events on its stream
+    for i in range(min(args.warmup, 5)):
+        part(i)
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        pev[i][0].record()
+        part(i)
+        pev[i][1].record()
+    torch.cuda.synchronize()
+    part_ms = np.array([a.elapsed_time(b) for a, b in pev])
+    part_mean_s = float(part_ms.mean()) / 1e3
+
+    # algorithmic bytes of the partition kernel per launch: valid latent rows
+    # (K and V), their int8 scales, q and B_K
+    part_bytes = ab["latents"] + ab["scales"] + ab["q"] + w.B_K.nbytes
+    achieved = part_bytes / part_mean_s / 1e9
+    traffic = load_traffic(args.config, part_bytes)
+
+    ms_per_step = wall / K * 1e3
+    line = {
+        "metric": "decode attention tokens/s per GPU + achieved HBM GB/s vs ~8 TB/s peak",
+        "value": w.batch * K / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded, workload shapes and distributions)",
+        "config": {
+            "workload": WORKLOAD_TEXT[args.config],
+            "name": args.config,
+            "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "rank": w.rank, "max_seq_len": w.max_seq_len,
+            "valid_tokens": ab["valid_tokens"], "storage": w.latent_dtype,
+            "num_splits": P, "split_tokens": S, "input_copies_rotated": copies,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "kernel": "partition_kernel",
+            "mean_launch_us": part_mean_s * 1e6,
+            "algorithmic_bytes_per_launch": part_bytes,
+        },
+        "step_hbm_GBps_algorithmic": ab["total"] / (ms_per_step / 1e3) / 1e9,
+        "step_event_ms_median": float(np.median(step_ms)),
+        "step_event_ms_min": float(step_ms.min()),
+        "input_generation_s": gen_s,
+    }
+    if args.probe:
+        line["probe"] = run_probe(torch, lr)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, gpu_out, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+def run_probe(torch, lr):
+    """Attainable streaming read/copy bandwidth (1 GiB buffers, rotated)."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(2)
+    sink = torch.empty(lr.probe_sink_floats(), dtype=torch.float32, device="cuda")
+    res = {}
+    for name, fn, moved in (("read", lambda: lr.probe_read(a, sink), n),
+                            ("copy", lambda: lr.probe_copy(b, a), 2 * n)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"{name}_GBps"] = moved * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+/*
+ * lrattn.h - single-token decode attention over a per-head low-rank KV cache
+ *            (gfx950 / MI355X, HIP).
+ *
+ * THE OPERATION
+ *   WSVD page ("WSVD: Weighted Low-Rank Approximation for Fast and Efficient
+ *   Execution of Low-Precision Vision-Language Models"), section 2.A: every
+ *   head's key (and value) projection is factored per head with rank r, so
+ *   the cache keeps a compact latent row per token and head, and each head's
+ *   K (V) is rebuilt from its own latent times its own r x d factor.
+ *   Section 2.C: the decode kernel fuses that rebuild with attention and Flash
+ *   Decoding in one flow, keeping intermediates on chip.  AttentionPack page,
+ *   section 2.C: the decompression is folded into the attention-score
+ *   computation so less data crosses between HBM and on-chip memory.
+ *
+ *   For every sequence b < B and query head h < Hq, with kv-head
+ *   g = h / (Hq / Hkv) and n = seq_lens[b]:
+ *
+ *     Lk[t] = L_K[b,g,t,:]           (times scales[0,b,g,t] for int8 latents)
+ *     Lv[t] = L_V[b,g,t,:]           (times scales[1,b,g,t] for int8 latents)
+ *     K[t]  = Lk[t] . B_K[g]         V[t] = Lv[t] . B_V[g]          t < n
+ *     p     = softmax_t( softmax_scale * <q[b,h,:], K[t]> )
+ *     out[b,h,:] = sum_t p[t] V[t]
+ *
+ *   The library never forms K or V.  By associativity it scores
+ *   (q . B_K^T) . Lk[t] and projects (sum_t p[t] Lv[t]) . B_V, the same
+ *   quantity, streaming 2r latent values per token and kv-head instead of 2d.
+ *   Flash Decoding: the token axis is cut into num_splits partitions; each
+ *   produces (running max, exp-sum, unnormalized latent accumulator) and a
+ *   second kernel merges them with a log-sum-exp rule in fixed order.
+ *
+ * TENSORS (all row-major, contiguous, device memory of the stream's device)
+ *   q        [B, Hq, d]            q_dtype       (F32, BF16 or F16)
+ *   L_K, L_V [B, Hkv, T, r]        latent_dtype  (F32, BF16, F16 or I8)
+ *   B_K, B_V [Hkv, r, d]           factor_dtype  (F32, BF16 or F16)
+ *   scales   [2, B, Hkv, T] fp32   index 0 scales K latents, 1 scales V
+ *                                  latents; required iff latent_dtype == I8,
+ *                                  must be NULL otherwise
+ *   seq_lens [B] int32             valid tokens per sequence, read on the
+ *                                  device only.  Values above T are treated
+ *                                  as T; values <= 0 produce a zero output row
+ *                                  (attention over no tokens is undefined).
+ *                                  Rows t >= seq_lens[b] are never read.
+ *   out      [B, Hq, d]            out_dtype     (F32 or BF16)
+ *   T is params.max_seq_len (the token stride of L_K, L_V and scales).
+ *
+ * SUPPORTED SHAPES
+ *   head_dim d in {64, 128, 256}; rank r in {16, 32, 48, 64, 128} with
+ *   r * sizeof(latent) <= 256 bytes (so r = 128 needs 1- or 2-byte latents);
+ *   group Hq / Hkv in {1, 2, 4, 8}; batch and Hkv <= 65535.
+ *   Anything else returns LRATTN_ERR_UNSUPPORTED before any device work.
+ *
+ * ALIGNMENT
+ *   Every tensor pointer and the workspace must be 16-byte aligned.
+ *
+ * OWNERSHIP AND EXECUTION
+ *   The caller owns every buffer, including the workspace (size from
+ *   lrattn_workspace_size).  The library allocates nothing, frees nothing and
+ *   keeps no pointer after a call returns.  Calls are asynchronous on `stream`
+ *   (NULL = the null stream of the current device), never synchronize the host
+ *   and read seq_lens only on the device, so they can be captured in a HIP
+ *   graph.  The library holds no state: concurrent calls are safe as long as
+ *   they do not share a workspace or output buffer.
+ *
+ * ERRORS
+ *   Every entry point returns LRATTN_OK (0) or a negative lrattn_status.  All
+ *   argument errors are detected on the host before anything is launched,
+ *   and `out` and the workspace are left untouched.  LRATTN_ERR_HIP reports a
+ *   failed launch (the HIP error is consumed from hipGetLastError).
+ *
+ * RESULTS
+ *   Scores, softmax and accumulation run in fp32 on exactly-converted inputs.
+ *   For a fixed num_splits, build and device, results are bitwise identical
+ *   from run to run (fixed reduction order, no atomics).
+ */
+#ifndef LRATTN_H
+#define LRATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t* lrattn_stream;
+
+typedef enum lrattn_dtype {
+  LRATTN_F32 = 0,
+  LRATTN_BF16 = 1,
+  LRATTN_F16 = 2,
+  LRATTN_I8 = 3
+} lrattn_dtype;
+
+typedef enum lrattn_status {
+  LRATTN_OK = 0,
+  LRATTN_ERR_NULL = -1,        /* a required pointer is NULL, or scales given for float latents */
+  LRATTN_ERR_SHAPE = -2,       /* a size is <= 0, Hq not a multiple of Hkv, or sizes overflow */
+  LRATTN_ERR_DTYPE = -3,       /* a dtype code outside lrattn_dtype, or not allowed for that tensor */
+  LRATTN_ERR_UNSUPPORTED = -4, /* valid request outside the compiled shape set */
+  LRATTN_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
+  LRATTN_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than lrattn_workspace_size */
+  LRATTN_ERR_SPLITS = -7,      /* num_splits < 0 or > max_seq_len */
+  LRATTN_ERR_HIP = -8          /* a kernel launch failed */
+} lrattn_status;
+
+typedef struct lrattn_params {
+  int32_t batch;         /* B */
+  int32_t num_q_heads;   /* Hq */
+  int32_t num_kv_heads;  /* Hkv, divides Hq */
+  int32_t head_dim;      /* d */
+  int32_t rank;          /* r */
+  int32_t max_seq_len;   /* T: token capacity (stride) of the latent cache */
+  int32_t q_dtype;       /* lrattn_dtype of q */
+  int32_t latent_dtype;  /* lrattn_dtype of L_K and L_V */
+  int32_t factor_dtype;  /* lrattn_dtype of B_K and B_V */
+  int32_t out_dtype;     /* lrattn_dtype of out: LRATTN_F32 or LRATTN_BF16 */
+  float softmax_scale;   /* logit multiplier; <= 0 selects 1/sqrt(head_dim) */
+  int32_t num_splits;    /* Flash-Decoding partitions over T per (b, kv-head);
+                            0 lets the library choose (see lrattn_plan) */
+} lrattn_params;
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int lrattn_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* lrattn_status_string(int status);
+
+/*
+ * Host-only.  Validates `p` and resolves the partition plan:
+ * *num_splits = partitions per (b, kv-head) actually used, *split_tokens =
+ * tokens per partition (partition i covers [i*split_tokens,
+ * (i+1)*split_tokens) intersected with [0, seq_len)).  Either output may be
+ * NULL.
+ */
+int lrattn_plan(const lrattn_params* p, int32_t* num_splits, int32_t* split_tokens);
+
+/*
+ * Host-only.  Bytes of device workspace lrattn_decode needs for `p`:
+ * B * Hq * num_splits * (r + 4) * 4 (one fp32 partial record per query head
+ * and partition), rounded up to 256.
+ */
+int lrattn_workspace_size(const lrattn_params* p, size_t* bytes);
+
+/*
+ * The decode step: partition kernel then combine kernel, both on `stream`.
+ * `workspace` holds workspace_bytes >= lrattn_workspace_size(p) bytes; its
+ * contents on entry do not matter and are scratch afterwards.
+ */
+int lrattn_decode(const lrattn_params* p,
+                  const void* q,
+                  const void* L_K,
+                  const void* L_V,
+                  const void* B_K,
+                  const void* B_V,
+                  const float* scales,
+                  const int32_t* seq_lens,
+                  void* out,
+                  void* workspace,
+                  size_t workspace_bytes,
+                  lrattn_stream stream);
+
+/*
+ * First half of lrattn_decode alone (for measurement and testing): absorb
+ * q . B_K^T, stream the latents, write one partial record per (b, query head,
+ * non-empty partition) into the workspace.  Records of partitions that lie
+ * past seq_len are not written.
+ */
+int lrattn_partition(const lrattn_params* p,
+                     const void* q,
+                     const void* L_K,
+                     const void* L_V,
+                     const void* B_K,
+                     const float* scales,
+                     const int32_t* seq_lens,
+                     void* workspace,
+                     size_t workspace_bytes,
+                     lrattn_stream stream);
+
+/*
+ * Second half of lrattn_decode alone: merge the partial records left by
+ * lrattn_partition (same p, seq_lens and workspace) and project through B_V.
+ */
+int lrattn_combine(const lrattn_params* p,
+                   const void* B_V,
+                   const int32_t* seq_lens,
+                   void* out,
+                   void* workspace,
+                   size_t workspace_bytes,
+                   lrattn_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRATTN_H */

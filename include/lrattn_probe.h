@@ -1,0 +1,40 @@
+/*
+ * lrattn_probe.h - plain HBM streaming kernels shipped beside lrattn for
+ * measurement: the attainable read / copy bandwidth of the device, and a copy
+ * of known size against which hardware byte counters are calibrated.  They
+ * compute nothing of the attention method.
+ *
+ * Same conventions as lrattn.h: device pointers, 16-byte aligned, caller-owned,
+ * asynchronous on `stream`, negative lrattn_status on error, host-side
+ * validation before any launch.
+ */
+#ifndef LRATTN_PROBE_H
+#define LRATTN_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lrattn.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Number of fp32 values lrattn_probe_read writes to its sink. */
+size_t lrattn_probe_sink_floats(void);
+
+/*
+ * Read `bytes` bytes (a multiple of 16) from `src` with 16-byte loads and
+ * write one fp32 per workgroup to `sink` (lrattn_probe_sink_floats() values)
+ * so the loads cannot be removed.  Bytes moved: `bytes` read, a few KB written.
+ */
+int lrattn_probe_read(const void* src, size_t bytes, float* sink, lrattn_stream stream);
+
+/* Copy `bytes` bytes (a multiple of 16) from `src` to `dst` (no overlap). */
+int lrattn_probe_copy(void* dst, const void* src, size_t bytes, lrattn_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRATTN_PROBE_H */

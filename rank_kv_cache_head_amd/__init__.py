@@ -1,0 +1,261 @@
+"""Python binding of liblrattn: decode attention over a per-head low-rank KV cache.
+
+Thin ctypes layer over the C-ABI declared in include/lrattn.h and
+include/lrattn_probe.h.  It only marshals arguments: it reads shapes and
+dtypes from torch tensors, passes their device pointers and the current HIP
+stream, and raises LrattnError on a nonzero status.  Every step of the
+computation runs in the library's gfx950 kernels; there is no fallback, and
+a missing library raises at first use.
+
+    out = decode(q, L_K, L_V, B_K, B_V, seq_lens, scales=None, ...)
+
+Shapes: q [B, Hq, d]; L_K, L_V [B, Hkv, T, r]; B_K, B_V [Hkv, r, d];
+scales [2, B, Hkv, T] fp32 (int8 latents only); seq_lens [B] int32.  All on
+the same GPU, contiguous.  See include/lrattn.h for the operation, supported
+shapes and error behaviour.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+__all__ = [
+    "LrattnError", "Params", "lib", "library_path", "version", "status_string",
+    "params_for", "plan", "workspace_size", "decode", "partition", "combine",
+    "probe_read", "probe_copy", "probe_sink_floats", "declared_symbols",
+    "F32", "BF16", "F16", "I8",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_ROOT = os.path.dirname(_PKG)
+F32, BF16, F16, I8 = 0, 1, 2, 3
+
+STATUS = {0: "LRATTN_OK", -1: "LRATTN_ERR_NULL", -2: "LRATTN_ERR_SHAPE",
+          -3: "LRATTN_ERR_DTYPE", -4: "LRATTN_ERR_UNSUPPORTED", -5: "LRATTN_ERR_ALIGN",
+          -6: "LRATTN_ERR_WORKSPACE", -7: "LRATTN_ERR_SPLITS", -8: "LRATTN_ERR_HIP"}
+
+
+class LrattnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("q_dtype", ctypes.c_int32), ("latent_dtype", ctypes.c_int32),
+                ("factor_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("num_splits", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return os.environ.get("LRATTN_LIBRARY", os.path.join(_PKG, "liblrattn.so"))
+
+
+_LIB = None
+_VP = ctypes.c_void_p
+_PP = ctypes.POINTER(Params)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded liblrattn.so (built by rank_kv_cache_head_amd.build)."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise ImportError(
+                f"liblrattn.so not found at {path}: build it with "
+                "`python -m rank_kv_cache_head_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(path)
+        L.lrattn_version.restype = ctypes.c_int
+        L.lrattn_status_string.restype = ctypes.c_char_p
+        L.lrattn_status_string.argtypes = [ctypes.c_int]
+        L.lrattn_plan.argtypes = [_PP, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+        L.lrattn_workspace_size.argtypes = [_PP, ctypes.POINTER(ctypes.c_size_t)]
+        L.lrattn_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                    ctypes.c_size_t, _VP]
+        L.lrattn_partition.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                       ctypes.c_size_t, _VP]
+        L.lrattn_combine.argtypes = [_PP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]
+        L.lrattn_probe_sink_floats.restype = ctypes.c_size_t
+        L.lrattn_probe_read.argtypes = [_VP, ctypes.c_size_t, _VP, _VP]
+        L.lrattn_probe_copy.argtypes = [_VP, _VP, ctypes.c_size_t, _VP]
+        for fn in ("lrattn_plan", "lrattn_workspace_size", "lrattn_decode", "lrattn_partition",
+                   "lrattn_combine", "lrattn_probe_read", "lrattn_probe_copy"):
+            getattr(L, fn).restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def declared_symbols():
+    """Every function name declared in include/*.h (for export checks)."""
+    names = []
+    inc = os.path.join(_ROOT, "include")
+    for fn in sorted(os.listdir(inc)):
+        if fn.endswith(".h"):
+            text = open(os.path.join(inc, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(lrattn_\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+def version() -> int:
+    return lib().lrattn_version()
+
+
+def status_string(status: int) -> str:
+    try:
+        return lib().lrattn_status_string(int(status)).decode()
+    except ImportError:
+        return STATUS.get(status, "unknown")
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise LrattnError(status, where)
+
+
+# ------------------------------------------------------------ torch glue
+
+def _dtype_code(t) -> int:
+    import torch
+    m = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16, torch.int8: I8}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def params_for(q, L_K, B_K, *, out_dtype=None, softmax_scale=None, num_splits: int = 0) -> Params:
+    """Parameter block for tensors q [B,Hq,d], L_K [B,Hkv,T,r], B_K [Hkv,r,d]."""
+    import torch
+    if q.dim() != 3 or L_K.dim() != 4 or B_K.dim() != 3:
+        raise ValueError("q [B,Hq,d], L [B,Hkv,T,r], B [Hkv,r,d] expected")
+    B, Hq, d = q.shape
+    B2, Hkv, T, r = L_K.shape
+    if B2 != B or tuple(B_K.shape) != (Hkv, r, d):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} L {tuple(L_K.shape)} "
+                         f"B {tuple(B_K.shape)}")
+    od = F32 if out_dtype in (None, torch.float32) else (BF16 if out_dtype == torch.bfloat16 else -1)
+    return Params(B, Hq, Hkv, d, r, T, _dtype_code(q), _dtype_code(L_K), _dtype_code(B_K), od,
+                  float(softmax_scale) if softmax_scale else 0.0, int(num_splits))
+
+
+def plan(p: Params) -> Tuple[int, int]:
+    """(partitions per (b, kv-head), tokens per partition) the library will use."""
+    n = ctypes.c_int32()
+    s = ctypes.c_int32()
+    _check(lib().lrattn_plan(ctypes.byref(p), ctypes.byref(n), ctypes.byref(s)), "lrattn_plan")
+    return n.value, s.value
+
+
+def workspace_size(p: Params) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().lrattn_workspace_size(ctypes.byref(p), ctypes.byref(b)), "lrattn_workspace_size")
+    return b.value
+
+
+def _workspace(p: Params, workspace, device):
+    import torch
+    need = workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _check_shapes(p: Params, L_V, B_V, scales, seq_lens):
+    if tuple(L_V.shape) != (p.batch, p.num_kv_heads, p.max_seq_len, p.rank):
+        raise ValueError("L_V shape differs from L_K")
+    if B_V is not None and tuple(B_V.shape) != (p.num_kv_heads, p.rank, p.head_dim):
+        raise ValueError("B_V shape differs from B_K")
+    if scales is not None and tuple(scales.shape) != (2, p.batch, p.num_kv_heads, p.max_seq_len):
+        raise ValueError("scales must be [2, B, Hkv, T]")
+    if tuple(seq_lens.shape) != (p.batch,):
+        raise ValueError("seq_lens must be [B]")
+    import torch
+    if seq_lens.dtype != torch.int32 or (scales is not None and scales.dtype != torch.float32):
+        raise TypeError("seq_lens must be int32 and scales float32")
+
+
+def decode(q, L_K, L_V, B_K, B_V, seq_lens, scales=None, *, out=None, workspace=None,
+           softmax_scale=None, num_splits: int = 0, out_dtype=None, stream=None):
+    """lrattn_decode on torch tensors; returns `out` [B, Hq, d] (fp32 unless out_dtype)."""
+    import torch
+    p = params_for(q, L_K, B_K, out_dtype=out_dtype, softmax_scale=softmax_scale,
+                   num_splits=num_splits)
+    _check_shapes(p, L_V, B_V, scales, seq_lens)
+    if out is None:
+        out = torch.empty((p.batch, p.num_q_heads, p.head_dim),
+                          dtype=torch.float32 if p.out_dtype == F32 else torch.bfloat16,
+                          device=q.device)
+    ws, ws_bytes = _workspace(p, workspace, q.device)
+    st = lib().lrattn_decode(ctypes.byref(p), _ptr(q), _ptr(L_K), _ptr(L_V), _ptr(B_K), _ptr(B_V),
+                             _ptr(scales), _ptr(seq_lens), _ptr(out), _ptr(ws), ws_bytes,
+                             _stream(stream))
+    _check(st, "lrattn_decode")
+    return out
+
+
+def partition(q, L_K, L_V, B_K, seq_lens, scales=None, *, workspace=None, softmax_scale=None,
+              num_splits: int = 0, stream=None):
+    """lrattn_partition alone; returns the workspace tensor holding the partials."""
+    p = params_for(q, L_K, B_K, softmax_scale=softmax_scale, num_splits=num_splits)
+    _check_shapes(p, L_V, None, scales, seq_lens)
+    ws, ws_bytes = _workspace(p, workspace, q.device)
+    st = lib().lrattn_partition(ctypes.byref(p), _ptr(q), _ptr(L_K), _ptr(L_V), _ptr(B_K),
+                                _ptr(scales), _ptr(seq_lens), _ptr(ws), ws_bytes, _stream(stream))
+    _check(st, "lrattn_partition")
+    return ws
+
+
+def combine(p: Params, B_V, seq_lens, workspace, *, out=None, stream=None):
+    """lrattn_combine alone, on the workspace a matching partition() call filled."""
+    import torch
+    if out is None:
+        out = torch.empty((p.batch, p.num_q_heads, p.head_dim),
+                          dtype=torch.float32 if p.out_dtype == F32 else torch.bfloat16,
+                          device=B_V.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().lrattn_combine(ctypes.byref(p), _ptr(B_V), _ptr(seq_lens), _ptr(out),
+                              _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "lrattn_combine")
+    return out
+
+
+def probe_sink_floats() -> int:
+    return lib().lrattn_probe_sink_floats()
+
+
+def probe_read(src, sink, stream=None) -> None:
+    """Stream-read every byte of `src` (HBM bandwidth probe)."""
+    nbytes = src.numel() * src.element_size()
+    _check(lib().lrattn_probe_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)),
+           "lrattn_probe_read")
+
+
+def probe_copy(dst, src, stream=None) -> None:
+    """Copy `src` into `dst` (same byte size) with 16-byte loads and stores."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst smaller than src")
+    _check(lib().lrattn_probe_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)),
+           "lrattn_probe_copy")

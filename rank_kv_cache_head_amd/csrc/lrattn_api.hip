@@ -1,0 +1,263 @@
+// C-ABI host layer of liblrattn: argument validation, the partition plan,
+// workspace sizing and kernel launches.  Every argument error is detected here,
+// on the host, before any HIP call, so a rejected call has no device effect.
+#include <math.h>
+#include <initializer_list>
+#include <stdint.h>
+#include <string.h>
+
+#include "lrattn.h"
+#include "lrattn_internal.hpp"
+#include "lrattn_probe.h"
+
+namespace {
+
+using lrattn::kRecPad;
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+// Partition plan: at least kMinSplitTokens tokens per partition and, when the
+// caller leaves num_splits at 0, enough (b, kv-head, partition) workgroups to
+// cover the 256 compute units several times over.
+constexpr int kTargetBlocks = 2048;
+constexpr int kMinSplitTokens = 256;
+
+int esize(int dt) {
+  switch (dt) {
+    case LRATTN_F32: return 4;
+    case LRATTN_BF16: case LRATTN_F16: return 2;
+    case LRATTN_I8: return 1;
+    default: return 0;
+  }
+}
+
+bool is_float_dtype(int dt) { return dt == LRATTN_F32 || dt == LRATTN_BF16 || dt == LRATTN_F16; }
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Product of positive factors, or -1 when it would pass 2^62.
+int64_t checked_mul(std::initializer_list<int64_t> xs) {
+  int64_t r = 1;
+  for (int64_t x : xs) {
+    if (x <= 0) return -1;
+    if (r > (int64_t(1) << 62) / x) return -1;
+    r *= x;
+  }
+  return r;
+}
+
+struct Plan {
+  int32_t P;  // partitions per (b, kv-head)
+  int32_t S;  // tokens per partition
+};
+
+// Validates the parameter block alone (no pointers).
+int check_params(const lrattn_params* p, Plan* plan) {
+  if (!p) return LRATTN_ERR_NULL;
+  if (p->batch <= 0 || p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->head_dim <= 0 ||
+      p->rank <= 0 || p->max_seq_len <= 0)
+    return LRATTN_ERR_SHAPE;
+  if (p->num_q_heads % p->num_kv_heads) return LRATTN_ERR_SHAPE;
+  if (!is_float_dtype(p->q_dtype) || esize(p->latent_dtype) == 0 ||
+      !is_float_dtype(p->factor_dtype) ||
+      (p->out_dtype != LRATTN_F32 && p->out_dtype != LRATTN_BF16))
+    return LRATTN_ERR_DTYPE;
+  if (checked_mul({p->batch, p->num_kv_heads, p->max_seq_len, p->rank, 4}) < 0 ||
+      checked_mul({p->batch, p->num_q_heads, p->head_dim, 4}) < 0)
+    return LRATTN_ERR_SHAPE;
+  if (!(isfinite(p->softmax_scale))) return LRATTN_ERR_SHAPE;
+  const int group = p->num_q_heads / p->num_kv_heads;
+  const int d = p->head_dim;
+  if (!(d == 64 || d == 128 || d == 256)) return LRATTN_ERR_UNSUPPORTED;
+  if (!lrattn::partition_supported(p->latent_dtype, p->rank, group)) return LRATTN_ERR_UNSUPPORTED;
+  if (p->batch > 65535 || p->num_kv_heads > 65535) return LRATTN_ERR_UNSUPPORTED;
+  if (p->num_splits < 0 || p->num_splits > p->max_seq_len) return LRATTN_ERR_SPLITS;
+
+  const int64_t T = p->max_seq_len;
+  int64_t splits = p->num_splits;
+  if (splits == 0) {
+    const int64_t pairs = (int64_t)p->batch * p->num_kv_heads;
+    const int64_t want = (kTargetBlocks + pairs - 1) / pairs;
+    const int64_t cap = (T + kMinSplitTokens - 1) / kMinSplitTokens;
+    splits = want < cap ? want : cap;
+    if (splits < 1) splits = 1;
+  }
+  const int64_t S = (T + splits - 1) / splits;
+  const int64_t P = (T + S - 1) / S;
+  // byte offsets inside one partition stay below 2^30 (buffer addressing)
+  if (S * p->rank * esize(p->latent_dtype) >= (int64_t(1) << 30)) return LRATTN_ERR_UNSUPPORTED;
+  if (P > 2147483647LL) return LRATTN_ERR_UNSUPPORTED;
+  if (checked_mul({p->batch, p->num_q_heads, P, p->rank + kRecPad, 4}) < 0) return LRATTN_ERR_SHAPE;
+  if (plan) { plan->P = (int32_t)P; plan->S = (int32_t)S; }
+  return LRATTN_OK;
+}
+
+size_t workspace_bytes_for(const lrattn_params* p, const Plan& pl) {
+  const size_t bytes = (size_t)p->batch * p->num_q_heads * (size_t)pl.P *
+                       (size_t)(p->rank + kRecPad) * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+float qscale_for(const lrattn_params* p) {
+  const float scale = p->softmax_scale > 0.f ? p->softmax_scale
+                                             : (float)(1.0 / sqrt((double)p->head_dim));
+  return (float)((double)scale * 1.4426950408889634);  // log2(e): logits in base 2
+}
+
+int check_workspace(const lrattn_params* p, const Plan& pl, const void* ws, size_t ws_bytes) {
+  if (!ws) return LRATTN_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LRATTN_ERR_ALIGN;
+  if (ws_bytes < workspace_bytes_for(p, pl)) return LRATTN_ERR_WORKSPACE;
+  return LRATTN_OK;
+}
+
+int check_partition_ptrs(const lrattn_params* p, const void* q, const void* LK, const void* LV,
+                         const void* BK, const float* scales, const int32_t* seq_lens) {
+  if (!q || !LK || !LV || !BK || !seq_lens) return LRATTN_ERR_NULL;
+  const bool int8 = p->latent_dtype == LRATTN_I8;
+  if (int8 != (scales != nullptr)) return LRATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(LK) || !aligned16(LV) || !aligned16(BK) ||
+      !aligned16(seq_lens) || (scales && !aligned16(scales)))
+    return LRATTN_ERR_ALIGN;
+  return LRATTN_OK;
+}
+
+int check_combine_ptrs(const void* BV, const int32_t* seq_lens, const void* out) {
+  if (!BV || !seq_lens || !out) return LRATTN_ERR_NULL;
+  if (!aligned16(BV) || !aligned16(seq_lens) || !aligned16(out)) return LRATTN_ERR_ALIGN;
+  return LRATTN_OK;
+}
+
+lrattn::PartitionArgs partition_args(const lrattn_params* p, const Plan& pl, const void* q,
+                                     const void* LK, const void* LV, const void* BK,
+                                     const float* scales, const int32_t* seq_lens, void* ws) {
+  lrattn::PartitionArgs a;
+  a.q = q; a.LK = LK; a.LV = LV; a.BK = BK; a.scales = scales; a.seq_lens = seq_lens;
+  a.ws = static_cast<float*>(ws);
+  a.B = p->batch; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.d = p->head_dim;
+  a.T = p->max_seq_len; a.P = pl.P; a.S = pl.S;
+  a.q_dtype = p->q_dtype; a.f_dtype = p->factor_dtype;
+  a.qscale = qscale_for(p);
+  return a;
+}
+
+lrattn::CombineArgs combine_args(const lrattn_params* p, const Plan& pl, const void* BV,
+                                 const int32_t* seq_lens, void* out, const void* ws) {
+  lrattn::CombineArgs a;
+  a.BV = BV; a.seq_lens = seq_lens; a.ws = static_cast<const float*>(ws); a.out = out;
+  a.B = p->batch; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.d = p->head_dim;
+  a.r = p->rank; a.T = p->max_seq_len; a.P = pl.P; a.S = pl.S;
+  a.f_dtype = p->factor_dtype; a.out_dtype = p->out_dtype;
+  return a;
+}
+
+int group_of(const lrattn_params* p) { return p->num_q_heads / p->num_kv_heads; }
+
+}  // namespace
+
+extern "C" {
+
+int lrattn_version(void) { return kVersion; }
+
+const char* lrattn_status_string(int status) {
+  switch (status) {
+    case LRATTN_OK: return "ok";
+    case LRATTN_ERR_NULL: return "null pointer (or scales given for non-int8 latents)";
+    case LRATTN_ERR_SHAPE: return "invalid shape";
+    case LRATTN_ERR_DTYPE: return "invalid dtype";
+    case LRATTN_ERR_UNSUPPORTED: return "unsupported shape/dtype combination";
+    case LRATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case LRATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case LRATTN_ERR_SPLITS: return "num_splits out of range";
+    case LRATTN_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int lrattn_plan(const lrattn_params* p, int32_t* num_splits, int32_t* split_tokens) {
+  Plan pl;
+  const int st = check_params(p, &pl);
+  if (st != LRATTN_OK) return st;
+  if (num_splits) *num_splits = pl.P;
+  if (split_tokens) *split_tokens = pl.S;
+  return LRATTN_OK;
+}
+
+int lrattn_workspace_size(const lrattn_params* p, size_t* bytes) {
+  if (!bytes) return LRATTN_ERR_NULL;
+  Plan pl;
+  const int st = check_params(p, &pl);
+  if (st != LRATTN_OK) return st;
+  *bytes = workspace_bytes_for(p, pl);
+  return LRATTN_OK;
+}
+
+int lrattn_partition(const lrattn_params* p, const void* q, const void* L_K, const void* L_V,
+                     const void* B_K, const float* scales, const int32_t* seq_lens,
+                     void* workspace, size_t workspace_bytes, lrattn_stream stream) {
+  Plan pl;
+  int st = check_params(p, &pl);
+  if (st == LRATTN_OK) st = check_partition_ptrs(p, q, L_K, L_V, B_K, scales, seq_lens);
+  if (st == LRATTN_OK) st = check_workspace(p, pl, workspace, workspace_bytes);
+  if (st != LRATTN_OK) return st;
+  const auto a = partition_args(p, pl, q, L_K, L_V, B_K, scales, seq_lens, workspace);
+  if (lrattn::launch_partition(p->latent_dtype, p->rank, group_of(p), a,
+                               reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return LRATTN_ERR_HIP;
+  return LRATTN_OK;
+}
+
+int lrattn_combine(const lrattn_params* p, const void* B_V, const int32_t* seq_lens, void* out,
+                   void* workspace, size_t workspace_bytes, lrattn_stream stream) {
+  Plan pl;
+  int st = check_params(p, &pl);
+  if (st == LRATTN_OK) st = check_combine_ptrs(B_V, seq_lens, out);
+  if (st == LRATTN_OK) st = check_workspace(p, pl, workspace, workspace_bytes);
+  if (st != LRATTN_OK) return st;
+  const auto a = combine_args(p, pl, B_V, seq_lens, out, workspace);
+  if (lrattn::launch_combine(group_of(p), a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return LRATTN_ERR_HIP;
+  return LRATTN_OK;
+}
+
+int lrattn_decode(const lrattn_params* p, const void* q, const void* L_K, const void* L_V,
+                  const void* B_K, const void* B_V, const float* scales, const int32_t* seq_lens,
+                  void* out, void* workspace, size_t workspace_bytes, lrattn_stream stream) {
+  Plan pl;
+  int st = check_params(p, &pl);
+  if (st == LRATTN_OK) st = check_partition_ptrs(p, q, L_K, L_V, B_K, scales, seq_lens);
+  if (st == LRATTN_OK) st = check_combine_ptrs(B_V, seq_lens, out);
+  if (st == LRATTN_OK) st = check_workspace(p, pl, workspace, workspace_bytes);
+  if (st != LRATTN_OK) return st;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const auto pa = partition_args(p, pl, q, L_K, L_V, B_K, scales, seq_lens, workspace);
+  if (lrattn::launch_partition(p->latent_dtype, p->rank, group_of(p), pa, s) != hipSuccess)
+    return LRATTN_ERR_HIP;
+  const auto ca = combine_args(p, pl, B_V, seq_lens, out, workspace);
+  if (lrattn::launch_combine(group_of(p), ca, s) != hipSuccess) return LRATTN_ERR_HIP;
+  return LRATTN_OK;
+}
+
+size_t lrattn_probe_sink_floats(void) { return (size_t)lrattn::kProbeBlocks; }
+
+int lrattn_probe_read(const void* src, size_t bytes, float* sink, lrattn_stream stream) {
+  if (!src || !sink) return LRATTN_ERR_NULL;
+  if (bytes == 0 || bytes % 16) return LRATTN_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(sink)) return LRATTN_ERR_ALIGN;
+  if (lrattn::launch_probe_read(src, bytes, sink, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return LRATTN_ERR_HIP;
+  return LRATTN_OK;
+}
+
+int lrattn_probe_copy(void* dst, const void* src, size_t bytes, lrattn_stream stream) {
+  if (!src || !dst) return LRATTN_ERR_NULL;
+  if (bytes == 0 || bytes % 16) return LRATTN_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return LRATTN_ERR_ALIGN;
+  if (lrattn::launch_probe_copy(dst, src, bytes, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return LRATTN_ERR_HIP;
+  return LRATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Internal interface between the C-ABI host layer (lrattn_api.hip) and the
+// gfx950 kernels (lrattn_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lrattn.h"
+
+namespace lrattn {
+
+constexpr int kThreads = 256;   // 4 wave64 per workgroup
+constexpr int kWaves = kThreads / 64;
+constexpr int kRecPad = 4;      // partial record: r accumulators, max, sum, 2 pad
+constexpr int kMaxHeadDim = 256;
+constexpr int kMaxRank = 128;
+constexpr int kMaxGroup = 8;
+
+// One partial record per (b, query head, partition):
+//   rec[0..r)  sum_t 2^(s_t - m) * Lv[t]   (latent-space value accumulator)
+//   rec[r]     m   running max of the base-2 logits s_t
+//   rec[r+1]   l   sum_t 2^(s_t - m)
+// Base-2 logits: s_t = log2(e) * softmax_scale * <q, K[t]>, so 2^(s - m)
+// equals e^(logit - max logit).
+inline int record_floats(int rank) { return rank + kRecPad; }
+
+struct PartitionArgs {
+  const void* q;           // [B, Hq, d]
+  const void* LK;          // [B, Hkv, T, r]
+  const void* LV;          // [B, Hkv, T, r]
+  const void* BK;          // [Hkv, r, d]
+  const float* scales;     // [2, B, Hkv, T] or nullptr
+  const int32_t* seq_lens; // [B]
+  float* ws;               // [B, Hq, P, r + kRecPad]
+  int32_t B, Hq, Hkv, d, T;
+  int32_t P, S;            // partitions, tokens per partition
+  int32_t q_dtype, f_dtype;
+  float qscale;            // softmax_scale * log2(e)
+};
+
+struct CombineArgs {
+  const void* BV;          // [Hkv, r, d]
+  const int32_t* seq_lens; // [B]
+  const float* ws;         // [B, Hq, P, r + kRecPad]
+  void* out;               // [B, Hq, d]
+  int32_t B, Hq, Hkv, d, r, T;
+  int32_t P, S;
+  int32_t f_dtype, out_dtype;
+};
+
+// True when a partition kernel is compiled for (latent dtype, rank, group).
+bool partition_supported(int latent_dtype, int rank, int group);
+// Launch the partition grid (P, Hkv, B) on `s`.  Returns the launch error.
+hipError_t launch_partition(int latent_dtype, int rank, int group,
+                            const PartitionArgs& a, hipStream_t s);
+// Launch the combine grid (Hkv, B) on `s`.
+hipError_t launch_combine(int group, const CombineArgs& a, hipStream_t s);
+
+hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t s);
+hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+constexpr int kProbeBlocks = 4096;
+
+}  // namespace lrattn

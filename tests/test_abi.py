@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects bad arguments on the host before any device work.
+
+Every call below is made with arguments the host layer must reject, so no
+kernel is ever launched here (there is no GPU in the CPU suite).  Pointers are
+fake, never dereferenced: validation looks only at their values.
+"""
+import ctypes
+import math
+
+import pytest
+
+import rank_kv_cache_head_amd as lr
+
+ALIGNED = 0x10000          # a fake, 16-byte aligned device address
+MISALIGNED = 0x10004
+
+
+def params(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, rank=64, max_seq_len=1000,
+                q_dtype=lr.BF16, latent_dtype=lr.BF16, factor_dtype=lr.BF16, out_dtype=lr.F32,
+                softmax_scale=0.0, num_splits=0)
+    base.update(kw)
+    return lr.Params(**base)
+
+
+def decode_status(p, q=ALIGNED, lk=ALIGNED, lv=ALIGNED, bk=ALIGNED, bv=ALIGNED, scales=None,
+                  seq=ALIGNED, out=ALIGNED, ws=ALIGNED, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = 0        # too small: a fully valid call would otherwise launch
+    return lr.lib().lrattn_decode(ctypes.byref(p), q, lk, lv, bk, bv, scales, seq, out, ws,
+                                  ws_bytes, None)
+
+
+def test_library_loads_and_exports_everything_declared():
+    L = lr.lib()
+    names = lr.declared_symbols()
+    assert {"lrattn_decode", "lrattn_workspace_size", "lrattn_status_string", "lrattn_plan",
+            "lrattn_partition", "lrattn_combine", "lrattn_probe_read", "lrattn_probe_copy",
+            "lrattn_probe_sink_floats", "lrattn_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared but not exported"
+    assert lr.version() == 10000
+
+
+def test_status_strings():
+    for code in range(-8, 1):
+        assert lr.status_string(code) and lr.status_string(code) != "unknown status"
+    assert lr.status_string(-99) == "unknown status"
+
+
+def test_workspace_size_formula():
+    p = params(num_splits=7)
+    P, S = lr.plan(p)
+    assert S == math.ceil(1000 / 7) and P == math.ceil(1000 / S)
+    want = 2 * 8 * P * (64 + 4) * 4
+    assert lr.workspace_size(p) == (want + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("B,Hkv,T,exp_P", [
+    (1, 4, 256, 1),        # tiny: one partition per head
+    (8, 32, 4096, 8),      # 7B-like
+    (16, 8, 16384, 16),    # GQA VLM
+    (32, 32, 8192, 2),     # int8
+    (4, 40, 131072, 13),   # ragged
+])
+def test_default_plan(B, Hkv, T, exp_P):
+    p = params(batch=B, num_q_heads=Hkv, num_kv_heads=Hkv, max_seq_len=T, rank=32)
+    P, S = lr.plan(p)
+    assert P == exp_P and P * S >= T and (P - 1) * S < T and S >= min(256, T)
+
+
+def test_plan_explicit_splits():
+    for splits in (1, 2, 3, 256, 1000):
+        P, S = lr.plan(params(num_splits=splits))
+        assert P <= splits and P * S >= 1000 and (P - 1) * S < 1000
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), -2), (dict(num_q_heads=-1), -2), (dict(num_q_heads=7), -2),
+    (dict(max_seq_len=0), -2), (dict(rank=0), -2),
+    (dict(q_dtype=lr.I8), -3), (dict(latent_dtype=9), -3), (dict(factor_dtype=lr.I8), -3),
+    (dict(out_dtype=lr.F16), -3),
+    (dict(head_dim=96), -4), (dict(rank=24), -4), (dict(rank=128, latent_dtype=lr.F32), -4),
+    (dict(num_q_heads=6, num_kv_heads=2), -4), (dict(num_q_heads=32, num_kv_heads=2), -4),
+    (dict(batch=70000), -4),
+    (dict(num_splits=-1), -7), (dict(num_splits=1001), -7),
+    (dict(softmax_scale=float("nan")), -2),
+])
+def test_param_errors(kw, status):
+    p = params(**kw)
+    b = ctypes.c_size_t(12345)
+    assert lr.lib().lrattn_workspace_size(ctypes.byref(p), ctypes.byref(b)) == status
+    assert b.value == 12345  # untouched on error
+    assert decode_status(p) == status
+
+
+def test_pointer_errors():
+    p = params()
+    assert lr.lib().lrattn_workspace_size(None, None) == -1
+    assert decode_status(p, q=None) == -1
+    assert decode_status(p, lv=None) == -1
+    assert decode_status(p, bv=None) == -1
+    assert decode_status(p, seq=None) == -1
+    assert decode_status(p, out=None) == -1
+    assert decode_status(p, scales=ALIGNED) == -1                       # scales with bf16 latents
+    assert decode_status(params(latent_dtype=lr.I8, rank=32)) == -1     # int8 without scales
+    assert decode_status(p, q=MISALIGNED) == -5
+    assert decode_status(p, bk=MISALIGNED) == -5
+    assert decode_status(p, out=MISALIGNED) == -5
+    assert decode_status(p, ws=MISALIGNED) == -5
+    assert decode_status(params(latent_dtype=lr.I8, rank=32), scales=MISALIGNED) == -5
+    assert decode_status(p, ws=None) == -6
+    need = lr.workspace_size(p)
+    assert decode_status(p, ws_bytes=need - 1) == -6
+
+
+def test_partition_and_combine_validate_too():
+    p = params()
+    L = lr.lib()
+    assert L.lrattn_partition(ctypes.byref(p), None, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED,
+                              ALIGNED, 1 << 30, None) == -1
+    assert L.lrattn_partition(ctypes.byref(p), ALIGNED, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED,
+                              ALIGNED, 0, None) == -6
+    assert L.lrattn_combine(ctypes.byref(p), ALIGNED, ALIGNED, None, ALIGNED, 1 << 30, None) == -1
+    assert L.lrattn_combine(ctypes.byref(p), ALIGNED, ALIGNED, ALIGNED, ALIGNED, 0, None) == -6
+
+
+def test_probe_validation():
+    L = lr.lib()
+    assert lr.probe_sink_floats() >= 1024
+    assert L.lrattn_probe_read(None, 16, ALIGNED, None) == -1
+    assert L.lrattn_probe_read(ALIGNED, 15, ALIGNED, None) == -2
+    assert L.lrattn_probe_read(ALIGNED, 0, ALIGNED, None) == -2
+    assert L.lrattn_probe_copy(ALIGNED, MISALIGNED, 32, None) == -5
+
+
+def test_supported_matrix_plans():
+    # every compiled (latent dtype, rank, group) combination is accepted
+    for lt, esz in ((lr.F32, 4), (lr.BF16, 2), (lr.F16, 2), (lr.I8, 1)):
+        for r in (16, 32, 48, 64, 128):
+            for G in (1, 2, 4, 8):
+                for d in (64, 128, 256):
+                    p = params(latent_dtype=lt, rank=r, num_q_heads=2 * G, num_kv_heads=2,
+                               head_dim=d)
+                    b = ctypes.c_size_t()
+                    st = lr.lib().lrattn_workspace_size(ctypes.byref(p), ctypes.byref(b))
+                    assert st == (0 if r * esz <= 256 else -4), (lt, r, G, d)

@@ -1,0 +1,275 @@
+"""GPU parity: the HIP path (through the C-ABI) against the fp64 oracle.
+
+Gate: max over output rows of ||gpu - oracle||_inf / ||oracle||_inf <= 2e-3
+for bf16/fp16/int8 inputs and <= 1e-5 for fp32 inputs, with fp32 output.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from gpu_helpers import (TOL, f64_args, oracle_rows, rel_rowmax, run_decode, say, to_device)
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    # reduced sizes the oracle finishes in seconds; several partitions and a
+    # ragged tail in every case
+    "tiny": dict(),
+    "llm7b": dict(B=2, Hq=4, Hkv=4, T=1500, seq_lens=[1500, 1037]),
+    "gqa_vlm": dict(B=2, Hq=8, Hkv=2, T=2000, seq_lens=[2000, 1234]),
+    "int8": dict(B=2, Hq=4, Hkv=4, T=1800, seq_lens=[1800, 999]),
+    "ragged": dict(B=3, Hq=2, Hkv=2, T=6000, len_lo=1024, len_hi=6000),
+}
+
+
+def _full_oracle(w):
+    args = f64_args(w)
+    return oracle.decode(*args[:6], scales=args[6], softmax_scale=w.softmax_scale)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3, 7])
+@pytest.mark.parametrize("name", workloads.CONFIG_ORDER)
+def test_small_config(name, splits):
+    w = workloads.make(name, **SMALL[name])
+    say(f"small {name} splits={splits} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+        f"T={w.max_seq_len} r={w.rank} lens={list(w.seq_lens)}")
+    got = run_decode(w, num_splits=splits).cpu().numpy()
+    ref = _full_oracle(w)
+    err = rel_rowmax(got, ref)
+    say(f"  err {err:.3e}")
+    assert err <= TOL[w.latent_dtype], err
+
+
+def _sample_rows(w, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = {(0, 0), (w.batch - 1, w.num_q_heads - 1)}
+    while len(rows) < n:
+        rows.add((int(rng.integers(w.batch)), int(rng.integers(w.num_q_heads))))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", workloads.CONFIG_ORDER)
+def test_full_size(name):
+    """Full-size workload in the default launch configuration (the benchmark's)."""
+    say(f"full {name}: drawing inputs")
+    w = workloads.make(name)
+    say(f"full {name}: decode B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+        f"T={w.max_seq_len} r={w.rank}")
+    got = run_decode(w).cpu().numpy()
+    assert np.isfinite(got).all()
+    if name in ("tiny", "llm7b"):
+        ref = _full_oracle(w)
+        err = rel_rowmax(got, ref)
+    else:
+        rows = _sample_rows(w, 6, seed=1)
+        ref = oracle_rows(w, rows)
+        err = rel_rowmax(np.stack([got[b, h] for b, h in rows]), ref)
+    say(f"  err {err:.3e}")
+    assert err <= TOL[w.latent_dtype], err
+
+
+@pytest.mark.parametrize("name", ["ragged", "int8"])
+def test_nan_padding_never_read(name):
+    kw = dict(SMALL[name])
+    a = workloads.make(name, pad="zero", **kw)
+    b = workloads.make(name, pad="nan", **kw)
+    say(f"nan padding {name} lens={list(a.seq_lens)}")
+    oa = run_decode(a).cpu().numpy()
+    ob = run_decode(b).cpu().numpy()
+    assert np.isfinite(ob).all()
+    assert np.array_equal(oa, ob)
+
+
+@pytest.mark.parametrize("name", ["gqa_vlm", "int8", "ragged"])
+def test_bitwise_deterministic(name):
+    w = workloads.make(name, **SMALL[name])
+    dev = to_device(w)
+    say(f"determinism {name}")
+    first = run_decode(w, dev).cpu().numpy()
+    for _ in range(9):
+        assert np.array_equal(run_decode(w, dev).cpu().numpy(), first)
+
+
+def test_split_count_invariance():
+    w = workloads.make("gqa_vlm", B=1, Hq=4, Hkv=1, T=3000, seq_lens=[2999])
+    dev = to_device(w)
+    ref = _full_oracle(w)
+    outs = []
+    for splits in (1, 2, 5, 11, 64, 3000):
+        say(f"split invariance splits={splits}")
+        o = run_decode(w, dev, num_splits=splits).cpu().numpy()
+        assert rel_rowmax(o, ref) <= 2e-3
+        outs.append(o)
+    for o in outs[1:]:
+        assert rel_rowmax(o, outs[0]) <= 1e-5
+
+
+def test_lengths_on_partition_boundaries():
+    import rank_kv_cache_head_amd as lr
+    T = 1024
+    w0 = workloads.make("llm7b", B=1, Hq=2, Hkv=2, T=T)
+    dev0 = to_device(w0)
+    p = lr.params_for(dev0["q"], dev0["L_K"], dev0["B_K"], num_splits=8)
+    P, S = lr.plan(p)
+    assert S == 128
+    lens = [1, 2, S - 1, S, S + 1, 2 * S, 3 * S - 1, T - 1, T]
+    w = workloads.make("llm7b", B=len(lens), Hq=2, Hkv=2, T=T, seq_lens=lens)
+    say(f"partition boundaries S={S} lens={lens}")
+    got = run_decode(w, num_splits=8).cpu().numpy()
+    ref = _full_oracle(w)
+    assert rel_rowmax(got, ref) <= 2e-3
+
+
+def test_single_token_cache():
+    w = workloads.make("gqa_vlm", B=3, Hq=8, Hkv=2, T=1)
+    say("T=1 cache")
+    got = run_decode(w).cpu().numpy()
+    assert rel_rowmax(got, _full_oracle(w)) <= 2e-3
+
+
+def test_zero_negative_and_overlong_lengths():
+    import torch
+    w = workloads.make("llm7b", B=4, Hq=2, Hkv=2, T=300, seq_lens=[300, 300, 300, 300])
+    dev = to_device(w)
+    dev["seq_lens"] = torch.tensor([0, -5, 1000, 150], dtype=torch.int32, device="cuda")
+    say("zero / negative / overlong lengths")
+    got = run_decode(w, dev).cpu().numpy()
+    assert (got[0] == 0).all() and (got[1] == 0).all()
+    w2 = workloads.make("llm7b", B=4, Hq=2, Hkv=2, T=300, seq_lens=[300, 300, 300, 150])
+    ref = _full_oracle(w2)
+    assert rel_rowmax(got[2:], ref[2:]) <= 2e-3
+
+
+def test_bf16_output():
+    import torch
+    w = workloads.make("gqa_vlm", **SMALL["gqa_vlm"])
+    say("bf16 output")
+    out = run_decode(w, out_dtype=torch.bfloat16)
+    assert out.dtype == torch.bfloat16
+    got = out.float().cpu().numpy()
+    # bf16 rounding of the output alone costs up to 2^-9 of each value
+    assert rel_rowmax(got, _full_oracle(w)) <= 2e-3 + 2.0 ** -8
+
+
+def test_explicit_softmax_scale():
+    w = workloads.make("llm7b", B=2, Hq=2, Hkv=2, T=700)
+    w.softmax_scale = 0.02
+    say("explicit softmax scale")
+    got = run_decode(w).cpu().numpy()
+    assert rel_rowmax(got, _full_oracle(w)) <= 2e-3
+
+
+def _matrix():
+    cases = []
+    for lt in ("f32", "bf16", "f16", "i8"):
+        esz = {"f32": 4, "bf16": 2, "f16": 2, "i8": 1}[lt]
+        for r in (16, 32, 48, 64, 128):
+            if r * esz > 256:
+                continue
+            for G in (1, 2, 4, 8):
+                cases.append((lt, r, G, 128))
+    cases += [("bf16", 32, 1, 64), ("bf16", 64, 4, 256), ("f32", 16, 2, 256), ("i8", 64, 8, 64)]
+    return cases
+
+
+@pytest.mark.parametrize("lt,r,G,d", _matrix())
+def test_instantiation_matrix(lt, r, G, d):
+    base = "int8" if lt == "i8" else "tiny"
+    fdt = "f32" if lt == "f32" else ("f16" if lt == "f16" else "bf16")
+    kw = dict(B=2, Hq=2 * G, Hkv=2, d=d, r=r, T=700, seq_lens=[700, 333],
+              q_dtype=fdt, factor_dtype=fdt, factor_std=1.0 / np.sqrt(r))
+    if lt != "i8":
+        kw["latent_dtype"] = lt
+    w = workloads.make(base, seed=100 + r + G, **kw)
+    say(f"matrix latent={lt} r={r} G={G} d={d}")
+    got = run_decode(w, num_splits=3).cpu().numpy()
+    err = rel_rowmax(got, _full_oracle(w))
+    assert err <= TOL[lt], err
+
+
+def test_guard_bands_untouched():
+    import torch
+    import rank_kv_cache_head_amd as lr
+    w = workloads.make("ragged", **SMALL["ragged"])
+    dev = to_device(w)
+    p = lr.params_for(dev["q"], dev["L_K"], dev["B_K"])
+    need = lr.workspace_size(p)
+    n_out = w.batch * w.num_q_heads * w.head_dim
+    guard = 4096
+    out_buf = torch.full((n_out + 2 * guard,), 1234.5, dtype=torch.float32, device="cuda")
+    ws_buf = torch.full((need // 4 + 2 * guard,), -777.25, dtype=torch.float32, device="cuda")
+    out = out_buf[guard:guard + n_out].view(w.batch, w.num_q_heads, w.head_dim)
+    ws = ws_buf[guard:guard + need // 4]
+    say("guard bands")
+    lr.decode(dev["q"], dev["L_K"], dev["L_V"], dev["B_K"], dev["B_V"], dev["seq_lens"],
+              dev["scales"], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ob = out_buf.cpu().numpy()
+    wb = ws_buf.cpu().numpy()
+    assert (ob[:guard] == 1234.5).all() and (ob[guard + n_out:] == 1234.5).all()
+    assert (wb[:guard] == -777.25).all() and (wb[guard + need // 4:] == -777.25).all()
+    assert rel_rowmax(out.cpu().numpy(), _full_oracle(w)) <= 2e-3
+
+
+def test_partition_then_combine_equals_decode():
+    import torch
+    import rank_kv_cache_head_amd as lr
+    w = workloads.make("int8", **SMALL["int8"])
+    dev = to_device(w)
+    say("partition + combine")
+    ref = run_decode(w, dev, num_splits=5).cpu().numpy()
+    ws = lr.partition(dev["q"], dev["L_K"], dev["L_V"], dev["B_K"], dev["seq_lens"],
+                      dev["scales"], num_splits=5)
+    p = lr.params_for(dev["q"], dev["L_K"], dev["B_K"], num_splits=5)
+    out = lr.combine(p, dev["B_V"], dev["seq_lens"], ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_side_stream():
+    import torch
+    w = workloads.make("gqa_vlm", **SMALL["gqa_vlm"])
+    dev = to_device(w)
+    ref = run_decode(w, dev).cpu().numpy()
+    s = torch.cuda.Stream()
+    say("side stream")
+    import rank_kv_cache_head_amd as lr
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        out = lr.decode(dev["q"], dev["L_K"], dev["L_V"], dev["B_K"], dev["B_V"],
+                        dev["seq_lens"], dev["scales"])
+    s.synchronize()
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_host_errors_through_binding():
+    import torch
+    import rank_kv_cache_head_amd as lr
+    w = workloads.make("llm7b", B=1, Hq=2, Hkv=2, T=64)
+    dev = to_device(w)
+    say("binding errors")
+    big = torch.empty(dev["q"].numel() + 8, dtype=torch.bfloat16, device="cuda")
+    q_mis = big[1:1 + dev["q"].numel()].view_as(dev["q"])
+    with pytest.raises(lr.LrattnError) as e:
+        lr.decode(q_mis, dev["L_K"], dev["L_V"], dev["B_K"], dev["B_V"], dev["seq_lens"])
+    assert e.value.status == -5
+    with pytest.raises(lr.LrattnError) as e:
+        lr.decode(dev["q"], dev["L_K"], dev["L_V"], dev["B_K"], dev["B_V"], dev["seq_lens"],
+                  num_splits=65)
+    assert e.value.status == -7
+    with pytest.raises(ValueError):
+        lr.decode(dev["q"].cpu(), dev["L_K"], dev["L_V"], dev["B_K"], dev["B_V"], dev["seq_lens"])
+
+
+def test_probe_copy_and_read():
+    import torch
+    import rank_kv_cache_head_amd as lr
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (1 << 22,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    say("probe copy/read")
+    lr.probe_copy(dst, src)
+    sink = torch.empty(lr.probe_sink_floats(), dtype=torch.float32, device="cuda")
+    lr.probe_read(src, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
