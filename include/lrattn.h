@@ -26,8 +26,9 @@
  *   (q . B_K^T) . Lk[t] and projects (sum_t p[t] Lv[t]) . B_V, the same
  *   quantity, streaming 2r latent values per token and kv-head instead of 2d.
  *   Flash Decoding: the token axis is cut into num_splits partitions; each
- *   produces (running max, exp-sum, unnormalized latent accumulator) and a
- *   second kernel merges them with a log-sum-exp rule in fixed order.
+ *   produces (reference max, exp-sum, unnormalized latent accumulator), and a
+ *   second kernel merges the partitions of each (b, kv-head) with a
+ *   log-sum-exp rule in fixed order and applies B_V.
  *
  * TENSORS (all row-major, contiguous, device memory of the stream's device)
  *   q        [B, Hq, d]            q_dtype       (F32, BF16 or F16)
@@ -56,11 +57,11 @@
  * OWNERSHIP AND EXECUTION
  *   The caller owns every buffer, including the workspace (size from
  *   lrattn_workspace_size).  The library allocates nothing, frees nothing and
- *   keeps no pointer after a call returns.  Calls are asynchronous on `stream`
- *   (NULL = the null stream of the current device), never synchronize the host
- *   and read seq_lens only on the device, so they can be captured in a HIP
- *   graph.  The library holds no state: concurrent calls are safe as long as
- *   they do not share a workspace or output buffer.
+ *   keeps no pointer after a call returns.  Calls are asynchronous on
+ *   `stream` (NULL = the null stream of the current device), never
+ *   synchronize the host and read seq_lens only on the device, so they can be
+ *   captured in a HIP graph.  The library holds no state: concurrent calls
+ *   are safe as long as they do not share a workspace or output buffer.
  *
  * ERRORS
  *   Every entry point returns LRATTN_OK (0) or a negative lrattn_status.  All

@@ -24,7 +24,7 @@ from typing import Optional, Tuple
 __all__ = [
     "LrattnError", "Params", "lib", "library_path", "version", "status_string",
     "params_for", "plan", "workspace_size", "decode", "partition", "combine",
-    "probe_read", "probe_copy", "probe_sink_floats", "declared_symbols",
+    "probe_read", "probe_copy", "probe_sink_floats", "declared_symbols", "Decoder",
     "F32", "BF16", "F16", "I8",
 ]
 
@@ -259,3 +259,54 @@ def probe_copy(dst, src, stream=None) -> None:
         raise ValueError("dst smaller than src")
     _check(lib().lrattn_probe_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)),
            "lrattn_probe_copy")
+
+
+class Decoder:
+    """lrattn_decode / lrattn_partition / lrattn_combine on fixed buffers.
+
+    Arguments are validated and marshalled once; each call then passes the
+    same pointers and stream straight to the library (for loops that reuse
+    buffers, e.g. a decode loop or a benchmark).  The tensors must stay alive
+    and keep their storage while the object is used.
+    """
+
+    def __init__(self, q, L_K, L_V, B_K, B_V, seq_lens, scales=None, *, out=None,
+                 workspace=None, softmax_scale=None, num_splits: int = 0, out_dtype=None,
+                 stream=None):
+        import torch
+        p = params_for(q, L_K, B_K, out_dtype=out_dtype, softmax_scale=softmax_scale,
+                       num_splits=num_splits)
+        _check_shapes(p, L_V, B_V, scales, seq_lens)
+        if out is None:
+            out = torch.empty((p.batch, p.num_q_heads, p.head_dim),
+                              dtype=torch.float32 if p.out_dtype == F32 else torch.bfloat16,
+                              device=q.device)
+        ws, ws_bytes = _workspace(p, workspace, q.device)
+        self.params, self.out, self.workspace = p, out, ws
+        self.plan = plan(p)
+        self._keep = (q, L_K, L_V, B_K, B_V, seq_lens, scales)
+        st = _stream(stream)
+        pp = ctypes.byref(p)
+        L = lib()
+        self._decode = (L.lrattn_decode, (pp, _ptr(q), _ptr(L_K), _ptr(L_V), _ptr(B_K), _ptr(B_V),
+                                          _ptr(scales), _ptr(seq_lens), _ptr(out), _ptr(ws),
+                                          ws_bytes, st))
+        self._partition = (L.lrattn_partition, (pp, _ptr(q), _ptr(L_K), _ptr(L_V), _ptr(B_K),
+                                                _ptr(scales), _ptr(seq_lens), _ptr(ws), ws_bytes,
+                                                st))
+        self._combine = (L.lrattn_combine, (pp, _ptr(B_V), _ptr(seq_lens), _ptr(out), _ptr(ws),
+                                            ws_bytes, st))
+
+    def __call__(self):
+        fn, args = self._decode
+        _check(fn(*args), "lrattn_decode")
+        return self.out
+
+    def partition(self):
+        fn, args = self._partition
+        _check(fn(*args), "lrattn_partition")
+
+    def combine(self):
+        fn, args = self._combine
+        _check(fn(*args), "lrattn_combine")
+        return self.out

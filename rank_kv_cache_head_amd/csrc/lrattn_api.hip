@@ -93,9 +93,7 @@ int check_params(const lrattn_params* p, Plan* plan) {
 }
 
 size_t workspace_bytes_for(const lrattn_params* p, const Plan& pl) {
-  const size_t bytes = (size_t)p->batch * p->num_q_heads * (size_t)pl.P *
-                       (size_t)(p->rank + kRecPad) * sizeof(float);
-  return (bytes + 255) & ~(size_t)255;
+  return lrattn::records_bytes(p->batch, p->num_q_heads, pl.P, p->rank);
 }
 
 float qscale_for(const lrattn_params* p) {
@@ -128,6 +126,12 @@ int check_combine_ptrs(const void* BV, const int32_t* seq_lens, const void* out)
   return LRATTN_OK;
 }
 
+lrattn::MergeArgs merge_args(const lrattn_params* p, const void* BV, void* out) {
+  lrattn::MergeArgs m;
+  m.BV = BV; m.out = out; m.f_dtype = p->factor_dtype; m.out_dtype = p->out_dtype;
+  return m;
+}
+
 lrattn::PartitionArgs partition_args(const lrattn_params* p, const Plan& pl, const void* q,
                                      const void* LK, const void* LV, const void* BK,
                                      const float* scales, const int32_t* seq_lens, void* ws) {
@@ -142,12 +146,11 @@ lrattn::PartitionArgs partition_args(const lrattn_params* p, const Plan& pl, con
 }
 
 lrattn::CombineArgs combine_args(const lrattn_params* p, const Plan& pl, const void* BV,
-                                 const int32_t* seq_lens, void* out, const void* ws) {
+                                 const int32_t* seq_lens, void* out, void* ws) {
   lrattn::CombineArgs a;
-  a.BV = BV; a.seq_lens = seq_lens; a.ws = static_cast<const float*>(ws); a.out = out;
+  a.seq_lens = seq_lens; a.ws = static_cast<const float*>(ws); a.merge = merge_args(p, BV, out);
   a.B = p->batch; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.d = p->head_dim;
   a.r = p->rank; a.T = p->max_seq_len; a.P = pl.P; a.S = pl.S;
-  a.f_dtype = p->factor_dtype; a.out_dtype = p->out_dtype;
   return a;
 }
 

@@ -18,11 +18,24 @@ constexpr int kMaxGroup = 8;
 
 // One partial record per (b, query head, partition):
 //   rec[0..r)  sum_t 2^(s_t - m) * Lv[t]   (latent-space value accumulator)
-//   rec[r]     m   running max of the base-2 logits s_t
+//   rec[r]     m   reference max of the base-2 logits s_t
 //   rec[r+1]   l   sum_t 2^(s_t - m)
 // Base-2 logits: s_t = log2(e) * softmax_scale * <q, K[t]>, so 2^(s - m)
-// equals e^(logit - max logit).
+// equals e^(logit - reference logit).
 inline int record_floats(int rank) { return rank + kRecPad; }
+
+// Workspace: the partial records [B, Hq, P, r + kRecPad] fp32.
+inline size_t records_bytes(int B, int Hq, int P, int rank) {
+  const size_t b = (size_t)B * Hq * (size_t)P * (size_t)record_floats(rank) * sizeof(float);
+  return (b + 255) & ~(size_t)255;
+}
+
+// Where the merged rows go.
+struct MergeArgs {
+  const void* BV;          // [Hkv, r, d]
+  void* out;               // [B, Hq, d]
+  int32_t f_dtype, out_dtype;
+};
 
 struct PartitionArgs {
   const void* q;           // [B, Hq, d]
@@ -39,13 +52,11 @@ struct PartitionArgs {
 };
 
 struct CombineArgs {
-  const void* BV;          // [Hkv, r, d]
   const int32_t* seq_lens; // [B]
   const float* ws;         // [B, Hq, P, r + kRecPad]
-  void* out;               // [B, Hq, d]
+  MergeArgs merge;
   int32_t B, Hq, Hkv, d, r, T;
   int32_t P, S;
-  int32_t f_dtype, out_dtype;
 };
 
 // True when a partition kernel is compiled for (latent dtype, rank, group).
@@ -53,11 +64,11 @@ bool partition_supported(int latent_dtype, int rank, int group);
 // Launch the partition grid (P, Hkv, B) on `s`.  Returns the launch error.
 hipError_t launch_partition(int latent_dtype, int rank, int group,
                             const PartitionArgs& a, hipStream_t s);
-// Launch the combine grid (Hkv, B) on `s`.
+// Launch the combine grid (Hq, B) on `s`.
 hipError_t launch_combine(int group, const CombineArgs& a, hipStream_t s);
 
 hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t s);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
-constexpr int kProbeBlocks = 4096;
+constexpr int kProbeBlocks = 8192;
 
 }  // namespace lrattn

@@ -15,16 +15,17 @@
 //   the tokens [p*S, min((p+1)*S, seq_len)) of one (b, kv-head) and all G
 //   query heads of that kv-head, so each latent byte is read once for the
 //   whole group.
-//   combine grid (Hkv, B), 256 threads.
+//   combine grid (Hq, B), 256 threads.
 //
 // Lane mapping inside a wave (the hot loop):
-//   a latent row of r elements is kRowBytes bytes = kAct 16-byte pieces.
-//   kLPR (= kAct rounded up to a power of two) consecutive lanes form a "slot"
-//   that holds one row: lane cc of the slot loads bytes [16cc, 16cc+16).  A
-//   wave holds kRPW = 64 / kLPR slots, so one 16-byte load instruction covers
-//   kRPW consecutive rows = one contiguous span of memory.  Each slot runs its
-//   own online softmax (running max m, exp-sum l, accumulator) over the rows
-//   it sees; slots and waves are merged once, at the end of the partition.
+//   a latent row of r elements is kRowBytes bytes = kAct pieces of kVec bytes
+//   (16, or 8 for int8 latents with 4+ heads).  kLPR (= kAct rounded up to a
+//   power of two) consecutive lanes form a "slot" that holds one row: lane cc
+//   of the slot loads bytes [kVec*cc, kVec*(cc+1)).  A wave holds
+//   kRPW = 64 / kLPR slots, so one load instruction covers kRPW consecutive
+//   rows = one contiguous span of memory.  Each slot runs its own online
+//   softmax (reference max m, exp-sum l, accumulator) over the rows it sees;
+//   slots and waves are merged once, at the end of the partition.
 //   The per-row dot product is summed across the slot's lanes with DPP
 //   (quad_perm, row_half_mirror, row_mirror), which leaves the identical sum
 //   in every lane of the slot.
@@ -54,32 +55,36 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
-// 16 bytes of latent row -> 16 / kBytes fp32 values (every conversion exact).
+// kWords 32-bit words of a latent row -> fp32 values (every conversion exact).
 template <class LT> struct Unpack;
 template <> struct Unpack<LatF32> {
-  static __device__ __forceinline__ void run(const u32x4& v, float* x) {
+  template <int kWords>
+  static __device__ __forceinline__ void run(const uint32_t (&w)[kWords], float* x) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(v[k]);
+    for (int k = 0; k < kWords; ++k) x[k] = __uint_as_float(w[k]);
   }
 };
 template <> struct Unpack<LatBF16> {
-  static __device__ __forceinline__ void run(const u32x4& v, float* x) {
+  template <int kWords>
+  static __device__ __forceinline__ void run(const uint32_t (&w)[kWords], float* x) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) { x[2 * k] = bf16_lo(v[k]); x[2 * k + 1] = bf16_hi(v[k]); }
+    for (int k = 0; k < kWords; ++k) { x[2 * k] = bf16_lo(w[k]); x[2 * k + 1] = bf16_hi(w[k]); }
   }
 };
 template <> struct Unpack<LatF16> {
-  static __device__ __forceinline__ void run(const u32x4& v, float* x) {
+  template <int kWords>
+  static __device__ __forceinline__ void run(const uint32_t (&w)[kWords], float* x) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) { x[2 * k] = f16_lo(v[k]); x[2 * k + 1] = f16_hi(v[k]); }
+    for (int k = 0; k < kWords; ++k) { x[2 * k] = f16_lo(w[k]); x[2 * k + 1] = f16_hi(w[k]); }
   }
 };
 template <> struct Unpack<LatI8> {
-  static __device__ __forceinline__ void run(const u32x4& v, float* x) {
+  template <int kWords>
+  static __device__ __forceinline__ void run(const uint32_t (&w)[kWords], float* x) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kWords; ++k) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[4 * k + i] = (float)(int8_t)(v[k] >> (8 * i));
+      for (int i = 0; i < 4; ++i) x[4 * k + i] = (float)(int8_t)(w[k] >> (8 * i));
     }
   }
 };
@@ -129,9 +134,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-}
 __device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
@@ -158,60 +160,144 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Largest base-2 logit excess over the running reference max before the
+// reference is moved (weights stay <= 2^8).
+constexpr float kLazyLog2 = 8.0f;
+
 // ------------------------------------------------------------ partition
+// Compile-time tuning knobs (ordinary parameters; every setting computes the
+// same result):
+//   LRATTN_UNROLL_SMALL_G  rows per slot per step, 1-2 heads, 2- and 4-byte latents
+//   LRATTN_UNROLL_LARGE_G  rows per slot per step, 4-8 heads
+//   LRATTN_UNROLL_I8       rows per slot per step, 1-2 heads, int8 latents
+//   LRATTN_PREFETCH        1: load step i+1 while step i computes
+//   LRATTN_LOAD_AUX        cache-policy bits of the streaming latent loads;
+//                          2 = non-temporal: each latent byte is used once, so
+//                          it should not displace reusable lines in L2
+#ifndef LRATTN_UNROLL_SMALL_G
+#define LRATTN_UNROLL_SMALL_G 4
+#endif
+#ifndef LRATTN_UNROLL_LARGE_G
+#define LRATTN_UNROLL_LARGE_G 2
+#endif
+#ifndef LRATTN_UNROLL_I8
+#define LRATTN_UNROLL_I8 2
+#endif
+#ifndef LRATTN_PREFETCH
+#define LRATTN_PREFETCH 0
+#endif
+#ifndef LRATTN_LOAD_AUX
+#define LRATTN_LOAD_AUX 2
+#endif
+
 
 template <class LT, int R, int G>
 struct Geo {
   static constexpr int kRowBytes = R * LT::kBytes;
-  static constexpr int kEPL = 16 / LT::kBytes;            // elements per lane load
-  static constexpr int kAct = kRowBytes / 16;             // lanes carrying a row
+  // bytes per lane load: 16, or 8 for int8 latents with 4+ heads, whose 16
+  // values per lane would need 32+ registers per head for q~ and accumulators
+  static constexpr int kVec = (LT::kBytes == 1 && G >= 4 && kRowBytes >= 16) ? 8 : 16;
+  static constexpr int kWords = kVec / 4;
+  static constexpr int kEPL = kVec / LT::kBytes;          // elements per lane load
+  static constexpr int kAct = kRowBytes / kVec;           // lanes carrying a row
   static constexpr int kLPR = kAct <= 1 ? 1 : kAct <= 2 ? 2 : kAct <= 4 ? 4 : kAct <= 8 ? 8 : 16;
   static constexpr int kRPW = 64 / kLPR;                  // rows per wave load
-  static constexpr int kU = G >= 4 ? 2 : 4;               // rows per slot per step
+  // q~ and the accumulators take kEPL * G registers each; when that reaches
+  // 128 (int8 latents with 8 heads) q~ is read from LDS in the score loop
+  // instead of being held in registers, and one row per slot is processed
+  // per step.
+  static constexpr bool kQtInLds = kEPL * G >= 128;
+  static constexpr int kU = kQtInLds ? 1
+                           : G >= 4 ? LRATTN_UNROLL_LARGE_G
+                           : (LT::kBytes == 1 ? LRATTN_UNROLL_I8 : LRATTN_UNROLL_SMALL_G);
   static constexpr int kChunk = kU * kRPW;                // rows per wave per step
+  // Occupancy target (waves per SIMD) the register allocation must meet:
+  // 4 (<= 128 VGPRs) unless q~ plus accumulators alone need more than 64.
+  static constexpr int kWavesPerEU =
+      (kEPL * G <= 16 && kEPL * G * kU <= 32) || (kEPL * G <= 32 && R >= 64) ? 4 : 2;
   static_assert(kRowBytes % 16 == 0, "latent row must be whole 16-byte pieces");
-  static_assert(kAct <= 16, "latent row wider than 256 bytes");
+  static_assert(kAct <= 16, "latent row wider than 16 lane loads");
 };
 
-template <class LT, int R, int G, bool kMask>
-__device__ __forceinline__ void partition_step(
-    int cb, int ntok, int slot, uint32_t lane_off,
-    __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-    __amdgpu_buffer_rsrc_t rsk, __amdgpu_buffer_rsrc_t rsv,
-    const float (&qt)[G][Geo<LT, R, G>::kEPL], float (&m)[G], float (&l)[G],
-    float (&acc)[G][Geo<LT, R, G>::kEPL]) {
-  using Gm = Geo<LT, R, G>;
-  constexpr int EPL = Gm::kEPL, U = Gm::kU, RPW = Gm::kRPW;
-  constexpr bool kInt8 = std::is_same<LT, LatI8>::value;
+// One lane load of kWords 32-bit words (16 or 8 bytes), streaming cache policy.
+template <int kWords>
+__device__ __forceinline__ void load_words(uint32_t (&w)[kWords], __amdgpu_buffer_rsrc_t r,
+                                           uint32_t off) {
+  if constexpr (kWords == 4) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, LRATTN_LOAD_AUX);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+  } else {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, LRATTN_LOAD_AUX);
+    w[0] = v[0]; w[1] = v[1];
+  }
+}
 
-  u32x4 kv[U], vv[U];
-  float sk[U], sv[U];
+// The latent data of one step of one wave: kU rows per slot of K and of V
+// (and their int8 scales).
+template <class LT, int R, int G>
+struct Step {
+  uint32_t k[Geo<LT, R, G>::kU][Geo<LT, R, G>::kWords];
+  uint32_t v[Geo<LT, R, G>::kU][Geo<LT, R, G>::kWords];
+  float sk[Geo<LT, R, G>::kU];
+  float sv[Geo<LT, R, G>::kU];
+};
+
+template <class LT, int R, int G>
+__device__ __forceinline__ void load_step(Step<LT, R, G>& st, int cb, int slot, uint32_t lane_off,
+                                          __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                          __amdgpu_buffer_rsrc_t rsk, __amdgpu_buffer_rsrc_t rsv) {
+  using Gm = Geo<LT, R, G>;
+  constexpr int U = Gm::kU, RPW = Gm::kRPW;
 #pragma unroll
-  for (int u = 0; u < U; ++u) kv[u] = bload16(rk, (uint32_t)(cb + u * RPW) * Gm::kRowBytes + lane_off);
+  for (int u = 0; u < U; ++u)
+    load_words<Gm::kWords>(st.k[u], rk, (uint32_t)(cb + u * RPW) * Gm::kRowBytes + lane_off);
 #pragma unroll
-  for (int u = 0; u < U; ++u) vv[u] = bload16(rv, (uint32_t)(cb + u * RPW) * Gm::kRowBytes + lane_off);
-  if constexpr (kInt8) {
+  for (int u = 0; u < U; ++u)
+    load_words<Gm::kWords>(st.v[u], rv, (uint32_t)(cb + u * RPW) * Gm::kRowBytes + lane_off);
+  if constexpr (std::is_same<LT, LatI8>::value) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t so = (uint32_t)(cb + u * RPW + slot) * 4u;
-      sk[u] = bload4f(rsk, so);
-      sv[u] = bload4f(rsv, so);
+      st.sk[u] = bload4f(rsk, so);
+      st.sv[u] = bload4f(rsv, so);
     }
   }
+}
+
+// q~ of this lane's columns: registers, or (kQtInLds) LDS rows of stride R.
+template <class LT, int R, int G>
+struct QtView {
+  static constexpr bool kLds = Geo<LT, R, G>::kQtInLds;
+  float reg[kLds ? 1 : G][Geo<LT, R, G>::kEPL];
+  const float* lds;  // &qt_lds[cc * kEPL]
+  __device__ __forceinline__ float at(int h, int e) const {
+    if constexpr (kLds) return lds[h * R + e];
+    else return reg[h][e];
+  }
+};
+
+template <class LT, int R, int G, bool kMask>
+__device__ __forceinline__ void compute_step(
+    const Step<LT, R, G>& st, int cb, int ntok, int slot, const QtView<LT, R, G>& qt,
+    float (&m)[G], float (&l)[G], float (&acc)[G][Geo<LT, R, G>::kEPL]) {
+  using Gm = Geo<LT, R, G>;
+  constexpr int EPL = Gm::kEPL, U = Gm::kU, RPW = Gm::kRPW;
+  constexpr bool kInt8 = std::is_same<LT, LatI8>::value;
 
   // scores: s[u][h] = q~_h . Lk[row]   (base-2 logits)
   float s[U][G];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     float x[EPL];
-    Unpack<LT>::run(kv[u], x);
+    Unpack<LT>::run(st.k[u], x);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float t = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) t = fmaf(qt[h][e], x[e], t);
+      for (int e = 0; e < EPL; ++e) t = fmaf(qt.at(h, e), x[e], t);
       t = group_sum<Gm::kLPR>(t);
-      if constexpr (kInt8) t *= sk[u];
+      if constexpr (kInt8) t *= st.sk[u];
       if constexpr (kMask) {
         if (cb + u * RPW + slot >= ntok) t = -INFINITY;
       }
@@ -219,32 +305,50 @@ __device__ __forceinline__ void partition_step(
     }
   }
 
-  // online softmax per slot and head; w[u][h] = weight of row u
+  // online softmax per slot and head, with a lazily moved reference max: the
+  // running reference m only moves when a score exceeds it by more than
+  // kLazyLog2 (base-2 logits), so weights 2^(s - m) stay <= 2^kLazyLog2 and
+  // the accumulator rescale (and its exp) is skipped unless some lane of the
+  // wave needs it.  Any reference gives the same result: the record stores m
+  // with the sums taken relative to it.
+  float mx[G];
+  bool need = false;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    mx[h] = s[0][h];
+#pragma unroll
+    for (int u = 1; u < U; ++u) mx[h] = fmaxf(mx[h], s[u][h]);
+    need |= mx[h] > m[h] + kLazyLog2;
+  }
+  if (__builtin_amdgcn_ballot_w64(need)) {  // wave-uniform
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float nm = mx[h] > m[h] + kLazyLog2 ? mx[h] : m[h];
+      const float corr = fast_exp2(m[h] - nm);
+      l[h] *= corr;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= corr;
+      m[h] = nm;
+    }
+  }
   float w[U][G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float mx = m[h];
-#pragma unroll
-    for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[u][h]);
-    const float corr = fast_exp2(m[h] - mx);
     float es = 0.f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float e = fast_exp2(s[u][h] - mx);
+      const float e = fast_exp2(s[u][h] - m[h]);
       es += e;
-      w[u][h] = kInt8 ? e * sv[u] : e;
+      w[u][h] = kInt8 ? e * st.sv[u] : e;
     }
-    l[h] = fmaf(l[h], corr, es);
-    m[h] = mx;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] *= corr;
+    l[h] += es;
   }
 
   // latent-space value accumulation
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     float x[EPL];
-    Unpack<LT>::run(vv[u], x);
+    Unpack<LT>::run(st.v[u], x);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -253,24 +357,57 @@ __device__ __forceinline__ void partition_step(
   }
 }
 
+// Sum of `x` over aligned groups of n lanes, n in {8, 16, 32} (runtime, uniform).
+__device__ __forceinline__ float piece_sum(float x, int n) {
+  if (n <= 8) return group_sum<8>(x);
+  x = group_sum<16>(x);
+  if (n > 16) x += __shfl_xor(x, 16);
+  return x;
+}
+
+// ------------------------------------------------------------------ merge
+
+// Zero rows for a sequence with no valid token (attention over no tokens is
+// defined as a zero output).
+__device__ __forceinline__ void write_zero_rows(const MergeArgs& mg, size_t out_row0, int n) {
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    if (mg.out_dtype == LRATTN_F32) static_cast<float*>(mg.out)[out_row0 + i] = 0.f;
+    else static_cast<uint16_t*>(mg.out)[out_row0 + i] = 0;
+  }
+}
+
+// ------------------------------------------------------------ partition kernel
+
+template <int R, int G>
+struct PartLds {
+  float q[G * kMaxHeadDim];
+  float qt[G * R];
+  float acc[kWaves * G * R];
+  float m[kWaves * G];
+  float l[kWaves * G];
+};
+
 template <class LT, int R, int G>
-__global__ __launch_bounds__(kThreads) void partition_kernel(PartitionArgs a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(Geo<LT, R, G>::kWavesPerEU)))
+void partition_kernel(PartitionArgs a) {
   using Gm = Geo<LT, R, G>;
   constexpr int EPL = Gm::kEPL, LPR = Gm::kLPR, CH = Gm::kChunk;
   constexpr bool kInt8 = std::is_same<LT, LatI8>::value;
 
   const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int len = min(max(a.seq_lens[b], 0), a.T);
+  // seq_lens[b] is one value for the whole workgroup; keeping it in a scalar
+  // register keeps the buffer descriptors below scalar (a descriptor the
+  // compiler must treat as per-lane costs a readfirstlane loop per load)
+  const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
   const int t0 = p * a.S;
   const int t1 = min(t0 + a.S, len);
   if (t0 >= t1) return;  // partition past the sequence: nothing to write
   const int ntok = t1 - t0;
 
-  __shared__ float q_lds[G * kMaxHeadDim];
-  __shared__ float qt_lds[G * R];
-  __shared__ float red_acc[kWaves * G * R];
-  __shared__ float red_m[kWaves * G];
-  __shared__ float red_l[kWaves * G];
+  __shared__ PartLds<R, G> lds;
+  float* q_lds = lds.q;
+  float* qt_lds = lds.qt;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = lane / LPR, cc = lane % LPR;
@@ -287,45 +424,78 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(PartitionArgs a) {
     rsk = make_rsrc(a.scales + row0, (uint32_t)ntok * 4u);
     rsv = make_rsrc(a.scales + plane + row0, (uint32_t)ntok * 4u);
   }
-  const uint32_t lane_off = colact ? (uint32_t)(slot * Gm::kRowBytes + cc * 16) : kOffNone;
+  const uint32_t lane_off = colact ? (uint32_t)(slot * Gm::kRowBytes + cc * Gm::kVec) : kOffNone;
+
+  // The first step's latents are requested before the prologue, so their
+  // latency overlaps the absorption instead of following it.
+  Step<LT, R, G> cur;
+  load_step(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv);
 
   // ---- absorption: q~[h][j] = qscale * sum_i q[h][i] * B_K[g][j][i]
+  // All q and B_K loads of a thread are issued before any is used (one
+  // memory round trip); the G*d query values are contiguous.
   const int d = a.d;
-  for (int i = tid; i < G * d; i += kThreads) {
-    const int h = i / d, k = i - h * d;
-    q_lds[h * kMaxHeadDim + k] =
-        load_elem(a.q, ((size_t)b * a.Hq + (size_t)g * G + h) * d + k, a.q_dtype);
+  {
+    constexpr int kQPer = (G * kMaxHeadDim + kThreads - 1) / kThreads;
+    const size_t q0 = ((size_t)b * a.Hq + (size_t)g * G) * d;
+    float qv[kQPer];
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+      const int i = tid + k * kThreads;
+      qv[k] = i < G * d ? load_elem(a.q, q0 + i, a.q_dtype) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+      const int i = tid + k * kThreads;
+      if (i < G * d) {
+        const int h = i / d;
+        q_lds[h * kMaxHeadDim + (i - h * d)] = qv[k];
+      }
+    }
   }
   __syncthreads();
   const int nch = d >> 3;  // 8-element pieces per factor row; R * nch % 64 == 0
-  for (int it = tid; it < R * nch; it += kThreads) {
-    const int j = it / nch, c = it - j * nch;
-    float f[8];
-    load8(a.BK, ((size_t)g * R + j) * d + (size_t)c * 8, a.f_dtype, f);
-    float part[G];
+  // pieces per thread whose loads are in flight together: all of them for
+  // d = 128 and r <= 64
+  constexpr int kPieceBatch = R / 16 < 4 ? R / 16 : 4;
+  for (int base = 0; base < R * nch; base += kPieceBatch * kThreads) {
+    float f[kPieceBatch][8];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float t = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) t = fmaf(q_lds[h * kMaxHeadDim + c * 8 + k], f[k], t);
-      part[h] = t;
+    for (int k = 0; k < kPieceBatch; ++k) {
+      const int it = base + tid + k * kThreads;
+      if (it < R * nch) {
+        const int j = it / nch, c = it - j * nch;
+        load8(a.BK, ((size_t)g * R + j) * d + (size_t)c * 8, a.f_dtype, f[k]);
+      }
     }
-    for (int off = 1; off < nch; off <<= 1) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) part[h] += __shfl_xor(part[h], off);
-    }
-    if (c == 0) {
+    for (int k = 0; k < kPieceBatch; ++k) {
+      const int it = base + k * kThreads + (tid & ~63);  // wave-uniform guard
+      if (it < R * nch) {
+        const int itl = it + lane;
+        const int j = itl / nch, c = itl - j * nch;
 #pragma unroll
-      for (int h = 0; h < G; ++h) qt_lds[h * R + j] = part[h] * a.qscale;
+        for (int h = 0; h < G; ++h) {
+          float t = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t = fmaf(q_lds[h * kMaxHeadDim + c * 8 + e], f[k][e], t);
+          t = piece_sum(t, nch);
+          if (c == 0) qt_lds[h * R + j] = t * a.qscale;
+        }
+      }
     }
   }
   __syncthreads();
 
-  float qt[G][EPL];
+  QtView<LT, R, G> qt;
+  // idle lanes (cc >= kAct) load zeros, so their q~ is never read
+  qt.lds = qt_lds + (colact ? cc * EPL : 0);
+  if constexpr (!QtView<LT, R, G>::kLds) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < G; ++h) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qt[h][e] = colact ? qt_lds[h * R + cc * EPL + e] : 0.f;
+      for (int e = 0; e < EPL; ++e) qt.reg[h][e] = colact ? qt_lds[h * R + cc * EPL + e] : 0.f;
+    }
   }
 
   // ---- stream the partition
@@ -338,10 +508,21 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(PartitionArgs a) {
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
   for (int cb = wave * CH; cb < ntok; cb += kWaves * CH) {
+    Step<LT, R, G> nxt;
+    if constexpr (LRATTN_PREFETCH) {
+      // double buffering: step i+1 is in flight while step i computes; past
+      // the partition the loads return zero without touching memory
+      load_step(nxt, cb + kWaves * CH, slot, lane_off, rk, rv, rsk, rsv);
+    }
     if (cb + CH <= ntok)
-      partition_step<LT, R, G, false>(cb, ntok, slot, lane_off, rk, rv, rsk, rsv, qt, m, l, acc);
+      compute_step<LT, R, G, false>(cur, cb, ntok, slot, qt, m, l, acc);
     else
-      partition_step<LT, R, G, true>(cb, ntok, slot, lane_off, rk, rv, rsk, rsv, qt, m, l, acc);
+      compute_step<LT, R, G, true>(cur, cb, ntok, slot, qt, m, l, acc);
+    if constexpr (LRATTN_PREFETCH) {
+      cur = nxt;
+    } else {
+      load_step(cur, cb + kWaves * CH, slot, lane_off, rk, rv, rsk, rsv);
+    }
   }
 
   // ---- merge the slots of this wave (lanes with equal cc)
@@ -361,6 +542,7 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(PartitionArgs a) {
     m[h] = M;
     l[h] = L;
   }
+  float* red_acc = lds.acc;
   if (slot == 0 && colact) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -371,26 +553,27 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(PartitionArgs a) {
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      red_m[wave * G + h] = m[h];
-      red_l[wave * G + h] = l[h];
+      lds.m[wave * G + h] = m[h];
+      lds.l[wave * G + h] = l[h];
     }
   }
   __syncthreads();
 
   // ---- merge the waves (fixed order) and write the partial record
+  float* const rec0 = a.ws + ((size_t)b * a.Hq + (size_t)g * G) * (size_t)a.P * (R + kRecPad);
   for (int it = tid; it < G * R; it += kThreads) {
     const int h = it / R, j = it - h * R;
-    float M = red_m[h];
+    float M = lds.m[h];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red_m[w * G + h]);
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, lds.m[w * G + h]);
     float sacc = 0.f, L = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(red_m[w * G + h] - M);
+      const float f = fast_exp2(lds.m[w * G + h] - M);
       sacc = fmaf(f, red_acc[(w * G + h) * R + j], sacc);
-      L = fmaf(f, red_l[w * G + h], L);
+      L = fmaf(f, lds.l[w * G + h], L);
     }
-    float* rec = a.ws + (((size_t)b * a.Hq + (size_t)g * G + h) * a.P + p) * (R + kRecPad);
+    float* rec = rec0 + ((size_t)h * a.P + p) * (R + kRecPad);
     rec[j] = sacc;
     if (j == 0) {
       rec[R] = M;
@@ -400,101 +583,168 @@ __global__ __launch_bounds__(kThreads) void partition_kernel(PartitionArgs a) {
 }
 
 // ------------------------------------------------------------------ combine
+// Second kernel of the decode step: one workgroup per (b, query head) merges
+// that head's partial records and projects through B_V.  The kernel boundary
+// is what makes every partition's records visible to it: on this multi-XCD
+// part an in-kernel hand-off (last-arriving workgroup merges) needs an
+// agent-scope fence per workgroup, i.e. an L2 writeback each, which measured
+// several times slower than the second launch.
+//
+// The kernel is latency-bound, so every load is issued as early as possible
+// and dependency chains are kept short:
+//   1. each thread loads its slice of B_V[g] (column i = tid % d, row block
+//      jb = tid / d of NB = kThreads / d blocks) before anything else;
+//   2. the head's records are staged into LDS with 16-byte loads, all issued
+//      together (one round trip per chunk of partitions);
+//   3. thread (pg, j) folds coordinate j over partitions pg, pg + NPG, ...
+//      in ascending order (online log-sum-exp rule; NPG = kThreads / r
+//      groups shorten the chain), then the NPG groups are folded in
+//      ascending order: v~ = acc / l;
+//   4. thread (jb, i) forms the row-block partial of v~ . B_V[g][:, i] and
+//      the NB partials are added in ascending order.
+// Every order is fixed, so results are bitwise reproducible.
 
-__device__ __forceinline__ float wave_max(float x) {
-  for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
-}
+template <int R>
+struct CombineLds {
+  static constexpr int kNPG = kThreads / R;                 // partition groups
+  static constexpr int kStage = 4096;                       // staged floats
+  static constexpr int kChunk = kStage / (R + kRecPad);     // partitions per chunk
+  float4 stage[kStage / 4];
+  float m[kNPG * R];
+  float l[kNPG * R];
+  float v[kNPG * R];
+  float vt[R];
+  float part[kThreads];  // [jb][i], NB * d == kThreads
+};
 
-template <int G>
-__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int R = a.r, RS = a.r + kRecPad;
-  const int len = min(max(a.seq_lens[b], 0), a.T);
+template <int R>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void combine_kernel(CombineArgs a) {
+  using CL = CombineLds<R>;
+  constexpr int RS = R + kRecPad;
+  constexpr int kNPG = CL::kNPG, kChunk = CL::kChunk;
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int g = hq / (a.Hq / a.Hkv);
+  const int tid = threadIdx.x;
+  const int d = a.d;
+  const MergeArgs& mg = a.merge;
+
+  // 1. B_V slice: rows [jb * RB, (jb + 1) * RB) of column i
+  const int NB = kThreads / d;  // d in {64, 128, 256}
+  const int RB = R / NB;
+  const int i_col = tid % d, jb = tid / d;
+  float bv[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    bv[k] = 0.f;
+    if (k < RB)
+      bv[k] = load_elem(mg.BV, ((size_t)g * R + jb * RB + k) * d + i_col, mg.f_dtype);
+  }
+
+  const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
   const int np = (len + a.S - 1) / a.S;
-
-  __shared__ float vt[G * kMaxRank];
-  __shared__ float wmax[kWaves];
-  __shared__ float wl[kWaves];
-  __shared__ float wacc[kWaves * kMaxRank];
-
-  const size_t out_row0 = ((size_t)b * a.Hq + (size_t)g * G) * a.d;
-  if (np == 0) {  // no valid token: defined as a zero row
-    for (int i = tid; i < G * a.d; i += kThreads) {
-      if (a.out_dtype == LRATTN_F32) static_cast<float*>(a.out)[out_row0 + i] = 0.f;
-      else static_cast<uint16_t*>(a.out)[out_row0 + i] = 0;
-    }
+  const size_t out_row0 = ((size_t)b * a.Hq + hq) * d;
+  if (np == 0) {
+    write_zero_rows(mg, out_row0, d);
     return;
   }
 
-  for (int h = 0; h < G; ++h) {
-    const float* base = a.ws + ((size_t)b * a.Hq + (size_t)g * G + h) * a.P * RS;
-    float M = -FLT_MAX;
-    for (int pp = tid; pp < np; pp += kThreads) M = fmaxf(M, base[(size_t)pp * RS + R]);
-    M = wave_max(M);
-    if (lane == 0) wmax[wave] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-
-    float L = 0.f, v0 = 0.f, v1 = 0.f;
-    for (int pp = wave; pp < np; pp += kWaves) {
-      const float* rec = base + (size_t)pp * RS;
-      const float f = fast_exp2(rec[R] - M);
-      L = fmaf(f, rec[R + 1], L);
-      if (lane < R) v0 = fmaf(f, rec[lane], v0);
-      if (lane + 64 < R) v1 = fmaf(f, rec[lane + 64], v1);
+  __shared__ CL sm;
+  const float* stage = reinterpret_cast<const float*>(sm.stage);
+  const float* rec0 = a.ws + ((size_t)b * a.Hq + hq) * (size_t)a.P * RS;
+  // kNPG * R <= kThreads (r = 48 leaves 16 threads without a group)
+  const int pg = tid / R, j = tid - pg * R;
+  const bool folds = pg < kNPG;
+  float m = -FLT_MAX, L = 0.f, acc = 0.f;
+  for (int p0 = 0; p0 < np; p0 += kChunk) {
+    const int n4 = min(kChunk, np - p0) * RS / 4;  // float4 in this chunk
+    if (p0 > 0) __syncthreads();                   // previous chunk consumed
+    // 2. stage: every load of a thread is issued before the first LDS store
+    constexpr int kPer = CL::kStage / 4 / kThreads;
+    float4 v4[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + k * kThreads;
+      v4[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < n4) v4[k] = reinterpret_cast<const float4*>(rec0 + (size_t)p0 * RS)[i];
     }
-    if (lane == 0) wl[wave] = L;
-    wacc[wave * kMaxRank + lane] = v0;
-    wacc[wave * kMaxRank + 64 + lane] = v1;
-    __syncthreads();
-    if (tid < R) {
-      const float Ls = ((wl[0] + wl[1]) + wl[2]) + wl[3];
-      const float vs = ((wacc[tid] + wacc[kMaxRank + tid]) + wacc[2 * kMaxRank + tid]) +
-                       wacc[3 * kMaxRank + tid];
-      vt[h * kMaxRank + tid] = vs / Ls;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + k * kThreads;
+      if (i < n4) sm.stage[i] = v4[k];
     }
     __syncthreads();
+    // 3. fold this chunk's partitions pg, pg + NPG, ...
+    const int pc = folds ? min(kChunk, np - p0) : 0;
+    for (int pp = pg; pp < pc; pp += kNPG) {
+      const float* rec = stage + pp * RS;
+      const float mp = rec[R];
+      const float nm = fmaxf(m, mp);
+      const float fa = fast_exp2(m - nm), fb = fast_exp2(mp - nm);
+      L = fmaf(L, fa, rec[R + 1] * fb);
+      acc = fmaf(acc, fa, rec[j] * fb);
+      m = nm;
+    }
   }
+  if (folds) {
+    sm.m[tid] = m;
+    sm.l[tid] = L;
+    sm.v[tid] = acc;
+  }
+  __syncthreads();
+  if (tid < R) {
+#pragma unroll
+    for (int q = 1; q < kNPG; ++q) {
+      const int item = q * R + tid;
+      const float mp = sm.m[item];
+      const float nm = fmaxf(m, mp);
+      const float fa = fast_exp2(m - nm), fb = fast_exp2(mp - nm);
+      L = fmaf(L, fa, sm.l[item] * fb);
+      acc = fmaf(acc, fa, sm.v[item] * fb);
+      m = nm;
+    }
+    sm.vt[tid] = acc / L;
+  }
+  __syncthreads();
 
-  // out[b, g*G + h, i] = sum_j v~[h][j] * B_V[g][j][i]
-  for (int i = tid; i < a.d; i += kThreads) {
-    float o[G];
+  // 4. row-block partial of out[i] = sum_j v~[j] * B_V[g][j][i]
+  float o = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) o[h] = 0.f;
-    for (int j = 0; j < R; ++j) {
-      const float bv = load_elem(a.BV, ((size_t)g * R + j) * a.d + i, a.f_dtype);
-#pragma unroll
-      for (int h = 0; h < G; ++h) o[h] = fmaf(vt[h * kMaxRank + j], bv, o[h]);
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const size_t oi = out_row0 + (size_t)h * a.d + i;
-      if (a.out_dtype == LRATTN_F32) static_cast<float*>(a.out)[oi] = o[h];
-      else static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_rne(o[h]);
-    }
+  for (int k = 0; k < R; ++k) {
+    if (k < RB) o = fmaf(sm.vt[jb * RB + k], bv[k], o);
+  }
+  sm.part[jb * d + i_col] = o;
+  __syncthreads();
+  if (tid < d) {
+    float r = sm.part[tid];
+    for (int q = 1; q < NB; ++q) r += sm.part[q * d + tid];
+    const size_t oi = out_row0 + tid;
+    if (mg.out_dtype == LRATTN_F32) static_cast<float*>(mg.out)[oi] = r;
+    else static_cast<uint16_t*>(mg.out)[oi] = f32_to_bf16_rne(r);
   }
 }
 
 // ------------------------------------------------------------------ probes
 
-__global__ __launch_bounds__(kThreads) void probe_read_kernel(const u32x4* __restrict__ src,
-                                                              size_t n16, float* __restrict__ sink) {
+// Streaming read: each workgroup reads one contiguous chunk with
+// non-temporal 16-byte buffer loads, eight in flight per lane.
+__global__ __launch_bounds__(kThreads) void probe_read_kernel(const char* __restrict__ src,
+                                                              size_t chunk, size_t total,
+                                                              float* __restrict__ sink) {
+  constexpr int kDepth = 8;
+  const size_t beg = (size_t)blockIdx.x * chunk;
   uint32_t x = 0;
-  const size_t stride = (size_t)gridDim.x * kThreads;
-  size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = __builtin_nontemporal_load(src + i);
-    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
-    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
-    x ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3];
-    x ^= c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3];
-  }
-  for (; i < n16; i += stride) {
-    const u32x4 a = src[i];
-    x ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  if (beg < total) {
+    const uint32_t n = (uint32_t)((beg + chunk < total ? beg + chunk : total) - beg);
+    const auto r = make_rsrc(src + beg, n);
+    for (uint32_t off = threadIdx.x * 16u; off < n; off += kThreads * 16u * kDepth) {
+      u32x4 v[kDepth];
+#pragma unroll
+      for (int k = 0; k < kDepth; ++k)
+        v[k] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + k * kThreads * 16u), 0, 2);
+#pragma unroll
+      for (int k = 0; k < kDepth; ++k) x ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
+    }
   }
   for (int off = 1; off < 64; off <<= 1) x ^= __shfl_xor(x, off);
   __shared__ uint32_t s[kWaves];
@@ -540,6 +790,12 @@ hipError_t launch_pr(int rank, int group, const PartitionArgs& a, hipStream_t s)
   }
 }
 
+template <int R>
+hipError_t launch_cg(const CombineArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((combine_kernel<R>), dim3(a.Hq, a.B), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool partition_supported(int latent_dtype, int rank, int group) {
@@ -567,20 +823,24 @@ hipError_t launch_partition(int latent_dtype, int rank, int group, const Partiti
 }
 
 hipError_t launch_combine(int group, const CombineArgs& a, hipStream_t s) {
-  const dim3 grid(a.Hkv, a.B), block(kThreads);
-  switch (group) {
-    case 1: hipLaunchKernelGGL((combine_kernel<1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((combine_kernel<2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((combine_kernel<4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((combine_kernel<8>), grid, block, 0, s, a); break;
+  (void)group;  // one workgroup per query head: the group size only maps h to g
+  switch (a.r) {
+    case 16: return launch_cg<16>(a, s);
+    case 32: return launch_cg<32>(a, s);
+    case 48: return launch_cg<48>(a, s);
+    case 64: return launch_cg<64>(a, s);
+    case 128: return launch_cg<128>(a, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t s) {
+  // chunks of whole 4 KiB pages, each below 2^31 bytes (buffer addressing)
+  size_t chunk = (bytes + kProbeBlocks - 1) / kProbeBlocks;
+  chunk = (chunk + 4095) & ~(size_t)4095;
+  if (chunk >= ((size_t)1 << 31)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(probe_read_kernel, dim3(kProbeBlocks), dim3(kThreads), 0, s,
-                     static_cast<const u32x4*>(src), bytes / 16, sink);
+                     static_cast<const char*>(src), chunk, bytes, sink);
   return hipGetLastError();
 }
 

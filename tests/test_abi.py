@@ -53,8 +53,8 @@ def test_workspace_size_formula():
     p = params(num_splits=7)
     P, S = lr.plan(p)
     assert S == math.ceil(1000 / 7) and P == math.ceil(1000 / S)
-    want = 2 * 8 * P * (64 + 4) * 4
-    assert lr.workspace_size(p) == (want + 255) // 256 * 256
+    records = 2 * 8 * P * (64 + 4) * 4
+    assert lr.workspace_size(p) == (records + 255) // 256 * 256
 
 
 @pytest.mark.parametrize("B,Hkv,T,exp_P", [

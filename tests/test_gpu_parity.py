@@ -169,7 +169,8 @@ def _matrix():
                 continue
             for G in (1, 2, 4, 8):
                 cases.append((lt, r, G, 128))
-    cases += [("bf16", 32, 1, 64), ("bf16", 64, 4, 256), ("f32", 16, 2, 256), ("i8", 64, 8, 64)]
+    cases += [("bf16", 32, 1, 64), ("bf16", 64, 4, 256), ("f32", 16, 2, 256), ("i8", 64, 8, 64),
+              ("bf16", 48, 2, 64), ("bf16", 16, 1, 64), ("bf16", 128, 2, 256), ("f16", 48, 4, 256)]
     return cases
 
 
@@ -273,3 +274,64 @@ def test_probe_copy_and_read():
     lr.probe_read(src, sink)
     torch.cuda.synchronize()
     assert torch.equal(dst, src)
+
+
+def test_back_to_back_inputs_share_a_workspace():
+    """Two different inputs decoded back to back on one workspace, no host
+    sync in between: each result must come from its own call's partials."""
+    import torch
+    import rank_kv_cache_head_amd as lr
+    wa = workloads.make("gqa_vlm", seed=21, **SMALL["gqa_vlm"])
+    wb = workloads.make("gqa_vlm", seed=22, **SMALL["gqa_vlm"])
+    da, db = to_device(wa), to_device(wb)
+    p = lr.params_for(da["q"], da["L_K"], da["B_K"], num_splits=5)
+    ws = torch.empty(lr.workspace_size(p), dtype=torch.uint8, device="cuda")
+    say("back-to-back inputs on one workspace")
+    outs = []
+    for _ in range(3):
+        for d in (da, db):
+            outs.append(lr.decode(d["q"], d["L_K"], d["L_V"], d["B_K"], d["B_V"], d["seq_lens"],
+                                  workspace=ws, num_splits=5))
+    torch.cuda.synchronize()
+    ra, rb = _full_oracle(wa), _full_oracle(wb)
+    for i, o in enumerate(outs):
+        assert rel_rowmax(o.cpu().numpy(), ra if i % 2 == 0 else rb) <= 2e-3, i
+
+
+def test_graph_capture_replay():
+    """lrattn_decode captured in a HIP graph and replayed with new inputs
+    copied into the captured buffers; every replay must equal eager decode."""
+    import torch
+    import rank_kv_cache_head_amd as lr
+    w0 = workloads.make("int8", seed=31, **SMALL["int8"])
+    d0 = to_device(w0)
+    dec = lr.Decoder(d0["q"], d0["L_K"], d0["L_V"], d0["B_K"], d0["B_V"], d0["seq_lens"],
+                     d0["scales"], num_splits=3)
+    torch.cuda.synchronize()
+    say("graph capture")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dec()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        # decode() launches on the current (capturing) stream
+        lr.decode(d0["q"], d0["L_K"], d0["L_V"], d0["B_K"], d0["B_V"], d0["seq_lens"],
+                  d0["scales"], out=dec.out, workspace=dec.workspace, num_splits=3)
+    torch.cuda.synchronize()
+    for seed in (32, 33, 34):
+        w = workloads.make("int8", seed=seed, **SMALL["int8"])
+        d = to_device(w)
+        for k in ("q", "L_K", "L_V", "B_K", "B_V", "scales", "seq_lens"):
+            d0[k].copy_(d[k])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = dec.out.cpu().numpy().copy()
+        eager = lr.decode(d["q"], d["L_K"], d["L_V"], d["B_K"], d["B_V"], d["seq_lens"],
+                          d["scales"], num_splits=3)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, eager.cpu().numpy()), seed
+        assert rel_rowmax(got, _full_oracle(w)) <= 2e-3
