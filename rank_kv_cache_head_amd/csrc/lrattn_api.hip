@@ -16,11 +16,16 @@ using lrattn::kRecPad;
 
 constexpr int kVersion = 10000;  // 1.0.0
 
-// Partition plan: at least kMinSplitTokens tokens per partition and, when the
-// caller leaves num_splits at 0, enough (b, kv-head, partition) workgroups to
-// cover the 256 compute units several times over.
-constexpr int kTargetBlocks = 2048;
-constexpr int kMinSplitTokens = 256;
+// Default partition plan (num_splits = 0), from measurements on MI355X:
+// a partition streams at least kSplitBytes of latents (and scales) and at
+// least kSplitTokensPerHead tokens per query head of its group, since each
+// workgroup pays a fixed prologue (absorbing q into the factor) and epilogue
+// (merging its waves); the split is only made finer when that would leave
+// fewer than kMinBlocks workgroups.
+constexpr int64_t kSplitBytes = 128 * 1024;
+constexpr int64_t kSplitTokensPerHead = 1024;
+constexpr int64_t kMinBlocks = 512;
+constexpr int64_t kMinSplitTokens = 256;
 
 int esize(int dt) {
   switch (dt) {
@@ -77,9 +82,17 @@ int check_params(const lrattn_params* p, Plan* plan) {
   int64_t splits = p->num_splits;
   if (splits == 0) {
     const int64_t pairs = (int64_t)p->batch * p->num_kv_heads;
-    const int64_t want = (kTargetBlocks + pairs - 1) / pairs;
-    const int64_t cap = (T + kMinSplitTokens - 1) / kMinSplitTokens;
-    splits = want < cap ? want : cap;
+    const int64_t row_pair = 2 * (int64_t)p->rank * esize(p->latent_dtype) +
+                             (p->latent_dtype == LRATTN_I8 ? 8 : 0);
+    int64_t tokens = (kSplitBytes + row_pair - 1) / row_pair;
+    if (tokens < kSplitTokensPerHead * group) tokens = kSplitTokensPerHead * group;
+    tokens = (tokens + 255) / 256 * 256;
+    splits = (T + tokens - 1) / tokens;
+    if (pairs * splits < kMinBlocks) {
+      const int64_t cap = (T + kMinSplitTokens - 1) / kMinSplitTokens;
+      const int64_t want = (kMinBlocks + pairs - 1) / pairs;
+      splits = want < cap ? want : cap;
+    }
     if (splits < 1) splits = 1;
   }
   const int64_t S = (T + splits - 1) / splits;

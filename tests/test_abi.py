@@ -57,17 +57,23 @@ def test_workspace_size_formula():
     assert lr.workspace_size(p) == (records + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("B,Hkv,T,exp_P", [
-    (1, 4, 256, 1),        # tiny: one partition per head
-    (8, 32, 4096, 8),      # 7B-like
-    (16, 8, 16384, 16),    # GQA VLM
-    (32, 32, 8192, 2),     # int8
-    (4, 40, 131072, 13),   # ragged
+@pytest.mark.parametrize("kw,exp_P,exp_S", [
+    # the five workloads' shapes and storage types
+    (dict(batch=1, num_q_heads=4, num_kv_heads=4, head_dim=64, rank=16, max_seq_len=256,
+          q_dtype=lr.F32, latent_dtype=lr.F32, factor_dtype=lr.F32), 1, 256),
+    (dict(batch=8, num_q_heads=32, num_kv_heads=32, rank=32, max_seq_len=4096), 4, 1024),
+    (dict(batch=16, num_q_heads=32, num_kv_heads=8, rank=64, max_seq_len=16384), 4, 4096),
+    (dict(batch=32, num_q_heads=32, num_kv_heads=32, rank=32, max_seq_len=8192,
+          latent_dtype=lr.I8), 4, 2048),
+    (dict(batch=4, num_q_heads=40, num_kv_heads=40, rank=48, max_seq_len=131072), 128, 1024),
+    # few (b, kv-head) pairs: split finer to keep >= 512 workgroups
+    (dict(batch=1, num_q_heads=8, num_kv_heads=8, rank=64, max_seq_len=65536), 64, 1024),
 ])
-def test_default_plan(B, Hkv, T, exp_P):
-    p = params(batch=B, num_q_heads=Hkv, num_kv_heads=Hkv, max_seq_len=T, rank=32)
-    P, S = lr.plan(p)
-    assert P == exp_P and P * S >= T and (P - 1) * S < T and S >= min(256, T)
+def test_default_plan(kw, exp_P, exp_S):
+    P, S = lr.plan(params(**kw))
+    T = kw["max_seq_len"]
+    assert (P, S) == (exp_P, exp_S)
+    assert P * S >= T and (P - 1) * S < T
 
 
 def test_plan_explicit_splits():
