@@ -248,7 +248,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
-            "kernel": "partition_kernel",
+            "kernel": lr.partition_kernel(p),
             "mean_launch_us": launch_mean_s * 1e6,
             "min_launch_us": float(launch_ms.min()) * 1e3,
             "algorithmic_bytes_per_launch": part_bytes,

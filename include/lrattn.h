@@ -71,6 +71,10 @@
  *
  * RESULTS
  *   Scores, softmax and accumulation run in fp32 on exactly-converted inputs.
+ *   Where matrix cores take a product (q . B_K^T when q and B_K share a 2-byte
+ *   format; the scores for bf16 latents with 4 or 8 query heads per kv-head
+ *   and r a multiple of 32) the bf16/fp16 products are exact and summed in
+ *   fp32, and q~ enters as three bf16 terms whose sum is q~ exactly.
  *   For a fixed num_splits, build and device, results are bitwise identical
  *   from run to run (fixed reduction order, no atomics).
  */
@@ -136,6 +140,15 @@ const char* lrattn_status_string(int status);
  * NULL.
  */
 int lrattn_plan(const lrattn_params* p, int32_t* num_splits, int32_t* split_tokens);
+
+/*
+ * Host-only.  Name of the partition kernel that lrattn_partition (and
+ * lrattn_decode) launches for `p`, as profilers list it: static text,
+ * "partition_mfma_kernel" (bf16 latents, r a multiple of 32, 4 or 8 query
+ * heads per kv-head: scores on the matrix cores) or "partition_kernel".
+ * NULL when `p` is invalid or unsupported.
+ */
+const char* lrattn_partition_kernel(const lrattn_params* p);
 
 /*
  * Host-only.  Bytes of device workspace lrattn_decode needs for `p`:

@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.lrattn_status_string.argtypes = [ctypes.c_int]
         L.lrattn_plan.argtypes = [_PP, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
         L.lrattn_workspace_size.argtypes = [_PP, ctypes.POINTER(ctypes.c_size_t)]
+        L.lrattn_partition_kernel.argtypes = [_PP]
+        L.lrattn_partition_kernel.restype = ctypes.c_char_p
         L.lrattn_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                     ctypes.c_size_t, _VP]
         L.lrattn_partition.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -158,6 +160,12 @@ def params_for(q, L_K, B_K, *, out_dtype=None, softmax_scale=None, num_splits: i
     od = F32 if out_dtype in (None, torch.float32) else (BF16 if out_dtype == torch.bfloat16 else -1)
     return Params(B, Hq, Hkv, d, r, T, _dtype_code(q), _dtype_code(L_K), _dtype_code(B_K), od,
                   float(softmax_scale) if softmax_scale else 0.0, int(num_splits))
+
+
+def partition_kernel(p: Params) -> str:
+    """lrattn_partition_kernel: the partition kernel's name for these parameters."""
+    _check(lib().lrattn_plan(ctypes.byref(p), None, None), "lrattn_partition_kernel")
+    return lib().lrattn_partition_kernel(ctypes.byref(p)).decode()
 
 
 def plan(p: Params) -> Tuple[int, int]:

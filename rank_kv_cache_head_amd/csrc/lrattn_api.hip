@@ -199,6 +199,12 @@ int lrattn_plan(const lrattn_params* p, int32_t* num_splits, int32_t* split_toke
   return LRATTN_OK;
 }
 
+const char* lrattn_partition_kernel(const lrattn_params* p) {
+  Plan pl;
+  if (check_params(p, &pl) != LRATTN_OK) return nullptr;
+  return lrattn::partition_kernel_name(p->latent_dtype, p->rank, group_of(p));
+}
+
 int lrattn_workspace_size(const lrattn_params* p, size_t* bytes) {
   if (!bytes) return LRATTN_ERR_NULL;
   Plan pl;

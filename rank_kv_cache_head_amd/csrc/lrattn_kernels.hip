@@ -14,10 +14,13 @@
 //   partition grid (P, Hkv, B), 256 threads = 4 wave64.  One workgroup owns
 //   the tokens [p*S, min((p+1)*S, seq_len)) of one (b, kv-head) and all G
 //   query heads of that kv-head, so each latent byte is read once for the
-//   whole group.
+//   whole group.  Two kernel families: partition_mfma_kernel (bf16 latents,
+//   4 or 8 heads per kv-head, r a multiple of 32: scores on the matrix cores)
+//   and partition_kernel (everything else: scores on the VALU).
 //   combine grid (Hq, B), 256 threads.
 //
-// Lane mapping inside a wave (the hot loop):
+// Lane mapping inside a wave (the VALU kernel's hot loop; the matrix-core
+// kernel keeps it for the value side):
 //   a latent row of r elements is kRowBytes bytes = kAct pieces of kVec bytes
 //   (16, or 8 for int8 latents with 4+ heads).  kLPR (= kAct rounded up to a
 //   power of two) consecutive lanes form a "slot" that holds one row: lane cc
@@ -38,6 +41,9 @@ namespace lrattn {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ formats
 
@@ -89,34 +95,6 @@ template <> struct Unpack<LatI8> {
   }
 };
 
-// One element of q or of a factor, runtime dtype (prologue / epilogue only).
-__device__ __forceinline__ float load_elem(const void* p, size_t i, int dt) {
-  if (dt == LRATTN_F32) return static_cast<const float*>(p)[i];
-  const uint32_t h = static_cast<const uint16_t*>(p)[i];
-  if (dt == LRATTN_BF16) return __uint_as_float(h << 16);
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-}
-
-// Eight consecutive factor elements starting at element i (i % 8 == 0).
-__device__ __forceinline__ void load8(const void* p, size_t i, int dt, float* x) {
-  if (dt == LRATTN_F32) {
-    const float4* f = reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
-    const float4 a = f[0], b = f[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    return;
-  }
-  const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
-  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-  if (dt == LRATTN_BF16) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) { x[2 * k] = bf16_lo(ww[k]); x[2 * k + 1] = bf16_hi(ww[k]); }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) { x[2 * k] = f16_lo(ww[k]); x[2 * k + 1] = f16_hi(ww[k]); }
-  }
-}
-
 // fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -158,6 +136,20 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Maximum over aligned groups of 16 lanes (a DPP row); every lane of the row
+// ends with it.
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x140>(x));
+  return x;
+}
+
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Largest base-2 logit excess over the running reference max before the
@@ -188,6 +180,28 @@ constexpr float kLazyLog2 = 8.0f;
 #endif
 #ifndef LRATTN_LOAD_AUX
 #define LRATTN_LOAD_AUX 2
+#endif
+//   LRATTN_MFMA_SCORES     1: bf16 latents with 4 or 8 heads per kv-head and
+//                          r a multiple of 32 score on the matrix cores
+//   LRATTN_MFMA_TILES      16-token score tiles per wave per step there
+//   LRATTN_LATENTS_AFTER   where the VALU kernel issues its first latent
+//                          loads in the prologue: 0 first, 1 after q is
+//                          staged (the matrix-core absorption: first), 2
+//                          after the absorption (every load the prologue
+//                          waits for is then served ahead of the grid's
+//                          latent stream)
+//   LRATTN_MFMA_LATENTS_AFTER  the same for the matrix-core score kernel
+#ifndef LRATTN_LATENTS_AFTER
+#define LRATTN_LATENTS_AFTER 1
+#endif
+#ifndef LRATTN_MFMA_LATENTS_AFTER
+#define LRATTN_MFMA_LATENTS_AFTER 2
+#endif
+#ifndef LRATTN_MFMA_SCORES
+#define LRATTN_MFMA_SCORES 1
+#endif
+#ifndef LRATTN_MFMA_TILES
+#define LRATTN_MFMA_TILES 2
 #endif
 
 
@@ -367,25 +381,276 @@ __device__ __forceinline__ float piece_sum(float x, int n) {
 
 // ------------------------------------------------------------------ merge
 
-// Zero rows for a sequence with no valid token (attention over no tokens is
-// defined as a zero output).
-__device__ __forceinline__ void write_zero_rows(const MergeArgs& mg, size_t out_row0, int n) {
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    if (mg.out_dtype == LRATTN_F32) static_cast<float*>(mg.out)[out_row0 + i] = 0.f;
-    else static_cast<uint16_t*>(mg.out)[out_row0 + i] = 0;
+// ------------------------------------------------------------ partition kernel
+
+// Absorption for the G query heads of kv-head g of sequence b:
+// qt_lds[h][j] = qscale * sum_i q[h][i] * B_K[g][j][i]  (fp32, G x R).
+// Every product is exact in fp32 and the sums run in fp32.
+//
+// When q and B_K share a 2-byte format the product runs on the matrix cores
+// (absorb_mfma below).  Otherwise on the VALU, in three steps, so that a
+// kernel can place its first latent loads among them:
+// absorb_issue loads this thread's q values and its first batch of B_K
+// pieces (8 consecutive elements of one factor row) into registers;
+// absorb_stage_q stages q in LDS; absorb_dot forms the dot products (a
+// batch's loads are all in flight together) and leaves q~ in qt_lds.  Vector
+// loads of a wave return in issue order, so loads issued before the latents
+// are not held up by them, and the dot products overlap the first latent
+// round trip.
+template <int R, int G>
+struct AbsorbIn {
+  // q: G * d values of 2 or 4 bytes = at most 8 KiB = 2 x 16 bytes per thread
+  static constexpr int kQLoads = (G * kMaxHeadDim * 4 / 16 + kThreads - 1) / kThreads;
+  // B_K pieces per thread per batch: all of them for d = 128 and r <= 64
+  static constexpr int kPieceBatch = R / 16 < 4 ? R / 16 : 4;
+  u32x4 qw[kQLoads];
+  u32x4 fw[kPieceBatch][2];  // a piece is 16 bytes (2-byte factors) or 32 bytes (fp32)
+};
+
+// 16 raw bytes -> x[0..8): eight values of a 2-byte format, or four fp32
+// values (x[4..8) = 0).  Every conversion is exact; fixed indices and
+// selects on the uniform format only.
+__device__ __forceinline__ void words_to_floats(const u32x4& w, int dt, float* x) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t word = w[j >> 1];
+    const float two = dt == LRATTN_BF16 ? ((j & 1) ? bf16_hi(word) : bf16_lo(word))
+                                        : ((j & 1) ? f16_hi(word) : f16_lo(word));
+    const float four = j < 4 ? __uint_as_float(w[j & 3]) : 0.f;
+    x[j] = dt == LRATTN_F32 ? four : two;
   }
 }
 
-// ------------------------------------------------------------ partition kernel
+// The B_K[g] slice as a raw buffer resource.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t factor_rsrc(const PartitionArgs& a, int g, int R) {
+  const uint32_t fes = a.f_dtype == LRATTN_F32 ? 4u : 2u;
+  return make_rsrc(static_cast<const char*>(a.BK) + (size_t)g * R * a.d * fes,
+                   (uint32_t)(R * a.d) * fes);
+}
+
+// Piece `it` of B_K[g] (8 consecutive elements of one row): one 16-byte load
+// for 2-byte factors, two for fp32.  A piece past the factor loads zeros.
+__device__ __forceinline__ void load_piece(__amdgpu_buffer_rsrc_t rf, int it, int npieces,
+                                           bool f32, u32x4 (&w)[2]) {
+  const uint32_t off = it < npieces ? (uint32_t)it * (f32 ? 32u : 16u) : kOffNone;
+  w[0] = __builtin_amdgcn_raw_buffer_load_b128(rf, (int)off, 0, 0);
+  w[1] = __builtin_amdgcn_raw_buffer_load_b128(rf, (int)(f32 ? off + 16u : kOffNone), 0, 0);
+}
+
+// Every load below is a raw buffer load bounded by its slice and every loaded
+// value is used unconditionally, so no load sits behind a branch and all of a
+// thread's loads are in flight together.
+template <int R, int G>
+__device__ __forceinline__ void absorb_issue(const PartitionArgs& a, int b, int g,
+                                             AbsorbIn<R, G>& in) {
+  using AI = AbsorbIn<R, G>;
+  const int tid = threadIdx.x, d = a.d;
+  const uint32_t qes = a.q_dtype == LRATTN_F32 ? 4u : 2u;
+  const size_t q0 = ((size_t)b * a.Hq + (size_t)g * G) * d;  // the G*d values are contiguous
+  const auto rq = make_rsrc(static_cast<const char*>(a.q) + q0 * qes, (uint32_t)(G * d) * qes);
+#pragma unroll
+  for (int k = 0; k < AI::kQLoads; ++k)
+    in.qw[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)((tid + k * kThreads) * 16u), 0, 0);
+  const auto rf = factor_rsrc(a, g, R);
+#pragma unroll
+  for (int k = 0; k < AI::kPieceBatch; ++k)
+    load_piece(rf, tid + k * kThreads, R * (d >> 3), a.f_dtype == LRATTN_F32, in.fw[k]);
+}
+
+// q_lds holds G rows of kMaxHeadDim floats plus 8 floats of padding that
+// absorbs the stores of threads without q values.
+template <int R, int G>
+__device__ __forceinline__ void absorb_stage_q(const PartitionArgs& a, AbsorbIn<R, G>& in,
+                                               float* q_lds) {
+  using AI = AbsorbIn<R, G>;
+  const int tid = threadIdx.x, d = a.d;
+  {
+    const bool q32 = a.q_dtype == LRATTN_F32;
+    const int epc = q32 ? 4 : 8;  // values per 16 bytes; divides d
+#pragma unroll
+    for (int k = 0; k < AI::kQLoads; ++k) {
+      const int e0 = (tid + k * kThreads) * epc;
+      const int h = e0 / d;
+      float* dst = e0 < G * d ? q_lds + h * kMaxHeadDim + (e0 - h * d) : q_lds + G * kMaxHeadDim;
+      float x[8];
+      words_to_floats(in.qw[k], a.q_dtype, x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = x[e];
+      if (!q32) {
+#pragma unroll
+        for (int e = 4; e < 8; ++e) dst[e] = x[e];
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// One batch of pieces (first piece index base + tid): q~ rows j of this
+// batch's factor rows.  Pieces past the factor hold zeros and write nothing;
+// the sums run in every lane (the cross-lane sum cannot sit under a branch).
+template <int R, int G>
+__device__ __forceinline__ void absorb_batch(const PartitionArgs& a, const AbsorbIn<R, G>& in,
+                                             int base, const float* q_lds, float* qt_lds) {
+  constexpr int PB = AbsorbIn<R, G>::kPieceBatch;
+  const int tid = threadIdx.x;
+  const int nch = a.d >> 3, npieces = R * nch;
+  const bool f32 = a.f_dtype == LRATTN_F32;
+#pragma unroll
+  for (int k = 0; k < PB; ++k) {
+    const int it = base + k * kThreads + tid;
+    const int j = it / nch, c = it - j * nch;
+    float f[8], f2[8];
+    words_to_floats(in.fw[k][0], a.f_dtype, f);
+    words_to_floats(in.fw[k][1], LRATTN_F32, f2);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[4 + e] = f32 ? f2[e] : f[4 + e];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t = fmaf(q_lds[h * kMaxHeadDim + c * 8 + e], f[e], t);
+      t = piece_sum(t, nch);
+      if (c == 0 && it < npieces) qt_lds[h * R + j] = t * a.qscale;
+    }
+  }
+}
+
+// The first batch was loaded by absorb_issue and is used in straight-line
+// code: inside a loop whose body also loads, the hardware wait before its
+// first use could not be told apart from waits on the later loads (the
+// latents issued meanwhile included).  Later batches (d = 256 or r = 128)
+// are loaded and used in the loop.
+template <int R, int G>
+__device__ __forceinline__ void absorb_dot(const PartitionArgs& a, int g, AbsorbIn<R, G>& in,
+                                           const float* q_lds, float* qt_lds) {
+  constexpr int PB = AbsorbIn<R, G>::kPieceBatch;
+  const int tid = threadIdx.x;
+  const int npieces = R * (a.d >> 3);
+  const bool f32 = a.f_dtype == LRATTN_F32;
+  absorb_batch<R, G>(a, in, 0, q_lds, qt_lds);
+  if (npieces > PB * kThreads) {
+    const auto rf = factor_rsrc(a, g, R);
+    for (int base = PB * kThreads; base < npieces; base += PB * kThreads) {
+#pragma unroll
+      for (int k = 0; k < PB; ++k) load_piece(rf, base + tid + k * kThreads, npieces, f32, in.fw[k]);
+      absorb_batch<R, G>(a, in, base, q_lds, qt_lds);
+    }
+  }
+  __syncthreads();
+}
+
+// The matrix-core absorption: q and B_K both bf16 or both fp16 (exact
+// products, fp32 sums, as on the VALU).  D = A . B with A = the G query rows
+// (rows G..15 zero), B = B_K[g]^T, K = d in steps of 32
+// (v_mfma_f32_16x16x32_{bf16,f16}); wave w forms the 16-column tiles
+// nt = w, w + 4 of the r columns.  Lane l supplies row / column l % 16 and
+// the 8 elements 8 * (l / 16) .. + 7 of each 32-element step: 16 contiguous
+// bytes of q or of one B_K row, loaded straight into the operand register.
+// The result, lane l register i = (head 4 * (l / 16) + i, column l % 16),
+// goes to qt_lds.  All loads of a 4-step chunk are in flight together
+// (d = 256 takes two chunks).  Ends with a barrier.
+__device__ __forceinline__ bool absorb_on_mfma(const PartitionArgs& a) {
+  return a.q_dtype == a.f_dtype && a.q_dtype != LRATTN_F32;
+}
+
+template <int R, int G>
+__device__ __forceinline__ void absorb_mfma(const PartitionArgs& a, int b, int g, float* qt_lds) {
+  constexpr int NT = R / 16;                        // column tiles: 1, 2, 3, 4 or 8
+  constexpr int TPW = (NT + kWaves - 1) / kWaves;   // tiles per wave: 1 or 2
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int d = a.d, ksteps = d >> 5;               // 2, 4 or 8
+  const int row = lane & 15, kg = lane >> 4;
+  const bool bf = a.q_dtype == LRATTN_BF16;
+  const size_t q0 = ((size_t)b * a.Hq + (size_t)g * G) * d;
+  const auto rq = make_rsrc(static_cast<const uint16_t*>(a.q) + q0, (uint32_t)(G * d) * 2u);
+  const auto rf = make_rsrc(static_cast<const uint16_t*>(a.BK) + (size_t)g * R * d,
+                            (uint32_t)(R * d) * 2u);
+  f32x4 acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto chunk = [&](int k0) {
+    u32x4 qa[4], fb[TPW][4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int ks = k0 + kk;
+      const bool kv = ks < ksteps;
+      const uint32_t qoff = row < G && kv ? (uint32_t)(row * d + 32 * ks + 8 * kg) * 2u : kOffNone;
+      qa[kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qoff, 0, 0);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int nt = wave + kWaves * t;
+        const uint32_t foff =
+            nt < NT && kv ? (uint32_t)((16 * nt + row) * d + 32 * ks + 8 * kg) * 2u : kOffNone;
+        fb[t][kk] = __builtin_amdgcn_raw_buffer_load_b128(rf, (int)foff, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        if (bf)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[kk]),
+                                                           __builtin_bit_cast(bf16x8, fb[t][kk]),
+                                                           acc[t], 0, 0, 0);
+        else
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, qa[kk]),
+                                                          __builtin_bit_cast(f16x8, fb[t][kk]),
+                                                          acc[t], 0, 0, 0);
+      }
+    }
+  };
+  chunk(0);                   // steps 0..3 (zero operands past d)
+  if (ksteps > 4) chunk(4);   // d = 256
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int nt = wave + kWaves * t;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * kg + i;
+      if (nt < NT && h < G) qt_lds[h * R + 16 * nt + row] = acc[t][i] * a.qscale;
+    }
+  }
+  __syncthreads();
+}
 
 template <int R, int G>
 struct PartLds {
-  float q[G * kMaxHeadDim];
+  float q[G * kMaxHeadDim + 8];  // + padding for threads without q values
   float qt[G * R];
   float acc[kWaves * G * R];
   float m[kWaves * G];
   float l[kWaves * G];
 };
+
+// Merges the kWaves per-wave partials (fixed order) and writes one record
+// per query head of the group: acc[0..R), m, l.  red_acc [wave][h][R],
+// red_m and red_l [wave][h] are in LDS; the caller has synchronized.
+template <int R, int G>
+__device__ __forceinline__ void write_records(const PartitionArgs& a, int b, int g, int p,
+                                              const float* red_acc, const float* red_m,
+                                              const float* red_l) {
+  const int tid = threadIdx.x;
+  float* const rec0 = a.ws + ((size_t)b * a.Hq + (size_t)g * G) * (size_t)a.P * (R + kRecPad);
+  for (int it = tid; it < G * R; it += kThreads) {
+    const int h = it / R, j = it - h * R;
+    float M = red_m[h];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red_m[w * G + h]);
+    float sacc = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = fast_exp2(red_m[w * G + h] - M);
+      sacc = fmaf(f, red_acc[(w * G + h) * R + j], sacc);
+      L = fmaf(f, red_l[w * G + h], L);
+    }
+    float* rec = rec0 + ((size_t)h * a.P + p) * (R + kRecPad);
+    rec[j] = sacc;
+    if (j == 0) {
+      rec[R] = M;
+      rec[R + 1] = L;
+    }
+  }
+}
 
 template <class LT, int R, int G>
 __global__ __launch_bounds__(kThreads)
@@ -426,66 +691,21 @@ void partition_kernel(PartitionArgs a) {
   }
   const uint32_t lane_off = colact ? (uint32_t)(slot * Gm::kRowBytes + cc * Gm::kVec) : kOffNone;
 
-  // The first step's latents are requested before the prologue, so their
-  // latency overlaps the absorption instead of following it.
+  // q and B_K are requested first, then the first step's latents; the
+  // absorption then runs while the latents are in flight.
   Step<LT, R, G> cur;
-  load_step(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv);
-
-  // ---- absorption: q~[h][j] = qscale * sum_i q[h][i] * B_K[g][j][i]
-  // All q and B_K loads of a thread are issued before any is used (one
-  // memory round trip); the G*d query values are contiguous.
-  const int d = a.d;
-  {
-    constexpr int kQPer = (G * kMaxHeadDim + kThreads - 1) / kThreads;
-    const size_t q0 = ((size_t)b * a.Hq + (size_t)g * G) * d;
-    float qv[kQPer];
-#pragma unroll
-    for (int k = 0; k < kQPer; ++k) {
-      const int i = tid + k * kThreads;
-      qv[k] = i < G * d ? load_elem(a.q, q0 + i, a.q_dtype) : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < kQPer; ++k) {
-      const int i = tid + k * kThreads;
-      if (i < G * d) {
-        const int h = i / d;
-        q_lds[h * kMaxHeadDim + (i - h * d)] = qv[k];
-      }
-    }
+  if (absorb_on_mfma(a)) {
+    if constexpr (LRATTN_LATENTS_AFTER < 2) load_step(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv);
+    absorb_mfma<R, G>(a, b, g, qt_lds);
+  } else {
+    AbsorbIn<R, G> ab;
+    absorb_issue<R, G>(a, b, g, ab);
+    if constexpr (LRATTN_LATENTS_AFTER == 0) load_step(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv);
+    absorb_stage_q<R, G>(a, ab, q_lds);
+    if constexpr (LRATTN_LATENTS_AFTER == 1) load_step(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv);
+    absorb_dot<R, G>(a, g, ab, q_lds, qt_lds);
   }
-  __syncthreads();
-  const int nch = d >> 3;  // 8-element pieces per factor row; R * nch % 64 == 0
-  // pieces per thread whose loads are in flight together: all of them for
-  // d = 128 and r <= 64
-  constexpr int kPieceBatch = R / 16 < 4 ? R / 16 : 4;
-  for (int base = 0; base < R * nch; base += kPieceBatch * kThreads) {
-    float f[kPieceBatch][8];
-#pragma unroll
-    for (int k = 0; k < kPieceBatch; ++k) {
-      const int it = base + tid + k * kThreads;
-      if (it < R * nch) {
-        const int j = it / nch, c = it - j * nch;
-        load8(a.BK, ((size_t)g * R + j) * d + (size_t)c * 8, a.f_dtype, f[k]);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kPieceBatch; ++k) {
-      const int it = base + k * kThreads + (tid & ~63);  // wave-uniform guard
-      if (it < R * nch) {
-        const int itl = it + lane;
-        const int j = itl / nch, c = itl - j * nch;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float t = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) t = fmaf(q_lds[h * kMaxHeadDim + c * 8 + e], f[k][e], t);
-          t = piece_sum(t, nch);
-          if (c == 0) qt_lds[h * R + j] = t * a.qscale;
-        }
-      }
-    }
-  }
-  __syncthreads();
+  if constexpr (LRATTN_LATENTS_AFTER == 2) load_step(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv);
 
   QtView<LT, R, G> qt;
   // idle lanes (cc >= kAct) load zeros, so their q~ is never read
@@ -559,27 +779,317 @@ void partition_kernel(PartitionArgs a) {
   }
   __syncthreads();
 
-  // ---- merge the waves (fixed order) and write the partial record
-  float* const rec0 = a.ws + ((size_t)b * a.Hq + (size_t)g * G) * (size_t)a.P * (R + kRecPad);
-  for (int it = tid; it < G * R; it += kThreads) {
-    const int h = it / R, j = it - h * R;
-    float M = lds.m[h];
+  write_records<R, G>(a, b, g, p, lds.acc, lds.m, lds.l);
+}
+
+// ------------------------------------------------ partition, matrix-core scores
+// bf16 latents, 4 or 8 query heads per kv-head, r in {32, 64, 128}.
+//
+// The scores of a tile of 16 tokens are a dense product, D = A . B, taken on
+// the matrix cores as r / 32 steps of v_mfma_f32_16x16x32_bf16 per term:
+//   B[k][n] = Lk[token n][k]: the stored bf16 latents as they are.  Lane l
+//             loads 16 bytes (8 columns) of token l % 16, column group
+//             l / 16 of each 32-column step; that register is its B operand.
+//   A[i][k] = q~[i % G][k]: rows repeat the G heads.  q~ is split exactly
+//             into three bf16 terms (hi + mid + lo == q~ in fp32), each
+//             multiplied into the same fp32 accumulator, so the scores are
+//             fp32 products of the exact inputs, as on the VALU path.
+// Lane l receives rows 4 * (l / 16) + i (i < 4) of column l % 16: the scores
+// of token l % 16 for heads i (G = 4) or 4 * ((l / 16) % 2) + i (G = 8).
+// One reference max per head serves the whole wave (moved lazily, as on the
+// VALU path), so the exponentials computed in the score layout can be handed
+// to the value side through a per-wave LDS tile [token][head]; the value side
+// keeps the VALU path's slot layout: kLPR lanes per row, 8 columns per lane.
+template <int R, int G>
+struct MGeo {
+  static constexpr int kRowBytes = 2 * R;
+  static constexpr int kKC = R / 32;           // 32-column MFMA steps per tile
+  static constexpr int kTerms = 3;             // bf16 terms of q~
+  static constexpr int kLPR = kRowBytes / 16;  // value lanes per row: 4, 8, 16
+  static constexpr int kRPW = 64 / kLPR;       // rows per value load
+  static constexpr int kVU = 16 / kRPW;        // value loads per tile
+  static constexpr int kNT = LRATTN_MFMA_TILES;
+  static constexpr int kChunk = 16 * kNT;      // tokens per wave per step
+  // registers: q~ terms 12 * kKC, accumulators 8 * G, latents 4 * (kKC + kVU)
+  // per tile
+  static constexpr int kRegs = 12 * kKC + 8 * G + 4 * kNT * (kKC + kVU);
+  static constexpr int kWavesPerEU = kRegs <= 80 ? 4 : kRegs <= 120 ? 3 : 2;
+  static_assert(R % 32 == 0 && (G == 4 || G == 8), "matrix-core path shape");
+};
+
+template <int R, int G>
+struct MStep {
+  uint32_t k[MGeo<R, G>::kNT][MGeo<R, G>::kKC][4];
+  uint32_t v[MGeo<R, G>::kNT][MGeo<R, G>::kVU][4];
+};
+
+template <int R, int G>
+__device__ __forceinline__ void load_mstep(MStep<R, G>& st, int cb, uint32_t koff, uint32_t voff,
+                                           __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv) {
+  using Mg = MGeo<R, G>;
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, lds.m[w * G + h]);
-    float sacc = 0.f, L = 0.f;
+  for (int t = 0; t < Mg::kNT; ++t) {
+    const uint32_t base = (uint32_t)(cb + 16 * t) * Mg::kRowBytes;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(lds.m[w * G + h] - M);
-      sacc = fmaf(f, red_acc[(w * G + h) * R + j], sacc);
-      L = fmaf(f, lds.l[w * G + h], L);
+    for (int c = 0; c < Mg::kKC; ++c) load_words<4>(st.k[t][c], rk, base + koff + 64u * c);
+  }
+#pragma unroll
+  for (int t = 0; t < Mg::kNT; ++t) {
+    const uint32_t base = (uint32_t)(cb + 16 * t) * Mg::kRowBytes;
+#pragma unroll
+    for (int u = 0; u < Mg::kVU; ++u)
+      load_words<4>(st.v[t][u], rv, base + voff + (uint32_t)(u * Mg::kRPW) * Mg::kRowBytes);
+  }
+}
+
+template <int R, int G, bool kMask>
+__device__ __forceinline__ void compute_mstep(
+    const MStep<R, G>& st, int cb, int ntok, int lane, const bf16x8 (&qa)[3][MGeo<R, G>::kKC],
+    float (&mm)[4], float (&ll)[4], float (&acc)[G][8], float* wl) {
+  using Mg = MGeo<R, G>;
+  constexpr int NT = Mg::kNT, KC = Mg::kKC, VU = Mg::kVU, RPW = Mg::kRPW;
+  const int tok = lane & 15;
+  const bool hi_half = G == 8 && ((lane >> 4) & 1);  // this lane's results are heads 4..7
+
+  // scores (base-2 logits): s[t][i] for token 16 t + tok, this lane's head i
+  float s[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int term = 2; term >= 0; --term) {  // smallest term first
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const u32x4 kw = {st.k[t][c][0], st.k[t][c][1], st.k[t][c][2], st.k[t][c][3]};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[term][c], __builtin_bit_cast(bf16x8, kw), d,
+                                                    0, 0, 0);
+      }
     }
-    float* rec = rec0 + ((size_t)h * a.P + p) * (R + kRecPad);
-    rec[j] = sacc;
-    if (j == 0) {
-      rec[R] = M;
-      rec[R + 1] = L;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[t][i] = d[i];
+      if constexpr (kMask) {
+        if (cb + 16 * t + tok >= ntok) s[t][i] = -INFINITY;
+      }
     }
   }
+
+  // Lazily moved reference max per head, the same in every lane holding the
+  // head (lanes of the same row parity hold identical rows): mm[i] belongs to
+  // this lane's head i.  A 16-lane row max is the wave max of that head.
+  bool need = false;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) need |= s[t][i] > mm[i] + kLazyLog2;
+  }
+  if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = s[0][i];
+#pragma unroll
+      for (int t = 1; t < NT; ++t) x = fmaxf(x, s[t][i]);
+      x = row_max16(x);
+      const float nm = x > mm[i] + kLazyLog2 ? x : mm[i];
+      const float corr = fast_exp2(mm[i] - nm);
+      mm[i] = nm;
+      ll[i] *= corr;
+      // the value side holds every head: heads i (lane 0) and 4 + i (lane 16)
+      const float c0 = readlane_f(corr, 0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[i][e] *= c0;
+      if constexpr (G == 8) {
+        const float c1 = readlane_f(corr, 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[4 + i][e] *= c1;
+      }
+    }
+  }
+
+  // weights 2^(s - m) into the wave's [token][head] tile
+  float e[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e[t][i] = fast_exp2(s[t][i] - mm[i]);
+      ll[i] += e[t][i];
+    }
+  }
+  if (lane < 4 * G) {  // the lanes holding distinct (token, head) results
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      *reinterpret_cast<float4*>(wl + (16 * t + tok) * G + (hi_half ? 4 : 0)) =
+          make_float4(e[t][0], e[t][1], e[t][2], e[t][3]);
+  }
+  // LDS accesses of one wave complete in order; this keeps the compiler
+  // from moving the reads below above the writes of other lanes
+  __asm__ volatile("" ::: "memory");
+
+  // latent-space value accumulation, slot layout
+  const int slot = lane / Mg::kLPR;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      const float* wr = wl + (16 * t + slot + RPW * u) * G;
+      float w[G];
+#pragma unroll
+      for (int h4 = 0; h4 < G; h4 += 4) {
+        const float4 w4 = *reinterpret_cast<const float4*>(wr + h4);
+        w[h4] = w4.x; w[h4 + 1] = w4.y; w[h4 + 2] = w4.z; w[h4 + 3] = w4.w;
+      }
+      float x[8];
+      Unpack<LatBF16>::run(st.v[t][u], x);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(w[h], x[j], acc[h][j]);
+      }
+    }
+  }
+  __asm__ volatile("" ::: "memory");
+}
+
+template <int R, int G>
+struct MPartLds {
+  PartLds<R, G> base;
+  float w[kWaves * MGeo<R, G>::kChunk * G];
+};
+
+template <int R, int G>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(MGeo<R, G>::kWavesPerEU)))
+void partition_mfma_kernel(PartitionArgs a) {
+  using Mg = MGeo<R, G>;
+  constexpr int KC = Mg::kKC, LPR = Mg::kLPR, CH = Mg::kChunk;
+
+  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
+  const int t0 = p * a.S;
+  const int t1 = min(t0 + a.S, len);
+  if (t0 >= t1) return;  // partition past the sequence: nothing to write
+  const int ntok = t1 - t0;
+
+  __shared__ MPartLds<R, G> lds;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int slot = lane / LPR, cc = lane % LPR;
+
+  const size_t row0 = ((size_t)b * a.Hkv + g) * (size_t)a.T + (size_t)t0;
+  const uint32_t nbytes = (uint32_t)ntok * Mg::kRowBytes;
+  const auto rk = make_rsrc(static_cast<const char*>(a.LK) + row0 * Mg::kRowBytes, nbytes);
+  const auto rv = make_rsrc(static_cast<const char*>(a.LV) + row0 * Mg::kRowBytes, nbytes);
+  // score layout: token lane % 16, 16-byte column group lane / 16 of each
+  // 64-byte (32-column) step; value layout: slot rows, 16 bytes per lane
+  const uint32_t koff = (uint32_t)((lane & 15) * Mg::kRowBytes + (lane >> 4) * 16);
+  const uint32_t voff = (uint32_t)(slot * Mg::kRowBytes + cc * 16);
+
+  constexpr int kAfter = LRATTN_MFMA_LATENTS_AFTER;
+  MStep<R, G> cur;
+  if (absorb_on_mfma(a)) {
+    if constexpr (kAfter < 2) load_mstep(cur, wave * CH, koff, voff, rk, rv);
+    absorb_mfma<R, G>(a, b, g, lds.base.qt);
+  } else {
+    AbsorbIn<R, G> ab;
+    absorb_issue<R, G>(a, b, g, ab);
+    if constexpr (kAfter == 0) load_mstep(cur, wave * CH, koff, voff, rk, rv);
+    absorb_stage_q<R, G>(a, ab, lds.base.q);
+    if constexpr (kAfter == 1) load_mstep(cur, wave * CH, koff, voff, rk, rv);
+    absorb_dot<R, G>(a, g, ab, lds.base.q, lds.base.qt);
+  }
+  if constexpr (kAfter == 2) load_mstep(cur, wave * CH, koff, voff, rk, rv);
+
+  // A operands: row lane % 16 is head (lane % 16) % G; k-group lane / 16
+  bf16x8 qa[3][KC];
+  {
+    const float* qrow = lds.base.qt + ((lane & 15) % G) * R + 8 * (lane >> 4);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      u32x4 w3[3];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        uint32_t t3[3][2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          // x == hi + mid + lo exactly: each remainder is exact in fp32 and
+          // the last one has at most 8 significant bits
+          const float x = qrow[32 * c + j + jj];
+          const uint16_t hi = f32_to_bf16_rne(x);
+          const float r1 = x - __uint_as_float((uint32_t)hi << 16);
+          const uint16_t mid = f32_to_bf16_rne(r1);
+          const float r2 = r1 - __uint_as_float((uint32_t)mid << 16);
+          t3[0][jj] = hi;
+          t3[1][jj] = mid;
+          t3[2][jj] = f32_to_bf16_rne(r2);
+        }
+#pragma unroll
+        for (int term = 0; term < 3; ++term) w3[term][j / 2] = t3[term][0] | (t3[term][1] << 16);
+      }
+#pragma unroll
+      for (int term = 0; term < 3; ++term) qa[term][c] = __builtin_bit_cast(bf16x8, w3[term]);
+    }
+  }
+
+  float mm[4], ll[4], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mm[i] = -FLT_MAX;
+    ll[i] = 0.f;
+  }
+  float* wl = lds.w + wave * CH * G;
+  for (int cb = wave * CH; cb < ntok; cb += kWaves * CH) {
+    MStep<R, G> nxt;
+    if constexpr (LRATTN_PREFETCH) load_mstep(nxt, cb + kWaves * CH, koff, voff, rk, rv);
+    if (cb + CH <= ntok)
+      compute_mstep<R, G, false>(cur, cb, ntok, lane, qa, mm, ll, acc, wl);
+    else
+      compute_mstep<R, G, true>(cur, cb, ntok, lane, qa, mm, ll, acc, wl);
+    if constexpr (LRATTN_PREFETCH) cur = nxt;
+    else load_mstep(cur, cb + kWaves * CH, koff, voff, rk, rv);
+  }
+
+  // ---- wave totals: exp-sums over the 16 token lanes, accumulators over
+  // the slots (one reference per head for the whole wave: plain sums)
+  float m[G], l[G];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x = group_sum<16>(ll[i]);
+    l[i] = readlane_f(x, 0);
+    m[i] = readlane_f(mm[i], 0);
+    if constexpr (G == 8) {
+      l[4 + i] = readlane_f(x, 16);
+      m[4 + i] = readlane_f(mm[i], 16);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
+    }
+  }
+  if (slot == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lds.base.acc[(wave * G + h) * R + cc * 8 + e] = acc[h][e];
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      lds.base.m[wave * G + h] = m[h];
+      lds.base.l[wave * G + h] = l[h];
+    }
+  }
+  __syncthreads();
+
+  write_records<R, G>(a, b, g, p, lds.base.acc, lds.base.m, lds.base.l);
 }
 
 // ------------------------------------------------------------------ combine
@@ -590,12 +1100,14 @@ void partition_kernel(PartitionArgs a) {
 // agent-scope fence per workgroup, i.e. an L2 writeback each, which measured
 // several times slower than the second launch.
 //
-// The kernel is latency-bound, so every load is issued as early as possible
-// and dependency chains are kept short:
+// The kernel is latency-bound, so its loads are issued together, before
+// anything waits, as raw buffer loads bounded by their slices with no branch
+// around any of them (a load past a slice returns zero):
 //   1. each thread loads its slice of B_V[g] (column i = tid % d, row block
-//      jb = tid / d of NB = kThreads / d blocks) before anything else;
-//   2. the head's records are staged into LDS with 16-byte loads, all issued
-//      together (one round trip per chunk of partitions);
+//      jb = tid / d of NB = kThreads / d blocks) and its share of the first
+//      chunk of the head's records (16 bytes per load) -- speculatively, as
+//      the records past seq_len's last partition are never folded;
+//   2. the chunk is staged in LDS (further chunks: one round trip each);
 //   3. thread (pg, j) folds coordinate j over partitions pg, pg + NPG, ...
 //      in ascending order (online log-sum-exp rule; NPG = kThreads / r
 //      groups shorten the chain), then the NPG groups are folded in
@@ -617,62 +1129,80 @@ struct CombineLds {
   float part[kThreads];  // [jb][i], NB * d == kThreads
 };
 
+// 16-byte loads of records [p0, p0 + n) of one head into this thread's
+// share of the stage (slots tid + k * kThreads).
 template <int R>
+__device__ __forceinline__ void load_chunk(const float* rec0, int p0, int n,
+                                           float4 (&v4)[CombineLds<R>::kStage / 4 / kThreads]) {
+  constexpr int RS = R + kRecPad;
+  const auto rr = make_rsrc(rec0 + (size_t)p0 * RS, (uint32_t)n * RS * 4u);
+#pragma unroll
+  for (int k = 0; k < CombineLds<R>::kStage / 4 / kThreads; ++k) {
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+        rr, (int)((threadIdx.x + k * kThreads) * 16u), 0, 0);
+    v4[k] = make_float4(__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
+                        __uint_as_float(w[3]));
+  }
+}
+
+template <int R, int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void combine_kernel(CombineArgs a) {
   using CL = CombineLds<R>;
   constexpr int RS = R + kRecPad;
   constexpr int kNPG = CL::kNPG, kChunk = CL::kChunk;
+  constexpr int kPer = CL::kStage / 4 / kThreads;
+  constexpr int NB = kThreads / D, RB = R / NB;
+  static_assert(NB * D == kThreads && RB * NB == R, "combine tiling");
   const int hq = blockIdx.x, b = blockIdx.y;
   const int g = hq / (a.Hq / a.Hkv);
   const int tid = threadIdx.x;
-  const int d = a.d;
   const MergeArgs& mg = a.merge;
 
-  // 1. B_V slice: rows [jb * RB, (jb + 1) * RB) of column i
-  const int NB = kThreads / d;  // d in {64, 128, 256}
-  const int RB = R / NB;
-  const int i_col = tid % d, jb = tid / d;
-  float bv[R];
+  // 1. B_V[g] rows [jb * RB, (jb + 1) * RB) of column i: the 32-bit word
+  //    holding each element (2-byte formats: the element's half of it)
+  const int i_col = tid % D, jb = tid / D;
+  const int fdt = mg.f_dtype;
+  const uint32_t fes = fdt == LRATTN_F32 ? 4u : 2u;
+  const auto rbv = make_rsrc(static_cast<const char*>(mg.BV) + (size_t)g * R * D * fes,
+                             (uint32_t)(R * D) * fes);
+  // at most 64 words in flight per thread (r = 128 with d = 256 takes four
+  // batches of 32, the later ones loaded at the projection)
+  constexpr int kB = RB <= 64 ? RB : 32;
+  uint32_t bw[kB];
+  auto load_bv = [&](int k0) {
 #pragma unroll
-  for (int k = 0; k < R; ++k) {
-    bv[k] = 0.f;
-    if (k < RB)
-      bv[k] = load_elem(mg.BV, ((size_t)g * R + jb * RB + k) * d + i_col, mg.f_dtype);
-  }
+    for (int k = 0; k < kB; ++k) {
+      const uint32_t off = (uint32_t)((jb * RB + k0 + k) * D + i_col) * fes;
+      bw[k] = __builtin_amdgcn_raw_buffer_load_b32(rbv, (int)(off & ~3u), 0, 0);
+    }
+  };
+  load_bv(0);
+  const float* rec0 = a.ws + ((size_t)b * a.Hq + hq) * (size_t)a.P * RS;
+  float4 v4[kPer];
+  load_chunk<R>(rec0, 0, min(kChunk, a.P), v4);
 
+  // No early exit for an empty sequence (np == 0): it runs the same steps
+  // with nothing to fold and writes a zero row.  A branch here would let the
+  // compiler move the loads above behind the seq_lens round trip.
   const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
   const int np = (len + a.S - 1) / a.S;
-  const size_t out_row0 = ((size_t)b * a.Hq + hq) * d;
-  if (np == 0) {
-    write_zero_rows(mg, out_row0, d);
-    return;
-  }
+  const size_t out_row0 = ((size_t)b * a.Hq + hq) * D;
 
   __shared__ CL sm;
   const float* stage = reinterpret_cast<const float*>(sm.stage);
-  const float* rec0 = a.ws + ((size_t)b * a.Hq + hq) * (size_t)a.P * RS;
   // kNPG * R <= kThreads (r = 48 leaves 16 threads without a group)
   const int pg = tid / R, j = tid - pg * R;
   const bool folds = pg < kNPG;
   float m = -FLT_MAX, L = 0.f, acc = 0.f;
   for (int p0 = 0; p0 < np; p0 += kChunk) {
-    const int n4 = min(kChunk, np - p0) * RS / 4;  // float4 in this chunk
-    if (p0 > 0) __syncthreads();                   // previous chunk consumed
-    // 2. stage: every load of a thread is issued before the first LDS store
-    constexpr int kPer = CL::kStage / 4 / kThreads;
-    float4 v4[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = tid + k * kThreads;
-      v4[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i < n4) v4[k] = reinterpret_cast<const float4*>(rec0 + (size_t)p0 * RS)[i];
+    if (p0 > 0) {
+      __syncthreads();  // previous chunk consumed
+      load_chunk<R>(rec0, p0, min(kChunk, np - p0), v4);
     }
+    // 2. stage (every slot is written: zeros past the chunk)
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = tid + k * kThreads;
-      if (i < n4) sm.stage[i] = v4[k];
-    }
+    for (int k = 0; k < kPer; ++k) sm.stage[tid + k * kThreads] = v4[k];
     __syncthreads();
     // 3. fold this chunk's partitions pg, pg + NPG, ...
     const int pc = folds ? min(kChunk, np - p0) : 0;
@@ -703,21 +1233,34 @@ void combine_kernel(CombineArgs a) {
       acc = fmaf(acc, fa, sm.v[item] * fb);
       m = nm;
     }
-    sm.vt[tid] = acc / L;
+    sm.vt[tid] = np > 0 ? acc / L : 0.f;
   }
   __syncthreads();
 
   // 4. row-block partial of out[i] = sum_j v~[j] * B_V[g][j][i]
+  const bool odd = i_col & 1;
   float o = 0.f;
 #pragma unroll
-  for (int k = 0; k < R; ++k) {
-    if (k < RB) o = fmaf(sm.vt[jb * RB + k], bv[k], o);
+  for (int k0 = 0; k0 < RB; k0 += kB) {
+    if (k0 > 0) {
+      __syncthreads();  // a scheduling boundary: the batches never overlap in registers
+      load_bv(k0);
+    }
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      const uint32_t w = bw[k];
+      const float two = fdt == LRATTN_BF16 ? (odd ? bf16_hi(w) : bf16_lo(w))
+                                           : (odd ? f16_hi(w) : f16_lo(w));
+      o = fmaf(sm.vt[jb * RB + k0 + k], fdt == LRATTN_F32 ? __uint_as_float(w) : two, o);
+    }
   }
-  sm.part[jb * d + i_col] = o;
+  sm.part[jb * D + i_col] = o;
   __syncthreads();
-  if (tid < d) {
+  if (tid < D) {
     float r = sm.part[tid];
-    for (int q = 1; q < NB; ++q) r += sm.part[q * d + tid];
+#pragma unroll
+    for (int q = 1; q < NB; ++q) r += sm.part[q * D + tid];
+    if (np == 0) r = 0.f;  // attention over no tokens: zero output
     const size_t oi = out_row0 + tid;
     if (mg.out_dtype == LRATTN_F32) static_cast<float*>(mg.out)[oi] = r;
     else static_cast<uint16_t*>(mg.out)[oi] = f32_to_bf16_rne(r);
@@ -763,9 +1306,26 @@ __global__ __launch_bounds__(kThreads) void probe_copy_kernel(u32x4* __restrict_
 
 // ------------------------------------------------------------ dispatch
 
+// The matrix-core score kernel serves bf16 latents, r a multiple of 32 and
+// 4 or 8 heads per kv-head.
+constexpr bool mfma_scores(int latent_dtype, int rank, int group) {
+  return LRATTN_MFMA_SCORES && latent_dtype == LRATTN_BF16 && rank % 32 == 0 &&
+         (group == 4 || group == 8);
+}
+
 template <class LT, int R>
 hipError_t launch_pg(int group, const PartitionArgs& a, hipStream_t s) {
   const dim3 grid(a.P, a.Hkv, a.B), block(kThreads);
+  if constexpr (mfma_scores(std::is_same<LT, LatBF16>::value ? LRATTN_BF16 : -1, R, 4)) {
+    if (group == 4) {
+      hipLaunchKernelGGL((partition_mfma_kernel<R, 4>), grid, block, 0, s, a);
+      return hipGetLastError();
+    }
+    if (group == 8) {
+      hipLaunchKernelGGL((partition_mfma_kernel<R, 8>), grid, block, 0, s, a);
+      return hipGetLastError();
+    }
+  }
   switch (group) {
     case 1: hipLaunchKernelGGL((partition_kernel<LT, R, 1>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((partition_kernel<LT, R, 2>), grid, block, 0, s, a); break;
@@ -792,7 +1352,13 @@ hipError_t launch_pr(int rank, int group, const PartitionArgs& a, hipStream_t s)
 
 template <int R>
 hipError_t launch_cg(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((combine_kernel<R>), dim3(a.Hq, a.B), dim3(kThreads), 0, s, a);
+  const dim3 grid(a.Hq, a.B), block(kThreads);
+  switch (a.d) {
+    case 64: hipLaunchKernelGGL((combine_kernel<R, 64>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((combine_kernel<R, 128>), grid, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((combine_kernel<R, 256>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -809,6 +1375,11 @@ bool partition_supported(int latent_dtype, int rank, int group) {
   const bool rank_ok = rank == 16 || rank == 32 || rank == 48 || rank == 64 || rank == 128;
   const bool group_ok = group == 1 || group == 2 || group == 4 || group == 8;
   return rank_ok && group_ok && rank * esz <= 256;
+}
+
+const char* partition_kernel_name(int latent_dtype, int rank, int group) {
+  if (!partition_supported(latent_dtype, rank, group)) return "";
+  return mfma_scores(latent_dtype, rank, group) ? "partition_mfma_kernel" : "partition_kernel";
 }
 
 hipError_t launch_partition(int latent_dtype, int rank, int group, const PartitionArgs& a,

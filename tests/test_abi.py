@@ -36,6 +36,7 @@ def test_library_loads_and_exports_everything_declared():
     L = lr.lib()
     names = lr.declared_symbols()
     assert {"lrattn_decode", "lrattn_workspace_size", "lrattn_status_string", "lrattn_plan",
+            "lrattn_partition_kernel",
             "lrattn_partition", "lrattn_combine", "lrattn_probe_read", "lrattn_probe_copy",
             "lrattn_probe_sink_floats", "lrattn_version"} <= set(names)
     for n in names:
@@ -152,3 +153,18 @@ def test_supported_matrix_plans():
                     b = ctypes.c_size_t()
                     st = lr.lib().lrattn_workspace_size(ctypes.byref(p), ctypes.byref(b))
                     assert st == (0 if r * esz <= 256 else -4), (lt, r, G, d)
+
+
+def test_partition_kernel_names():
+    # bf16 latents, r a multiple of 32, 4 or 8 heads per kv-head: matrix-core scores
+    for r in (16, 32, 48, 64, 128):
+        for G in (1, 2, 4, 8):
+            p = params(rank=r, num_q_heads=2 * G, num_kv_heads=2)
+            want = "partition_mfma_kernel" if r % 32 == 0 and G >= 4 else "partition_kernel"
+            assert lr.partition_kernel(p) == want, (r, G)
+    for lt in (lr.F32, lr.F16, lr.I8):
+        assert lr.partition_kernel(params(latent_dtype=lt, rank=32)) == "partition_kernel"
+    assert lr.lib().lrattn_partition_kernel(ctypes.byref(params(head_dim=96))) is None
+    assert lr.lib().lrattn_partition_kernel(None) is None
+    with pytest.raises(lr.LrattnError):
+        lr.partition_kernel(params(rank=24))

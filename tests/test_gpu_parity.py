@@ -69,7 +69,7 @@ def test_full_size(name):
     assert err <= TOL[w.latent_dtype], err
 
 
-@pytest.mark.parametrize("name", ["ragged", "int8"])
+@pytest.mark.parametrize("name", ["ragged", "int8", "gqa_vlm"])
 def test_nan_padding_never_read(name):
     kw = dict(SMALL[name])
     a = workloads.make(name, pad="zero", **kw)
@@ -187,6 +187,49 @@ def test_instantiation_matrix(lt, r, G, d):
     got = run_decode(w, num_splits=3).cpu().numpy()
     err = rel_rowmax(got, _full_oracle(w))
     assert err <= TOL[lt], err
+
+
+@pytest.mark.parametrize("r,G", [(32, 4), (32, 8), (64, 4), (64, 8), (128, 4), (128, 8)])
+def test_matrix_core_scores_exact_inputs(r, G):
+    """bf16 latents with 4 or 8 heads per kv-head are scored on the matrix
+    cores, with q~ split exactly into three bf16 terms.  Scores are then fp32
+    sums of exact products, as on the VALU path, so the result must agree with
+    the oracle to fp32 accumulation accuracy: far inside the bf16 gate, and
+    tight enough that a q~ rounded to one or two bf16 terms fails.  Lengths
+    cover empty, partial and full 16-token tiles; q_std = 4 spreads the logits
+    so the reference max moves within partitions."""
+    lens = [1, 15, 16, 17, 33, 200, 511, 700]
+    w = workloads.make("gqa_vlm", seed=300 + r + G, B=len(lens), Hq=2 * G, Hkv=2, r=r, T=700,
+                       seq_lens=lens, q_std=4.0, factor_std=1.0 / np.sqrt(r))
+    dev = to_device(w)
+    ref = _full_oracle(w)
+    for splits in (1, 3, 0, 700):
+        say(f"matrix-core scores r={r} G={G} splits={splits}")
+        got = run_decode(w, dev, num_splits=splits).cpu().numpy()
+        err = rel_rowmax(got, ref)
+        say(f"  err {err:.3e}")
+        assert err <= 2e-5, err
+
+
+@pytest.mark.parametrize("qdt,fdt", [("bf16", "bf16"), ("f16", "f16"), ("f32", "bf16"),
+                                     ("bf16", "f16"), ("f32", "f32"), ("f16", "f32")])
+@pytest.mark.parametrize("G,d", [(4, 64), (4, 256), (1, 128), (8, 128)])
+def test_absorption_formats(qdt, fdt, G, d):
+    """q . B_K^T runs on the matrix cores when q and B_K share a 2-byte
+    format and on the VALU otherwise; both keep exact products and fp32
+    sums, so every pairing must match the oracle to fp32 accuracy.  d = 64
+    leaves half of the 32-wide k-steps of a chunk empty, d = 256 takes two
+    chunks; G = 1 runs the VALU partition kernel, G = 4 and 8 the
+    matrix-core one."""
+    lens = [300, 17, 1]
+    w = workloads.make("gqa_vlm", seed=400 + G + d, B=len(lens), Hq=2 * G, Hkv=2, d=d, r=64,
+                       T=300, seq_lens=lens, q_dtype=qdt, factor_dtype=fdt,
+                       factor_std=1.0 / np.sqrt(64))
+    say(f"absorption q={qdt} factors={fdt} G={G} d={d}")
+    got = run_decode(w, num_splits=2).cpu().numpy()
+    err = rel_rowmax(got, _full_oracle(w))
+    say(f"  err {err:.3e}")
+    assert err <= 2e-5, err
 
 
 def test_guard_bands_untouched():
