@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe", action="store_true",
                     help="also run the HBM read/copy probe kernels (calibration)")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense-cache baseline (same workload, K and V of d columns)")
     return ap.parse_args()
 
 
@@ -198,20 +200,28 @@ def main():
     region_ms = e_beg.elapsed_time(e_end)
     gpu_out = out.cpu().numpy().astype(np.float64)
 
-    # ---- the dominant kernel (partition) alone, launch by launch: HIP events
-    # on the stream it is launched on
+    # ---- the dominant kernel (partition) alone: K launches back to back
+    # between two HIP events on the stream they are launched on (the average
+    # launch duration), then K launches each between its own pair of events
+    # (an isolated launch, which adds the launch latency)
     for i in range(min(args.warmup, 5)):
         decs[i % copies].partition()
+    torch.cuda.synchronize()
+    r_beg, r_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r_beg.record()
+    for i in range(K):
+        decs[i % copies].partition()
+    r_end.record()
+    torch.cuda.synchronize()
+    launch_mean_s = r_beg.elapsed_time(r_end) / K / 1e3
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(K)]
-    torch.cuda.synchronize()
     for i in range(K):
         ev[i][0].record()
         decs[i % copies].partition()
         ev[i][1].record()
     torch.cuda.synchronize()
     launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    launch_mean_s = float(launch_ms.mean()) / 1e3
 
     # algorithmic bytes of one partition launch: valid latent rows (K and V),
     # their int8 scales, q and B_K
@@ -250,13 +260,16 @@ def main():
             "traffic": traffic,
             "kernel": lr.partition_kernel(p),
             "mean_launch_us": launch_mean_s * 1e6,
-            "min_launch_us": float(launch_ms.min()) * 1e3,
+            "isolated_launch_us": float(launch_ms.mean()) * 1e3,
+            "min_isolated_launch_us": float(launch_ms.min()) * 1e3,
             "algorithmic_bytes_per_launch": part_bytes,
         },
         "step_algorithmic_GBps": ab["total"] / (ms_per_step / 1e3) / 1e9,
         "timed_region_event_ms": region_ms,
         "input_generation_s": gen_s,
     }
+    if not args.no_dense:
+        line["dense_baseline"] = dense_baseline(w, torch, lr, args, ms_per_step)
     if args.probe:
         line["probe"] = run_probe(torch, lr)
     if not args.no_cpu_baseline:
@@ -264,6 +277,59 @@ def main():
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
+
+
+def dense_baseline(w, torch, lr, args, compressed_ms):
+    """The same workload over an uncompressed cache: K, V [B, Hkv, T, d] in
+    the latent storage type (random values drawn on the device; the content
+    does not change the work), timed like the main loop.  None when such rows
+    exceed what the kernels take (d * sizeof > 256 bytes)."""
+    esz = {"f32": 4, "bf16": 2, "f16": 2, "i8": 1}[w.latent_dtype]
+    d = w.head_dim
+    if d * esz > 256:
+        return None
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1000 + d)
+    shape = (w.batch, w.num_kv_heads, w.max_seq_len, d)
+
+    def draw():
+        if w.latent_dtype == "i8":
+            return torch.randint(-127, 128, shape, generator=g, device="cuda", dtype=torch.int8)
+        dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.latent_dtype]
+        return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(dt)
+
+    import numpy as np
+    q = torch.randn((w.batch, w.num_q_heads, d), generator=g, device="cuda").to(
+        torch.float32 if w.q_dtype == "f32" else
+        torch.float16 if w.q_dtype == "f16" else torch.bfloat16)
+    seq = torch.from_numpy(w.seq_lens.astype(np.int32)).cuda()
+    sc = None if w.scales is None else torch.from_numpy(w.scales).cuda()
+    per_copy = 2 * math.prod(shape) * esz
+    copies = max(1, min(4, math.ceil(ROTATE_BYTES / per_copy)))
+    out = torch.empty((w.batch, w.num_q_heads, d), dtype=torch.float32, device="cuda")
+    decs, keep = [], []
+    for _ in range(copies):
+        K, V = draw(), draw()
+        keep.append((K, V))
+        decs.append(lr.DenseDecoder(q, K, V, seq, sc, out=out, num_splits=args.num_splits))
+    for i in range(args.warmup):
+        decs[i % copies]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        decs[i % copies]()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    valid = int(w.seq_lens.sum())
+    alg = valid * w.num_kv_heads * (2 * d * esz + (8 if w.latent_dtype == "i8" else 0))
+    P, S = decs[0].plan
+    res = dict(ms_per_step=ms, tokens_per_s=w.batch / (ms / 1e3),
+               cache_bytes_per_step=alg, cache_GBps=alg / (ms / 1e3) / 1e9,
+               kernel=lr.partition_kernel(decs[0].params), num_splits=P,
+               speedup_of_factored=ms / compressed_ms)
+    del decs, keep
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_probe(torch, lr):

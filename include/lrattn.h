@@ -204,6 +204,30 @@ int lrattn_combine(const lrattn_params* p,
                    size_t workspace_bytes,
                    lrattn_stream stream);
 
+/*
+ * Dense baseline on the same kernels: single-token decode attention over an
+ * uncompressed cache, for comparison with the factored cache (the pages
+ * measure their kernels against dense Flash Decoding: WSVD section 4,
+ * FlashSVD's dense-cache path).  For every b, h with g = h / (Hq / Hkv):
+ *   out[b,h,:] = sum_t softmax_t(scale * <q[b,h,:], K[b,g,t,:]>) V[b,g,t,:]
+ *   K, V     [B, Hkv, T, d]  latent_dtype (int8 takes `scales` as above)
+ * `p` is the same parameter block with rank == head_dim (else
+ * LRATTN_ERR_SHAPE); factor_dtype is not used but must be a valid factor
+ * code.  Workspace size, plan, alignment, ownership, seq_lens handling,
+ * errors and determinism are those of lrattn_decode, with d * sizeof(K) <=
+ * 256 bytes (d = 64, or d = 128 with 2- or 1-byte K and V).
+ */
+int lrattn_dense_decode(const lrattn_params* p,
+                        const void* q,
+                        const void* K,
+                        const void* V,
+                        const float* scales,
+                        const int32_t* seq_lens,
+                        void* out,
+                        void* workspace,
+                        size_t workspace_bytes,
+                        lrattn_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

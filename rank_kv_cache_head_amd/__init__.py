@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.lrattn_status_string.argtypes = [ctypes.c_int]
         L.lrattn_plan.argtypes = [_PP, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
         L.lrattn_workspace_size.argtypes = [_PP, ctypes.POINTER(ctypes.c_size_t)]
+        L.lrattn_dense_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                          ctypes.c_size_t, _VP]
         L.lrattn_partition_kernel.argtypes = [_PP]
         L.lrattn_partition_kernel.restype = ctypes.c_char_p
         L.lrattn_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -87,7 +89,8 @@ def lib() -> ctypes.CDLL:
         L.lrattn_probe_read.argtypes = [_VP, ctypes.c_size_t, _VP, _VP]
         L.lrattn_probe_copy.argtypes = [_VP, _VP, ctypes.c_size_t, _VP]
         for fn in ("lrattn_plan", "lrattn_workspace_size", "lrattn_decode", "lrattn_partition",
-                   "lrattn_combine", "lrattn_probe_read", "lrattn_probe_copy"):
+                   "lrattn_combine", "lrattn_dense_decode", "lrattn_probe_read",
+                   "lrattn_probe_copy"):
             getattr(L, fn).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -223,6 +226,37 @@ def decode(q, L_K, L_V, B_K, B_V, seq_lens, scales=None, *, out=None, workspace=
     return out
 
 
+def dense_params_for(q, K, *, out_dtype=None, softmax_scale=None, num_splits: int = 0) -> Params:
+    """Parameter block for the dense baseline: q [B,Hq,d], K [B,Hkv,T,d] (rank = d)."""
+    import torch
+    if q.dim() != 3 or K.dim() != 4 or K.shape[0] != q.shape[0] or K.shape[3] != q.shape[2]:
+        raise ValueError("q [B,Hq,d], K [B,Hkv,T,d] expected")
+    B, Hq, d = q.shape
+    _, Hkv, T, _ = K.shape
+    od = F32 if out_dtype in (None, torch.float32) else (BF16 if out_dtype == torch.bfloat16 else -1)
+    qd = _dtype_code(q)
+    return Params(B, Hq, Hkv, d, d, T, qd, _dtype_code(K), qd, od,
+                  float(softmax_scale) if softmax_scale else 0.0, int(num_splits))
+
+
+def dense_decode(q, K, V, seq_lens, scales=None, *, out=None, workspace=None,
+                 softmax_scale=None, num_splits: int = 0, out_dtype=None, stream=None):
+    """lrattn_dense_decode: the same decode over an uncompressed cache K, V [B,Hkv,T,d]."""
+    import torch
+    p = dense_params_for(q, K, out_dtype=out_dtype, softmax_scale=softmax_scale,
+                         num_splits=num_splits)
+    _check_shapes(p, V, None, scales, seq_lens)
+    if out is None:
+        out = torch.empty((p.batch, p.num_q_heads, p.head_dim),
+                          dtype=torch.float32 if p.out_dtype == F32 else torch.bfloat16,
+                          device=q.device)
+    ws, ws_bytes = _workspace(p, workspace, q.device)
+    st = lib().lrattn_dense_decode(ctypes.byref(p), _ptr(q), _ptr(K), _ptr(V), _ptr(scales),
+                                   _ptr(seq_lens), _ptr(out), _ptr(ws), ws_bytes, _stream(stream))
+    _check(st, "lrattn_dense_decode")
+    return out
+
+
 def partition(q, L_K, L_V, B_K, seq_lens, scales=None, *, workspace=None, softmax_scale=None,
               num_splits: int = 0, stream=None):
     """lrattn_partition alone; returns the workspace tensor holding the partials."""
@@ -317,4 +351,30 @@ class Decoder:
     def combine(self):
         fn, args = self._combine
         _check(fn(*args), "lrattn_combine")
+        return self.out
+
+
+class DenseDecoder:
+    """lrattn_dense_decode on fixed buffers, marshalled once (see Decoder)."""
+
+    def __init__(self, q, K, V, seq_lens, scales=None, *, out=None, workspace=None,
+                 softmax_scale=None, num_splits: int = 0, out_dtype=None, stream=None):
+        import torch
+        p = dense_params_for(q, K, out_dtype=out_dtype, softmax_scale=softmax_scale,
+                             num_splits=num_splits)
+        _check_shapes(p, V, None, scales, seq_lens)
+        if out is None:
+            out = torch.empty((p.batch, p.num_q_heads, p.head_dim),
+                              dtype=torch.float32 if p.out_dtype == F32 else torch.bfloat16,
+                              device=q.device)
+        ws, ws_bytes = _workspace(p, workspace, q.device)
+        self.params, self.out, self.workspace = p, out, ws
+        self.plan = plan(p)
+        self._keep = (q, K, V, seq_lens, scales)
+        self._fn = lib().lrattn_dense_decode
+        self._args = (ctypes.byref(p), _ptr(q), _ptr(K), _ptr(V), _ptr(scales), _ptr(seq_lens),
+                      _ptr(out), _ptr(ws), ws_bytes, _stream(stream))
+
+    def __call__(self):
+        _check(self._fn(*self._args), "lrattn_dense_decode")
         return self.out

@@ -260,6 +260,29 @@ int lrattn_decode(const lrattn_params* p, const void* q, const void* L_K, const 
   return LRATTN_OK;
 }
 
+int lrattn_dense_decode(const lrattn_params* p, const void* q, const void* K, const void* V,
+                        const float* scales, const int32_t* seq_lens, void* out,
+                        void* workspace, size_t workspace_bytes, lrattn_stream stream) {
+  Plan pl;
+  int st = check_params(p, &pl);
+  if (st == LRATTN_OK && p->rank != p->head_dim) st = LRATTN_ERR_SHAPE;
+  if (st == LRATTN_OK && (!q || !K || !V || !seq_lens || !out)) st = LRATTN_ERR_NULL;
+  if (st == LRATTN_OK && (p->latent_dtype == LRATTN_I8) != (scales != nullptr)) st = LRATTN_ERR_NULL;
+  if (st == LRATTN_OK && (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(seq_lens) ||
+                          !aligned16(out) || (scales && !aligned16(scales))))
+    st = LRATTN_ERR_ALIGN;
+  if (st == LRATTN_OK) st = check_workspace(p, pl, workspace, workspace_bytes);
+  if (st != LRATTN_OK) return st;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // no factors: the kernels take q~ = scale * q and write v~ as the output
+  const auto pa = partition_args(p, pl, q, K, V, nullptr, scales, seq_lens, workspace);
+  if (lrattn::launch_partition(p->latent_dtype, p->rank, group_of(p), pa, s) != hipSuccess)
+    return LRATTN_ERR_HIP;
+  const auto ca = combine_args(p, pl, nullptr, seq_lens, out, workspace);
+  if (lrattn::launch_combine(group_of(p), ca, s) != hipSuccess) return LRATTN_ERR_HIP;
+  return LRATTN_OK;
+}
+
 size_t lrattn_probe_sink_floats(void) { return (size_t)lrattn::kProbeBlocks; }
 
 int lrattn_probe_read(const void* src, size_t bytes, float* sink, lrattn_stream stream) {

@@ -388,7 +388,8 @@ __device__ __forceinline__ float piece_sum(float x, int n) {
 // Every product is exact in fp32 and the sums run in fp32.
 //
 // When q and B_K share a 2-byte format the product runs on the matrix cores
-// (absorb_mfma below).  Otherwise on the VALU, in three steps, so that a
+// (absorb_mfma_issue / absorb_mfma_finish below).  Otherwise on the VALU,
+// in three steps, so that a
 // kernel can place its first latent loads among them:
 // absorb_issue loads this thread's q values and its first batch of B_K
 // pieces (8 consecutive elements of one factor row) into registers;
@@ -548,75 +549,168 @@ __device__ __forceinline__ void absorb_dot(const PartitionArgs& a, int g, Absorb
 // bytes of q or of one B_K row, loaded straight into the operand register.
 // The result, lane l register i = (head 4 * (l / 16) + i, column l % 16),
 // goes to qt_lds.  All loads of a 4-step chunk are in flight together
-// (d = 256 takes two chunks).  Ends with a barrier.
+// (d = 256 takes two chunks).  absorb_mfma_finish ends with a barrier.
 __device__ __forceinline__ bool absorb_on_mfma(const PartitionArgs& a) {
   return a.q_dtype == a.f_dtype && a.q_dtype != LRATTN_F32;
 }
 
+// Operand registers of one 4-step chunk; absorb_mfma_issue loads the first
+// chunk so that a kernel can issue its first latent loads before the MMAs
+// wait (loads return in issue order: these come back first).
+template <int R>
+struct MfmaAbsorbIn {
+  static constexpr int kNT = R / 16;                        // column tiles: 1, 2, 3, 4 or 8
+  static constexpr int kTPW = (kNT + kWaves - 1) / kWaves;  // tiles per wave: 1 or 2
+  u32x4 qa[4];
+  u32x4 fb[kTPW][4];
+};
+
 template <int R, int G>
-__device__ __forceinline__ void absorb_mfma(const PartitionArgs& a, int b, int g, float* qt_lds) {
-  constexpr int NT = R / 16;                        // column tiles: 1, 2, 3, 4 or 8
-  constexpr int TPW = (NT + kWaves - 1) / kWaves;   // tiles per wave: 1 or 2
+__device__ __forceinline__ void absorb_mfma_load(const PartitionArgs& a, int b, int g, int k0,
+                                                 MfmaAbsorbIn<R>& in) {
+  using AI = MfmaAbsorbIn<R>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int d = a.d, ksteps = d >> 5;               // 2, 4 or 8
+  const int d = a.d, ksteps = d >> 5;  // 2, 4 or 8
   const int row = lane & 15, kg = lane >> 4;
-  const bool bf = a.q_dtype == LRATTN_BF16;
   const size_t q0 = ((size_t)b * a.Hq + (size_t)g * G) * d;
   const auto rq = make_rsrc(static_cast<const uint16_t*>(a.q) + q0, (uint32_t)(G * d) * 2u);
   const auto rf = make_rsrc(static_cast<const uint16_t*>(a.BK) + (size_t)g * R * d,
                             (uint32_t)(R * d) * 2u);
-  f32x4 acc[TPW];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto chunk = [&](int k0) {
-    u32x4 qa[4], fb[TPW][4];
+  for (int kk = 0; kk < 4; ++kk) {
+    const int ks = k0 + kk;
+    const bool kv = ks < ksteps;
+    const uint32_t qoff = row < G && kv ? (uint32_t)(row * d + 32 * ks + 8 * kg) * 2u : kOffNone;
+    in.qa[kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qoff, 0, 0);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int ks = k0 + kk;
-      const bool kv = ks < ksteps;
-      const uint32_t qoff = row < G && kv ? (uint32_t)(row * d + 32 * ks + 8 * kg) * 2u : kOffNone;
-      qa[kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qoff, 0, 0);
-#pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const int nt = wave + kWaves * t;
-        const uint32_t foff =
-            nt < NT && kv ? (uint32_t)((16 * nt + row) * d + 32 * ks + 8 * kg) * 2u : kOffNone;
-        fb[t][kk] = __builtin_amdgcn_raw_buffer_load_b128(rf, (int)foff, 0, 0);
-      }
+    for (int t = 0; t < AI::kTPW; ++t) {
+      const int nt = wave + kWaves * t;
+      const uint32_t foff =
+          nt < AI::kNT && kv ? (uint32_t)((16 * nt + row) * d + 32 * ks + 8 * kg) * 2u : kOffNone;
+      in.fb[t][kk] = __builtin_amdgcn_raw_buffer_load_b128(rf, (int)foff, 0, 0);
     }
+  }
+}
+
+template <int R, int G>
+__device__ __forceinline__ void absorb_mfma_issue(const PartitionArgs& a, int b, int g,
+                                                  MfmaAbsorbIn<R>& in) {
+  absorb_mfma_load<R, G>(a, b, g, 0, in);
+}
+
+template <int R, int G>
+__device__ __forceinline__ void absorb_mfma_finish(const PartitionArgs& a, int b, int g,
+                                                   MfmaAbsorbIn<R>& in, float* qt_lds) {
+  using AI = MfmaAbsorbIn<R>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const bool bf = a.q_dtype == LRATTN_BF16;
+  f32x4 acc[AI::kTPW];
+#pragma unroll
+  for (int t = 0; t < AI::kTPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&]() {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
+      for (int t = 0; t < AI::kTPW; ++t) {
         if (bf)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[kk]),
-                                                           __builtin_bit_cast(bf16x8, fb[t][kk]),
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, in.qa[kk]),
+                                                           __builtin_bit_cast(bf16x8, in.fb[t][kk]),
                                                            acc[t], 0, 0, 0);
         else
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, qa[kk]),
-                                                          __builtin_bit_cast(f16x8, fb[t][kk]),
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, in.qa[kk]),
+                                                          __builtin_bit_cast(f16x8, in.fb[t][kk]),
                                                           acc[t], 0, 0, 0);
       }
     }
   };
-  chunk(0);                   // steps 0..3 (zero operands past d)
-  if (ksteps > 4) chunk(4);   // d = 256
+  mma();                  // steps 0..3 (zero operands past d)
+  if (a.d > 128) {        // d = 256: steps 4..7
+    absorb_mfma_load<R, G>(a, b, g, 4, in);
+    mma();
+  }
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
+  for (int t = 0; t < AI::kTPW; ++t) {
     const int nt = wave + kWaves * t;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * kg + i;
-      if (nt < NT && h < G) qt_lds[h * R + 16 * nt + row] = acc[t][i] * a.qscale;
+      if (nt < AI::kNT && h < G) qt_lds[h * R + 16 * nt + row] = acc[t][i] * a.qscale;
     }
   }
   __syncthreads();
 }
 
+// Dense cache (no factors, r = d): q~ = qscale * q.  The loads are those of
+// absorb_issue's q part; threads without q values store into qt_lds's
+// padding, so no load sits behind a branch.
+template <int R, int G>
+__device__ __forceinline__ void identity_issue(const PartitionArgs& a, int b, int g,
+                                               AbsorbIn<R, G>& in) {
+  using AI = AbsorbIn<R, G>;
+  const int tid = threadIdx.x, d = a.d;
+  const uint32_t qes = a.q_dtype == LRATTN_F32 ? 4u : 2u;
+  const size_t q0 = ((size_t)b * a.Hq + (size_t)g * G) * d;
+  const auto rq = make_rsrc(static_cast<const char*>(a.q) + q0 * qes, (uint32_t)(G * d) * qes);
+#pragma unroll
+  for (int k = 0; k < AI::kQLoads; ++k)
+    in.qw[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)((tid + k * kThreads) * 16u), 0, 0);
+}
+
+template <int R, int G>
+__device__ __forceinline__ void identity_finish(const PartitionArgs& a, AbsorbIn<R, G>& in,
+                                                float* qt_lds) {
+  using AI = AbsorbIn<R, G>;
+  const int tid = threadIdx.x, d = a.d;  // d == R
+  const bool q32 = a.q_dtype == LRATTN_F32;
+  const int epc = q32 ? 4 : 8;
+#pragma unroll
+  for (int k = 0; k < AI::kQLoads; ++k) {
+    const int e0 = (tid + k * kThreads) * epc;
+    float* dst = e0 < G * d ? qt_lds + e0 : qt_lds + G * R;  // rows of R == d: [h][j] is e0
+    float x[8];
+    words_to_floats(in.qw[k], a.q_dtype, x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = x[e] * a.qscale;
+    if (!q32) {
+#pragma unroll
+      for (int e = 4; e < 8; ++e) dst[e] = x[e] * a.qscale;
+    }
+  }
+  __syncthreads();
+}
+
+// The partition prologue: q~ into qt_lds (fp32 [G][R]), with `issue` (the
+// first latent loads) placed at position kAfter: 0 first, 1 once q is in
+// flight / staged, 2 after the absorption.
+template <int R, int G, int kAfter, class Issue>
+__device__ __forceinline__ void prologue(const PartitionArgs& a, int b, int g, float* q_lds,
+                                         float* qt_lds, Issue&& issue) {
+  if (a.BK == nullptr) {
+    AbsorbIn<R, G> in;
+    identity_issue<R, G>(a, b, g, in);
+    if constexpr (kAfter < 2) issue();
+    identity_finish<R, G>(a, in, qt_lds);
+  } else if (absorb_on_mfma(a)) {
+    MfmaAbsorbIn<R> ai;
+    absorb_mfma_issue<R, G>(a, b, g, ai);
+    if constexpr (kAfter < 2) issue();
+    absorb_mfma_finish<R, G>(a, b, g, ai, qt_lds);
+  } else {
+    AbsorbIn<R, G> ab;
+    absorb_issue<R, G>(a, b, g, ab);
+    if constexpr (kAfter == 0) issue();
+    absorb_stage_q<R, G>(a, ab, q_lds);
+    if constexpr (kAfter == 1) issue();
+    absorb_dot<R, G>(a, g, ab, q_lds, qt_lds);
+  }
+  if constexpr (kAfter == 2) issue();
+}
+
 template <int R, int G>
 struct PartLds {
   float q[G * kMaxHeadDim + 8];  // + padding for threads without q values
-  float qt[G * R];
+  float qt[G * R + 8];  // + padding (dense prologue)
   float acc[kWaves * G * R];
   float m[kWaves * G];
   float l[kWaves * G];
@@ -694,18 +788,9 @@ void partition_kernel(PartitionArgs a) {
   // q and B_K are requested first, then the first step's latents; the
   // absorption then runs while the latents are in flight.
   Step<LT, R, G> cur;
-  if (absorb_on_mfma(a)) {
-    if constexpr (LRATTN_LATENTS_AFTER < 2) load_step(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv);
-    absorb_mfma<R, G>(a, b, g, qt_lds);
-  } else {
-    AbsorbIn<R, G> ab;
-    absorb_issue<R, G>(a, b, g, ab);
-    if constexpr (LRATTN_LATENTS_AFTER == 0) load_step(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv);
-    absorb_stage_q<R, G>(a, ab, q_lds);
-    if constexpr (LRATTN_LATENTS_AFTER == 1) load_step(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv);
-    absorb_dot<R, G>(a, g, ab, q_lds, qt_lds);
-  }
-  if constexpr (LRATTN_LATENTS_AFTER == 2) load_step(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv);
+  prologue<R, G, LRATTN_LATENTS_AFTER>(a, b, g, q_lds, qt_lds, [&]() {
+    load_step(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv);
+  });
 
   QtView<LT, R, G> qt;
   // idle lanes (cc >= kAct) load zeros, so their q~ is never read
@@ -984,20 +1069,10 @@ void partition_mfma_kernel(PartitionArgs a) {
   const uint32_t koff = (uint32_t)((lane & 15) * Mg::kRowBytes + (lane >> 4) * 16);
   const uint32_t voff = (uint32_t)(slot * Mg::kRowBytes + cc * 16);
 
-  constexpr int kAfter = LRATTN_MFMA_LATENTS_AFTER;
   MStep<R, G> cur;
-  if (absorb_on_mfma(a)) {
-    if constexpr (kAfter < 2) load_mstep(cur, wave * CH, koff, voff, rk, rv);
-    absorb_mfma<R, G>(a, b, g, lds.base.qt);
-  } else {
-    AbsorbIn<R, G> ab;
-    absorb_issue<R, G>(a, b, g, ab);
-    if constexpr (kAfter == 0) load_mstep(cur, wave * CH, koff, voff, rk, rv);
-    absorb_stage_q<R, G>(a, ab, lds.base.q);
-    if constexpr (kAfter == 1) load_mstep(cur, wave * CH, koff, voff, rk, rv);
-    absorb_dot<R, G>(a, g, ab, lds.base.q, lds.base.qt);
-  }
-  if constexpr (kAfter == 2) load_mstep(cur, wave * CH, koff, voff, rk, rv);
+  prologue<R, G, LRATTN_MFMA_LATENTS_AFTER>(a, b, g, lds.base.q, lds.base.qt, [&]() {
+    load_mstep(cur, wave * CH, koff, voff, rk, rv);
+  });
 
   // A operands: row lane % 16 is head (lane % 16) % G; k-group lane / 16
   bf16x8 qa[3][KC];
@@ -1164,8 +1239,11 @@ void combine_kernel(CombineArgs a) {
   const int i_col = tid % D, jb = tid / D;
   const int fdt = mg.f_dtype;
   const uint32_t fes = fdt == LRATTN_F32 ? 4u : 2u;
-  const auto rbv = make_rsrc(static_cast<const char*>(mg.BV) + (size_t)g * R * D * fes,
-                             (uint32_t)(R * D) * fes);
+  // dense cache (no B_V, r == d): an empty resource, every load returns zero
+  const bool dense = mg.BV == nullptr;
+  const auto rbv = dense ? make_rsrc(nullptr, 0u)
+                         : make_rsrc(static_cast<const char*>(mg.BV) + (size_t)g * R * D * fes,
+                                     (uint32_t)(R * D) * fes);
   // at most 64 words in flight per thread (r = 128 with d = 256 takes four
   // batches of 32, the later ones loaded at the projection)
   constexpr int kB = RB <= 64 ? RB : 32;
@@ -1260,7 +1338,8 @@ void combine_kernel(CombineArgs a) {
     float r = sm.part[tid];
 #pragma unroll
     for (int q = 1; q < NB; ++q) r += sm.part[q * D + tid];
-    if (np == 0) r = 0.f;  // attention over no tokens: zero output
+    if (dense) r = tid < R ? sm.vt[tid] : 0.f;  // r == d: v~ is the output row
+    if (np == 0) r = 0.f;       // attention over no tokens: zero output
     const size_t oi = out_row0 + tid;
     if (mg.out_dtype == LRATTN_F32) static_cast<float*>(mg.out)[oi] = r;
     else static_cast<uint16_t*>(mg.out)[oi] = f32_to_bf16_rne(r);

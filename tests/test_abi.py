@@ -168,3 +168,22 @@ def test_partition_kernel_names():
     assert lr.lib().lrattn_partition_kernel(None) is None
     with pytest.raises(lr.LrattnError):
         lr.partition_kernel(params(rank=24))
+
+
+def test_dense_decode_validates_on_host():
+    L = lr.lib()
+    p = params(rank=128)  # rank == head_dim
+    def call(p, q=ALIGNED, k=ALIGNED, v=ALIGNED, sc=None, seq=ALIGNED, out=ALIGNED, ws=ALIGNED,
+             ws_bytes=0):
+        return L.lrattn_dense_decode(ctypes.byref(p), q, k, v, sc, seq, out, ws, ws_bytes, None)
+    assert call(params(rank=64)) == -2          # rank must equal head_dim
+    assert call(p, k=None) == -1
+    assert call(p, out=None) == -1
+    assert call(p, sc=ALIGNED) == -1            # scales with bf16 K/V
+    assert call(params(rank=128, latent_dtype=lr.I8)) == -1
+    assert call(p, v=MISALIGNED) == -5
+    assert call(p, ws=None) == -6
+    assert call(p, ws_bytes=lr.workspace_size(p) - 1) == -6
+    assert call(params(rank=128, latent_dtype=lr.F32)) == -4   # 512-byte rows
+    assert L.lrattn_dense_decode(None, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, ALIGNED, ALIGNED,
+                                 1 << 30, None) == -1

@@ -232,6 +232,62 @@ def test_absorption_formats(qdt, fdt, G, d):
     assert err <= 2e-5, err
 
 
+def _dense_case(lt, d, G, seed):
+    """A dense cache drawn like the factored one with r = d; the oracle runs
+    it with identity factors (K = L . I)."""
+    base = "int8" if lt == "i8" else "gqa_vlm"
+    lens = [500, 129, 16, 1]
+    kw = dict(B=len(lens), Hq=2 * G, Hkv=2, d=d, r=d, T=500, seq_lens=lens,
+              factor_std=1.0 / np.sqrt(d))
+    if lt != "i8":
+        kw["latent_dtype"] = lt
+    return workloads.make(base, seed=seed, **kw)
+
+
+def _dense_oracle(w):
+    q, K, V, _, _, lens, sc = f64_args(w)
+    eye = np.broadcast_to(np.eye(w.head_dim), (w.num_kv_heads, w.head_dim, w.head_dim))
+    return oracle.decode(q, K, V, eye, eye, lens, scales=sc, softmax_scale=w.softmax_scale)
+
+
+@pytest.mark.parametrize("lt,d,G", [("bf16", 128, 4), ("bf16", 128, 1), ("bf16", 64, 8),
+                                    ("f16", 128, 2), ("f32", 64, 4), ("i8", 128, 1),
+                                    ("i8", 64, 4)])
+def test_dense_decode_matches_oracle(lt, d, G):
+    """The dense baseline is exact attention over the uncompressed cache."""
+    import rank_kv_cache_head_amd as lr
+    w = _dense_case(lt, d, G, seed=500 + d + G)
+    dev = to_device(w)
+    say(f"dense {lt} d={d} G={G} lens={list(w.seq_lens)}")
+    for splits in (0, 3):
+        got = lr.dense_decode(dev["q"], dev["L_K"], dev["L_V"], dev["seq_lens"], dev["scales"],
+                              softmax_scale=w.softmax_scale, num_splits=splits)
+        import torch
+        torch.cuda.synchronize()
+        err = rel_rowmax(got.cpu().numpy(), _dense_oracle(w))
+        say(f"  splits={splits} err {err:.3e}")
+        assert err <= 2e-5, err
+
+
+@pytest.mark.parametrize("lt,G", [("bf16", 4), ("bf16", 1), ("i8", 2)])
+def test_dense_equals_factored_with_identity_factors(lt, G):
+    """With B_K = B_V = I the factored path computes the dense result in the
+    same order: absorbing q into I and projecting through I add only exact
+    zeros, so the two outputs are bitwise equal."""
+    import torch
+    import rank_kv_cache_head_amd as lr
+    w = _dense_case(lt, 128, G, seed=600 + G)
+    dev = to_device(w)
+    eye = torch.eye(128, dtype=dev["q"].dtype, device="cuda").expand(2, 128, 128).contiguous()
+    say(f"dense == factored(I) {lt} G={G}")
+    a = lr.dense_decode(dev["q"], dev["L_K"], dev["L_V"], dev["seq_lens"], dev["scales"],
+                        num_splits=3)
+    b = lr.decode(dev["q"], dev["L_K"], dev["L_V"], eye, eye, dev["seq_lens"], dev["scales"],
+                  num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 def test_guard_bands_untouched():
     import torch
     import rank_kv_cache_head_amd as lr
