@@ -7,7 +7,8 @@ fallback.
 
 Modules
   lowrank_decode  the plain definition: dequantize, rebuild K and V
-                  explicitly, dense softmax attention, in float64
+                  explicitly, dense softmax attention, in float64; and the
+                  same with keys and query rotated by position (decode_rotated)
   brute           the same definition in 40-digit decimal, nested loops,
                   for tiny inputs
 
@@ -15,4 +16,4 @@ Parity status: every function is pinned (see the CPU tests); none is
 "parity unpinned".
 """
 from .lowrank_decode import (as_float64, attend, decode, decode_absorbed,  # noqa: F401
-                             decode_rows, dequantize, rebuild)
+                             decode_rotated, decode_rows, dequantize, rebuild, rotate)

@@ -26,7 +26,8 @@ What is computed, and where the pages define it
 Readings where the pages are silent (each is listed in the design notes):
   - query head h uses kv-head g = h // (Hq / Hkv) (consecutive groups);
   - softmax scale defaults to 1 / sqrt(d);
-  - no positional rotation between rebuild and scoring;
+  - no positional rotation between rebuild and scoring in decode();
+    decode_rotated() below adds one (its reading is stated there);
   - the current token is already in the cache: attend to rows [0, seq_len);
   - seq_len <= 0 has no defined result: the oracle raises ValueError.
 
@@ -41,7 +42,7 @@ from typing import Iterable, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = ["as_float64", "dequantize", "rebuild", "attend", "decode",
-           "decode_rows", "decode_absorbed"]
+           "decode_rows", "decode_absorbed", "rotate", "decode_rotated"]
 
 
 def as_float64(a: np.ndarray, tag: str) -> np.ndarray:
@@ -173,4 +174,56 @@ def decode_absorbed(q, L_K, L_V, B_K, B_V, seq_lens, scales=None,
             p = e / e.sum()
             vt = p @ dequantize(L_V[b, g, :n], sV)      # [r]
             out[b, h] = vt @ B_V[g]
+    return out
+
+
+# ---------------------------------------------------------------- rotated keys
+#
+# A position-dependent rotation between the rebuild and the score.  The pages
+# do not name one; WSVD section 2.C rebuilds K on chip before scoring, which is
+# the form a rotation needs (q . B_K^T no longer absorbs it).  Reading taken
+# (listed in the design notes): the rotary embedding with rotate-half pairing,
+# i.e. coordinates j and j + d/2 form a pair, and the caller supplies the
+# per-position cosines and sines as a table; key row t is rotated with the
+# table row of position t, the query with the row of its own position
+# seq_len - 1 (it is the last token in the cache); values are not rotated.
+
+
+def rotate(x: np.ndarray, row: np.ndarray) -> np.ndarray:
+    """Rotate each pair (x[j], x[j + d/2]) by the angle whose cosine is
+    row[j] and sine is row[d/2 + j]:  (a, b) -> (a cos - b sin, a sin + b cos).
+
+    x [..., d] float64 (d even), row [..., d] float64 (cosines, then sines)."""
+    h = x.shape[-1] // 2
+    a, b = x[..., :h], x[..., h:]
+    c, s = row[..., :h], row[..., h:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def decode_rotated(q, L_K, L_V, B_K, B_V, seq_lens, rope, scales=None,
+                   softmax_scale: Optional[float] = None) -> np.ndarray:
+    """Decode with rotated keys, float64 [B, Hq, d].
+
+    rope [T, d] float64: row p = cosines of the d/2 angles at position p, then
+    their sines.  For sequence b with n = seq_len_b: K[t] = rotate(L_K[t] B_K,
+    rope[t]) for t < n, q' = rotate(q, rope[n - 1]), V[t] = L_V[t] B_V, and
+    out = softmax(alpha K q') V.
+    """
+    Bsz, Hq, Hkv, T, r, d = _check_shapes(q, L_K, L_V, B_K, B_V, seq_lens, scales)
+    if rope.shape != (T, d) or d % 2:
+        raise ValueError("rope must be [T, d] with d even")
+    group = Hq // Hkv
+    alpha = float(softmax_scale) if softmax_scale is not None else 1.0 / np.sqrt(d)
+    out = np.empty((Bsz, Hq, d), dtype=np.float64)
+    for b in range(Bsz):
+        n = int(seq_lens[b])
+        if n <= 0 or n > T:
+            raise ValueError(f"seq_len {n} out of range")
+        for g in range(Hkv):
+            sK = scales[0, b, g, :n] if scales is not None else None
+            sV = scales[1, b, g, :n] if scales is not None else None
+            K = rotate(rebuild(dequantize(L_K[b, g, :n], sK), B_K[g]), rope[:n])
+            V = rebuild(dequantize(L_V[b, g, :n], sV), B_V[g])
+            for h in range(g * group, (g + 1) * group):
+                out[b, h] = attend(rotate(q[b, h], rope[n - 1]), K, V, alpha)
     return out

@@ -44,7 +44,7 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = [
-    "Workload", "CONFIG_ORDER", "SPECS", "make", "bf16_bits_from_f32",
+    "Workload", "CONFIG_ORDER", "SPECS", "make", "bf16_bits_from_f32", "rope_table",
     "storage_dtype", "fingerprint",
 ]
 
@@ -286,3 +286,14 @@ def fingerprint(w: Workload) -> Dict[str, str]:
             continue
         out[k] = hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()[:16]
     return out
+
+
+def rope_table(T: int, d: int, base: float = 10000.0, offset: int = 0) -> np.ndarray:
+    """Rotary cosine/sine table, float32 [T, d]: row p holds cos((p + offset)
+    w_j) for j < d/2, then sin((p + offset) w_j), with w_j = base^(-2j/d).
+    Angles and trigonometry in float64, rounded once to float32.  (An input of
+    the rotated-key decode, supplied by the caller like any cache tensor.)"""
+    j = np.arange(d // 2, dtype=np.float64)
+    w = base ** (-2.0 * j / d)
+    ang = (np.arange(T, dtype=np.float64)[:, None] + offset) * w[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
