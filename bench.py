@@ -55,6 +55,8 @@ def parse():
                     help="also run the HBM read/copy probe kernels (calibration)")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-cache baseline (same workload, K and V of d columns)")
+    ap.add_argument("--no-rebuild", action="store_true",
+                    help="skip the rebuilt-key (and rotated-key) mode timing")
     return ap.parse_args()
 
 
@@ -270,6 +272,8 @@ def main():
     }
     if not args.no_dense:
         line["dense_baseline"] = dense_baseline(w, torch, lr, args, ms_per_step)
+    if not args.no_rebuild:
+        line["rebuilt_keys"] = rebuilt_keys(w, torch, lr, args, base, sets, ms_per_step)
     if args.probe:
         line["probe"] = run_probe(torch, lr)
     if not args.no_cpu_baseline:
@@ -329,6 +333,37 @@ def dense_baseline(w, torch, lr, args, compressed_ms):
                speedup_of_factored=ms / compressed_ms)
     del decs, keep
     torch.cuda.empty_cache()
+    return res
+
+
+def rebuilt_keys(w, torch, lr, args, base, sets, absorbed_ms):
+    """The same step with keys rebuilt on chip (lrattn_rebuild_decode), without
+    and with a rotary table, on the same inputs.  None where the mode does not
+    apply (it takes bf16 inputs, d in {64, 128}, r in {32, 64})."""
+    G = w.num_q_heads // w.num_kv_heads
+    if not (w.q_dtype == w.latent_dtype == w.factor_dtype == "bf16" and
+            w.head_dim in (64, 128) and w.rank in (32, 64) and G in (1, 2, 4, 8)):
+        return None
+    import workloads
+    rope = torch.from_numpy(workloads.rope_table(w.max_seq_len, w.head_dim)).cuda()
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    res = {}
+    for name, tab in (("unrotated", None), ("rotated", rope)):
+        decs = [lr.RebuildDecoder(base["q"], lk, lv, base["B_K"], base["B_V"], base["seq_lens"],
+                                  tab, out=out, num_splits=args.num_splits)
+                for lk, lv, _ in sets]
+        n = len(decs)
+        for i in range(args.warmup):
+            decs[i % n]()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            decs[i % n]()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / args.steps * 1e3
+        res[name] = dict(ms_per_step=ms, tokens_per_s=w.batch / (ms / 1e3),
+                         vs_absorbed=ms / absorbed_ms)
+    res["kernel"] = "partition_rebuild_kernel"
     return res
 
 

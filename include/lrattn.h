@@ -228,6 +228,41 @@ int lrattn_dense_decode(const lrattn_params* p,
                         size_t workspace_bytes,
                         lrattn_stream stream);
 
+/*
+ * Rebuilt (and optionally rotated) keys: the decode with K rebuilt on chip
+ * before scoring, as the fused kernel of the WSVD page (section 2.C) does,
+ * so that a position-dependent rotation can act between the rebuild and the
+ * score (the absorbed form q . B_K^T of lrattn_decode cannot carry one).
+ * For every b, h with g = h / (Hq / Hkv), n = seq_lens[b], t < n:
+ *   K[t] = rot(L_K[b,g,t,:] . B_K[g], t)      V[t] = L_V[b,g,t,:] . B_V[g]
+ *   q'   = rot(q[b,h,:], n - 1)               (the query is the last token)
+ *   out[b,h,:] = sum_t softmax_t(softmax_scale * <q', K[t]>) V[t]
+ * where rot(x, p) turns each pair (x[j], x[j + d/2]), j < d/2, by the angle
+ * whose cosine is rope[p, j] and sine rope[p, d/2 + j]:
+ *   (a, b) -> (a cos - b sin, a sin + b cos).
+ *   rope  [T, d] fp32, T = max_seq_len, 16-byte aligned; NULL: no rotation
+ *         (the result then equals lrattn_decode's up to rounding).
+ * Values are not rotated.  q, latents and factors must be bf16 (LRATTN_BF16),
+ * head_dim in {64, 128}, rank in {32, 64}, group in {1, 2, 4, 8}, and
+ * T * d * 4 < 2^31 when rope is given; anything else returns
+ * LRATTN_ERR_UNSUPPORTED.  The keys are rebuilt with exact bf16 products and
+ * fp32 sums; rotation, scores, softmax and accumulation run in fp32.
+ * Workspace, plan, ownership, seq_lens handling, errors and determinism are
+ * those of lrattn_decode.
+ */
+int lrattn_rebuild_decode(const lrattn_params* p,
+                          const void* q,
+                          const void* L_K,
+                          const void* L_V,
+                          const void* B_K,
+                          const void* B_V,
+                          const float* rope,
+                          const int32_t* seq_lens,
+                          void* out,
+                          void* workspace,
+                          size_t workspace_bytes,
+                          lrattn_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

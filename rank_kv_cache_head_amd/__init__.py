@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.lrattn_workspace_size.argtypes = [_PP, ctypes.POINTER(ctypes.c_size_t)]
         L.lrattn_dense_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                           ctypes.c_size_t, _VP]
+        L.lrattn_rebuild_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                            ctypes.c_size_t, _VP]
         L.lrattn_partition_kernel.argtypes = [_PP]
         L.lrattn_partition_kernel.restype = ctypes.c_char_p
         L.lrattn_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -89,7 +91,8 @@ def lib() -> ctypes.CDLL:
         L.lrattn_probe_read.argtypes = [_VP, ctypes.c_size_t, _VP, _VP]
         L.lrattn_probe_copy.argtypes = [_VP, _VP, ctypes.c_size_t, _VP]
         for fn in ("lrattn_plan", "lrattn_workspace_size", "lrattn_decode", "lrattn_partition",
-                   "lrattn_combine", "lrattn_dense_decode", "lrattn_probe_read",
+                   "lrattn_combine", "lrattn_dense_decode", "lrattn_rebuild_decode",
+                   "lrattn_probe_read",
                    "lrattn_probe_copy"):
             getattr(L, fn).restype = ctypes.c_int
         _LIB = L
@@ -257,6 +260,34 @@ def dense_decode(q, K, V, seq_lens, scales=None, *, out=None, workspace=None,
     return out
 
 
+def _check_rope(p: Params, rope):
+    import torch
+    if rope is not None and (tuple(rope.shape) != (p.max_seq_len, p.head_dim) or
+                             rope.dtype != torch.float32):
+        raise ValueError("rope must be float32 [T, d]")
+
+
+def rebuild_decode(q, L_K, L_V, B_K, B_V, seq_lens, rope=None, *, out=None, workspace=None,
+                   softmax_scale=None, num_splits: int = 0, out_dtype=None, stream=None):
+    """lrattn_rebuild_decode: keys rebuilt on chip, rotated by position when
+    `rope` ([T, d] float32: cosines then sines per position) is given."""
+    import torch
+    p = params_for(q, L_K, B_K, out_dtype=out_dtype, softmax_scale=softmax_scale,
+                   num_splits=num_splits)
+    _check_shapes(p, L_V, B_V, None, seq_lens)
+    _check_rope(p, rope)
+    if out is None:
+        out = torch.empty((p.batch, p.num_q_heads, p.head_dim),
+                          dtype=torch.float32 if p.out_dtype == F32 else torch.bfloat16,
+                          device=q.device)
+    ws, ws_bytes = _workspace(p, workspace, q.device)
+    st = lib().lrattn_rebuild_decode(ctypes.byref(p), _ptr(q), _ptr(L_K), _ptr(L_V), _ptr(B_K),
+                                     _ptr(B_V), _ptr(rope), _ptr(seq_lens), _ptr(out), _ptr(ws),
+                                     ws_bytes, _stream(stream))
+    _check(st, "lrattn_rebuild_decode")
+    return out
+
+
 def partition(q, L_K, L_V, B_K, seq_lens, scales=None, *, workspace=None, softmax_scale=None,
               num_splits: int = 0, stream=None):
     """lrattn_partition alone; returns the workspace tensor holding the partials."""
@@ -377,4 +408,31 @@ class DenseDecoder:
 
     def __call__(self):
         _check(self._fn(*self._args), "lrattn_dense_decode")
+        return self.out
+
+
+class RebuildDecoder:
+    """lrattn_rebuild_decode on fixed buffers, marshalled once (see Decoder)."""
+
+    def __init__(self, q, L_K, L_V, B_K, B_V, seq_lens, rope=None, *, out=None, workspace=None,
+                 softmax_scale=None, num_splits: int = 0, out_dtype=None, stream=None):
+        import torch
+        p = params_for(q, L_K, B_K, out_dtype=out_dtype, softmax_scale=softmax_scale,
+                       num_splits=num_splits)
+        _check_shapes(p, L_V, B_V, None, seq_lens)
+        _check_rope(p, rope)
+        if out is None:
+            out = torch.empty((p.batch, p.num_q_heads, p.head_dim),
+                              dtype=torch.float32 if p.out_dtype == F32 else torch.bfloat16,
+                              device=q.device)
+        ws, ws_bytes = _workspace(p, workspace, q.device)
+        self.params, self.out, self.workspace = p, out, ws
+        self.plan = plan(p)
+        self._keep = (q, L_K, L_V, B_K, B_V, seq_lens, rope)
+        self._fn = lib().lrattn_rebuild_decode
+        self._args = (ctypes.byref(p), _ptr(q), _ptr(L_K), _ptr(L_V), _ptr(B_K), _ptr(B_V),
+                      _ptr(rope), _ptr(seq_lens), _ptr(out), _ptr(ws), ws_bytes, _stream(stream))
+
+    def __call__(self):
+        _check(self._fn(*self._args), "lrattn_rebuild_decode")
         return self.out

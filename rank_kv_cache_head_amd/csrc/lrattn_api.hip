@@ -150,6 +150,7 @@ lrattn::PartitionArgs partition_args(const lrattn_params* p, const Plan& pl, con
                                      const float* scales, const int32_t* seq_lens, void* ws) {
   lrattn::PartitionArgs a;
   a.q = q; a.LK = LK; a.LV = LV; a.BK = BK; a.scales = scales; a.seq_lens = seq_lens;
+  a.rope = nullptr;
   a.ws = static_cast<float*>(ws);
   a.B = p->batch; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.d = p->head_dim;
   a.T = p->max_seq_len; a.P = pl.P; a.S = pl.S;
@@ -279,6 +280,33 @@ int lrattn_dense_decode(const lrattn_params* p, const void* q, const void* K, co
   if (lrattn::launch_partition(p->latent_dtype, p->rank, group_of(p), pa, s) != hipSuccess)
     return LRATTN_ERR_HIP;
   const auto ca = combine_args(p, pl, nullptr, seq_lens, out, workspace);
+  if (lrattn::launch_combine(group_of(p), ca, s) != hipSuccess) return LRATTN_ERR_HIP;
+  return LRATTN_OK;
+}
+
+int lrattn_rebuild_decode(const lrattn_params* p, const void* q, const void* L_K,
+                          const void* L_V, const void* B_K, const void* B_V, const float* rope,
+                          const int32_t* seq_lens, void* out, void* workspace,
+                          size_t workspace_bytes, lrattn_stream stream) {
+  Plan pl;
+  int st = check_params(p, &pl);
+  if (st == LRATTN_OK &&
+      (p->q_dtype != LRATTN_BF16 || p->latent_dtype != LRATTN_BF16 ||
+       p->factor_dtype != LRATTN_BF16 ||
+       !lrattn::rebuild_supported(p->head_dim, p->rank, group_of(p)) ||
+       (rope && (int64_t)p->max_seq_len * p->head_dim * 4 >= (int64_t(1) << 31))))
+    st = LRATTN_ERR_UNSUPPORTED;
+  if (st == LRATTN_OK) st = check_partition_ptrs(p, q, L_K, L_V, B_K, nullptr, seq_lens);
+  if (st == LRATTN_OK) st = check_combine_ptrs(B_V, seq_lens, out);
+  if (st == LRATTN_OK && rope && !aligned16(rope)) st = LRATTN_ERR_ALIGN;
+  if (st == LRATTN_OK) st = check_workspace(p, pl, workspace, workspace_bytes);
+  if (st != LRATTN_OK) return st;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto pa = partition_args(p, pl, q, L_K, L_V, B_K, nullptr, seq_lens, workspace);
+  pa.rope = rope;
+  if (lrattn::launch_rebuild(p->head_dim, p->rank, group_of(p), pa, s) != hipSuccess)
+    return LRATTN_ERR_HIP;
+  const auto ca = combine_args(p, pl, B_V, seq_lens, out, workspace);
   if (lrattn::launch_combine(group_of(p), ca, s) != hipSuccess) return LRATTN_ERR_HIP;
   return LRATTN_OK;
 }

@@ -44,6 +44,7 @@ struct PartitionArgs {
   const void* BK;          // [Hkv, r, d]
   const float* scales;     // [2, B, Hkv, T] or nullptr
   const int32_t* seq_lens; // [B]
+  const float* rope;       // [T, d] cos | sin per position (rebuilt-key kernel), or nullptr
   float* ws;               // [B, Hq, P, r + kRecPad]
   int32_t B, Hq, Hkv, d, T;
   int32_t P, S;            // partitions, tokens per partition
@@ -69,6 +70,12 @@ hipError_t launch_partition(int latent_dtype, int rank, int group,
                             const PartitionArgs& a, hipStream_t s);
 // Launch the combine grid (Hq, B) on `s`.
 hipError_t launch_combine(int group, const CombineArgs& a, hipStream_t s);
+// The rebuilt-key partition kernel (bf16 q, latents and factors; d in
+// {64, 128}, r in {32, 64}, group in {1, 2, 4, 8}); a.rope selects the
+// rotating instantiation.  Same grid and records as launch_partition.
+bool rebuild_supported(int head_dim, int rank, int group);
+hipError_t launch_rebuild(int head_dim, int rank, int group, const PartitionArgs& a,
+                          hipStream_t s);
 
 hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t s);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t s);

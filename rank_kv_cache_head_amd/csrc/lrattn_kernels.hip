@@ -885,7 +885,7 @@ void partition_kernel(PartitionArgs a) {
 // VALU path), so the exponentials computed in the score layout can be handed
 // to the value side through a per-wave LDS tile [token][head]; the value side
 // keeps the VALU path's slot layout: kLPR lanes per row, 8 columns per lane.
-template <int R, int G>
+template <int R, int G, int NT = LRATTN_MFMA_TILES>
 struct MGeo {
   static constexpr int kRowBytes = 2 * R;
   static constexpr int kKC = R / 32;           // 32-column MFMA steps per tile
@@ -893,25 +893,27 @@ struct MGeo {
   static constexpr int kLPR = kRowBytes / 16;  // value lanes per row: 4, 8, 16
   static constexpr int kRPW = 64 / kLPR;       // rows per value load
   static constexpr int kVU = 16 / kRPW;        // value loads per tile
-  static constexpr int kNT = LRATTN_MFMA_TILES;
+  static constexpr int kNT = NT;
   static constexpr int kChunk = 16 * kNT;      // tokens per wave per step
+  static constexpr int kHL = G < 4 ? G : 4;    // distinct heads in a lane's 4 results
   // registers: q~ terms 12 * kKC, accumulators 8 * G, latents 4 * (kKC + kVU)
   // per tile
   static constexpr int kRegs = 12 * kKC + 8 * G + 4 * kNT * (kKC + kVU);
   static constexpr int kWavesPerEU = kRegs <= 80 ? 4 : kRegs <= 120 ? 3 : 2;
-  static_assert(R % 32 == 0 && (G == 4 || G == 8), "matrix-core path shape");
+  static_assert(R % 32 == 0 && (G == 1 || G == 2 || G == 4 || G == 8), "matrix-core path shape");
 };
 
-template <int R, int G>
+template <int R, int G, int NT = LRATTN_MFMA_TILES>
 struct MStep {
-  uint32_t k[MGeo<R, G>::kNT][MGeo<R, G>::kKC][4];
-  uint32_t v[MGeo<R, G>::kNT][MGeo<R, G>::kVU][4];
+  uint32_t k[NT][MGeo<R, G, NT>::kKC][4];
+  uint32_t v[NT][MGeo<R, G, NT>::kVU][4];
 };
 
-template <int R, int G>
-__device__ __forceinline__ void load_mstep(MStep<R, G>& st, int cb, uint32_t koff, uint32_t voff,
-                                           __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv) {
-  using Mg = MGeo<R, G>;
+template <int R, int G, int NT>
+__device__ __forceinline__ void load_mstep(MStep<R, G, NT>& st, int cb, uint32_t koff,
+                                           uint32_t voff, __amdgpu_buffer_rsrc_t rk,
+                                           __amdgpu_buffer_rsrc_t rv) {
+  using Mg = MGeo<R, G, NT>;
 #pragma unroll
   for (int t = 0; t < Mg::kNT; ++t) {
     const uint32_t base = (uint32_t)(cb + 16 * t) * Mg::kRowBytes;
@@ -927,17 +929,14 @@ __device__ __forceinline__ void load_mstep(MStep<R, G>& st, int cb, uint32_t kof
   }
 }
 
-template <int R, int G, bool kMask>
-__device__ __forceinline__ void compute_mstep(
-    const MStep<R, G>& st, int cb, int ntok, int lane, const bf16x8 (&qa)[3][MGeo<R, G>::kKC],
-    float (&mm)[4], float (&ll)[4], float (&acc)[G][8], float* wl) {
-  using Mg = MGeo<R, G>;
-  constexpr int NT = Mg::kNT, KC = Mg::kKC, VU = Mg::kVU, RPW = Mg::kRPW;
+// Scores of the step's tiles: s[t][i] = base-2 logit of token 16 t + l % 16
+// for this lane's head i (rows 4 * (l / 16) + i of the product).
+template <int R, int G, int NT, bool kMask>
+__device__ __forceinline__ void mfma_scores(const MStep<R, G, NT>& st, int cb, int ntok, int lane,
+                                            const bf16x8 (&qa)[3][MGeo<R, G, NT>::kKC],
+                                            float (&s)[NT][4]) {
+  constexpr int KC = MGeo<R, G, NT>::kKC;
   const int tok = lane & 15;
-  const bool hi_half = G == 8 && ((lane >> 4) & 1);  // this lane's results are heads 4..7
-
-  // scores (base-2 logits): s[t][i] for token 16 t + tok, this lane's head i
-  float s[NT][4];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
@@ -958,6 +957,20 @@ __device__ __forceinline__ void compute_mstep(
       }
     }
   }
+}
+
+// Online softmax on scores in the matrix-core result layout, then the
+// latent-space value accumulation in the slot layout.  Lane l's result i is
+// head (4 * (l / 16) + i) % G: with G < 4 results i >= G repeat heads and are
+// not used.
+template <int R, int G, int NT>
+__device__ __forceinline__ void softmax_values(const float (&s)[NT][4], const MStep<R, G, NT>& st,
+                                               int lane, float (&mm)[4], float (&ll)[4],
+                                               float (&acc)[G][8], float* wl) {
+  using Mg = MGeo<R, G, NT>;
+  constexpr int VU = Mg::kVU, RPW = Mg::kRPW, HL = Mg::kHL;
+  const int tok = lane & 15;
+  const bool hi_half = G == 8 && ((lane >> 4) & 1);  // this lane's results are heads 4..7
 
   // Lazily moved reference max per head, the same in every lane holding the
   // head (lanes of the same row parity hold identical rows): mm[i] belongs to
@@ -966,11 +979,11 @@ __device__ __forceinline__ void compute_mstep(
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) need |= s[t][i] > mm[i] + kLazyLog2;
+    for (int i = 0; i < HL; ++i) need |= s[t][i] > mm[i] + kLazyLog2;
   }
   if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < HL; ++i) {
       float x = s[0][i];
 #pragma unroll
       for (int t = 1; t < NT; ++t) x = fmaxf(x, s[t][i]);
@@ -996,16 +1009,19 @@ __device__ __forceinline__ void compute_mstep(
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < HL; ++i) {
       e[t][i] = fast_exp2(s[t][i] - mm[i]);
       ll[i] += e[t][i];
     }
   }
-  if (lane < 4 * G) {  // the lanes holding distinct (token, head) results
+  if (lane < (G == 8 ? 32 : 16)) {  // the lanes holding distinct (token, head) results
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      *reinterpret_cast<float4*>(wl + (16 * t + tok) * G + (hi_half ? 4 : 0)) =
-          make_float4(e[t][0], e[t][1], e[t][2], e[t][3]);
+    for (int t = 0; t < NT; ++t) {
+      float* dst = wl + (16 * t + tok) * G + (hi_half ? 4 : 0);
+      if constexpr (HL == 4) *reinterpret_cast<float4*>(dst) = make_float4(e[t][0], e[t][1], e[t][2], e[t][3]);
+      else if constexpr (HL == 2) *reinterpret_cast<float2*>(dst) = make_float2(e[t][0], e[t][1]);
+      else dst[0] = e[t][0];
+    }
   }
   // LDS accesses of one wave complete in order; this keeps the compiler
   // from moving the reads below above the writes of other lanes
@@ -1019,10 +1035,17 @@ __device__ __forceinline__ void compute_mstep(
     for (int u = 0; u < VU; ++u) {
       const float* wr = wl + (16 * t + slot + RPW * u) * G;
       float w[G];
+      if constexpr (G >= 4) {
 #pragma unroll
-      for (int h4 = 0; h4 < G; h4 += 4) {
-        const float4 w4 = *reinterpret_cast<const float4*>(wr + h4);
-        w[h4] = w4.x; w[h4 + 1] = w4.y; w[h4 + 2] = w4.z; w[h4 + 3] = w4.w;
+        for (int h4 = 0; h4 < G; h4 += 4) {
+          const float4 w4 = *reinterpret_cast<const float4*>(wr + h4);
+          w[h4] = w4.x; w[h4 + 1] = w4.y; w[h4 + 2] = w4.z; w[h4 + 3] = w4.w;
+        }
+      } else if constexpr (G == 2) {
+        const float2 w2 = *reinterpret_cast<const float2*>(wr);
+        w[0] = w2.x; w[1] = w2.y;
+      } else {
+        w[0] = wr[0];
       }
       float x[8];
       Unpack<LatBF16>::run(st.v[t][u], x);
@@ -1034,6 +1057,87 @@ __device__ __forceinline__ void compute_mstep(
     }
   }
   __asm__ volatile("" ::: "memory");
+}
+
+template <int R, int G, bool kMask>
+__device__ __forceinline__ void compute_mstep(
+    const MStep<R, G>& st, int cb, int ntok, int lane, const bf16x8 (&qa)[3][MGeo<R, G>::kKC],
+    float (&mm)[4], float (&ll)[4], float (&acc)[G][8], float* wl) {
+  float s[MGeo<R, G>::kNT][4];
+  mfma_scores<R, G, MGeo<R, G>::kNT, kMask>(st, cb, ntok, lane, qa, s);
+  softmax_values<R, G, MGeo<R, G>::kNT>(s, st, lane, mm, ll, acc, wl);
+}
+
+// x == hi + mid + lo exactly (bf16 bit patterns): each remainder is exact in
+// fp32 and the last one has at most 8 significant bits.
+__device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = f32_to_bf16_rne(x);
+  const float r1 = x - __uint_as_float(hi << 16);
+  mid = f32_to_bf16_rne(r1);
+  lo = f32_to_bf16_rne(r1 - __uint_as_float(mid << 16));
+}
+
+// Three bf16x8 operands holding the exact split of 8 fp32 values.
+__device__ __forceinline__ void split3x8(const float (&x)[8], bf16x8 (&t)[3]) {
+  u32x4 w[3];
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    uint32_t a0, a1, a2, b0, b1, b2;
+    split3(x[j], a0, a1, a2);
+    split3(x[j + 1], b0, b1, b2);
+    w[0][j / 2] = a0 | (b0 << 16);
+    w[1][j / 2] = a1 | (b1 << 16);
+    w[2][j / 2] = a2 | (b2 << 16);
+  }
+#pragma unroll
+  for (int k = 0; k < 3; ++k) t[k] = __builtin_bit_cast(bf16x8, w[k]);
+}
+
+// End of a matrix-core partition: the wave's exp-sums over its 16 token
+// lanes, its accumulators over the slots (one reference per head for the
+// whole wave: plain sums), then the fixed-order merge of the waves.
+template <int R, int G, int NT>
+__device__ __forceinline__ void mfma_epilogue(const PartitionArgs& a, int b, int g, int p,
+                                              const float (&mm)[4], const float (&ll)[4],
+                                              float (&acc)[G][8], PartLds<R, G>& lds) {
+  using Mg = MGeo<R, G, NT>;
+  constexpr int LPR = Mg::kLPR, HL = Mg::kHL;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = lane / LPR, cc = lane % LPR;
+  float m[G], l[G];
+#pragma unroll
+  for (int i = 0; i < HL; ++i) {
+    const float x = group_sum<16>(ll[i]);
+    l[i] = readlane_f(x, 0);
+    m[i] = readlane_f(mm[i], 0);
+    if constexpr (G == 8) {
+      l[4 + i] = readlane_f(x, 16);
+      m[4 + i] = readlane_f(mm[i], 16);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
+    }
+  }
+  if (slot == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lds.acc[(wave * G + h) * R + cc * 8 + e] = acc[h][e];
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      lds.m[wave * G + h] = m[h];
+      lds.l[wave * G + h] = l[h];
+    }
+  }
+  __syncthreads();
+  write_records<R, G>(a, b, g, p, lds.acc, lds.m, lds.l);
 }
 
 template <int R, int G>
@@ -1080,28 +1184,13 @@ void partition_mfma_kernel(PartitionArgs a) {
     const float* qrow = lds.base.qt + ((lane & 15) % G) * R + 8 * (lane >> 4);
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      u32x4 w3[3];
+      float x[8];
 #pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        uint32_t t3[3][2];
+      for (int j = 0; j < 8; ++j) x[j] = qrow[32 * c + j];
+      bf16x8 t[3];
+      split3x8(x, t);
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          // x == hi + mid + lo exactly: each remainder is exact in fp32 and
-          // the last one has at most 8 significant bits
-          const float x = qrow[32 * c + j + jj];
-          const uint16_t hi = f32_to_bf16_rne(x);
-          const float r1 = x - __uint_as_float((uint32_t)hi << 16);
-          const uint16_t mid = f32_to_bf16_rne(r1);
-          const float r2 = r1 - __uint_as_float((uint32_t)mid << 16);
-          t3[0][jj] = hi;
-          t3[1][jj] = mid;
-          t3[2][jj] = f32_to_bf16_rne(r2);
-        }
-#pragma unroll
-        for (int term = 0; term < 3; ++term) w3[term][j / 2] = t3[term][0] | (t3[term][1] << 16);
-      }
-#pragma unroll
-      for (int term = 0; term < 3; ++term) qa[term][c] = __builtin_bit_cast(bf16x8, w3[term]);
+      for (int term = 0; term < 3; ++term) qa[term][c] = t[term];
     }
   }
 
@@ -1128,43 +1217,283 @@ void partition_mfma_kernel(PartitionArgs a) {
     else load_mstep(cur, cb + kWaves * CH, koff, voff, rk, rv);
   }
 
-  // ---- wave totals: exp-sums over the 16 token lanes, accumulators over
-  // the slots (one reference per head for the whole wave: plain sums)
-  float m[G], l[G];
+  mfma_epilogue<R, G, Mg::kNT>(a, b, g, p, mm, ll, acc, lds.base);
+}
+
+// --------------------------------------- partition, rebuilt (and rotated) keys
+// WSVD page, section 2.C: the decode kernel rebuilds the keys from the
+// latents on chip and scores the rebuilt keys.  This kernel does so for a
+// tile of 16 keys per wave on the matrix cores, can rotate the rebuilt keys
+// by position before scoring (a position-dependent rotation is what the
+// absorbed form q . B_K^T cannot carry), and scores them against the query
+// rotated by its own position.  Values are not rotated, so they stay in the
+// latent space: the value side, the records and the combine are those of the
+// absorbed path.  bf16 q, latents and factors; d in {64, 128}; r in {32, 64}.
+//
+//   rebuild  K^T (d x 16) = B_K^T (d x r) . L_K^T (r x 16): per 16-row block n
+//            of d and 32-row step c of r one v_mfma_f32_16x16x32_bf16.
+//            A = B_K^T fragments (arranged in LDS once per workgroup),
+//            B = the latent tile as loaded (lane l: token l % 16, latents
+//            32 c + 8 (l / 16) .. + 7).  Lane l's result register i of block
+//            n is d = 16 n + 4 (l / 16) + i of token l % 16: exact bf16
+//            products, fp32 sums.
+//   rotate   pairs (j, j + d/2) are blocks n and n + d/32 of one lane and
+//            register; the cosines and sines of the token's position come
+//            from the caller's table row (loaded with the tile's latents).
+//   score    S (16 x 16) = Q' . K'^T with K' (fp32) and q' = qscale *
+//            rotate(q, seq_len - 1) (fp32) each split exactly into three
+//            bf16 terms.  Per 32-wide step s of d, lane l supplies blocks 2s
+//            and 2s + 1, i.e. d = 32 s + 4 (l / 16) + i and 32 s + 16 +
+//            4 (l / 16) + i, and the query operand uses the same order.  The
+//            six products above 2^-24 of the score (hi.hi, hi.mid, mid.hi,
+//            hi.lo, lo.hi, mid.mid) are summed in fp32; the three left out are
+//            below fp32 rounding.  The result layout is that of
+//            partition_mfma_kernel, whose softmax and value code follow.
+
+template <int R, int D>
+struct RGeo {
+  static constexpr int kNB = D / 16;   // 16-row blocks of d
+  static constexpr int kKC = R / 32;   // 32-row steps of r
+  static constexpr int kKS = D / 32;   // 32-wide score steps of d
+  static constexpr int kHalf = D / 32; // blocks per half of d (rotation pairs)
+};
+
+// One tile of keys' table values: cosines and sines of d = 16 n + 4 (l / 16)
+// + i (i < 4) for the blocks n of the first half of d.
+template <int D, bool kRot>
+struct RopeTile {
+  u32x4 c[kRot ? D / 32 : 1];
+  u32x4 s[kRot ? D / 32 : 1];
+};
+
+template <int R, int G, int D, bool kRot>
+struct RStep {
+  MStep<R, G, 1> lat;
+  RopeTile<D, kRot> rope;
+};
+
+template <int R, int G, int D, bool kRot>
+__device__ __forceinline__ void load_rstep(RStep<R, G, D, kRot>& st, int cb, uint32_t koff,
+                                           uint32_t voff, __amdgpu_buffer_rsrc_t rk,
+                                           __amdgpu_buffer_rsrc_t rv, __amdgpu_buffer_rsrc_t rr,
+                                           uint32_t rope_off) {
+  load_mstep<R, G, 1>(st.lat, cb, koff, voff, rk, rv);
+  if constexpr (kRot) {
+    // table row of this lane's token (position t0 + cb + l % 16); rows past
+    // the table load zeros (masked tokens)
+    const uint32_t row = rope_off + (uint32_t)cb * D * 4u;
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) {
+      st.rope.c[n] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(row + 64u * n), 0, 0);
+      st.rope.s[n] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(row + 64u * n + 2u * D), 0, 0);
+    }
+  }
+}
+
+template <int R, int G, int D, bool kRot, bool kMask>
+__device__ __forceinline__ void rebuild_scores(const RStep<R, G, D, kRot>& st, int cb, int ntok,
+                                               int lane, const u32x4* frag,
+                                               const bf16x8 (&qa)[3][D / 32], float (&s)[1][4]) {
+  using Rg = RGeo<R, D>;
+  constexpr int NB = Rg::kNB, KC = Rg::kKC;
+  // rebuild the tile's keys, transposed
+  f32x4 kd[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    kd[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const u32x4 bk = frag[(n * KC + c) * 64 + lane];
+      const u32x4 lk = {st.lat.k[0][c][0], st.lat.k[0][c][1], st.lat.k[0][c][2], st.lat.k[0][c][3]};
+      kd[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bk),
+                                                      __builtin_bit_cast(bf16x8, lk), kd[n], 0, 0, 0);
+    }
+  }
+  if constexpr (kRot) {
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float c = __uint_as_float(st.rope.c[n][i]), sn = __uint_as_float(st.rope.s[n][i]);
+        const float x = kd[n][i], y = kd[n + D / 32][i];
+        kd[n][i] = x * c - y * sn;
+        kd[n + D / 32][i] = x * sn + y * c;
+      }
+    }
+  }
+  // scores: six products per 32-wide step of d, smallest first
+  f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = kd[2 * ks][i];
+      x[4 + i] = kd[2 * ks + 1][i];
+    }
+    bf16x8 kt[3];
+    split3x8(x, kt);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][ks], kt[1], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[2][ks], kt[0], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][ks], kt[2], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][ks], kt[0], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][ks], kt[1], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][ks], kt[0], d, 0, 0, 0);
+  }
+  const int tok = lane & 15;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float x = group_sum<16>(ll[i]);
-    l[i] = readlane_f(x, 0);
-    m[i] = readlane_f(mm[i], 0);
-    if constexpr (G == 8) {
-      l[4 + i] = readlane_f(x, 16);
-      m[4 + i] = readlane_f(mm[i], 16);
+    s[0][i] = d[i];
+    if constexpr (kMask) {
+      if (cb + tok >= ntok) s[0][i] = -INFINITY;
     }
   }
+}
+
+template <int R, int G, int D>
+struct RPartLds {
+  PartLds<R, G> base;          // q holds q' = qscale * rotate(q) [G][D]
+  u32x4 frag[D * R / 8];       // B_K^T fragments [n][c][lane]
+  uint16_t stage[R * D];       // B_K[g] as stored, for the fragment gather
+  float w[kWaves * 16 * G];
+};
+
+template <int R, int G, int D, bool kRot>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G == 8 ? 1 : 2)))
+void partition_rebuild_kernel(PartitionArgs a) {
+  using Mg = MGeo<R, G, 1>;
+  constexpr int LPR = Mg::kLPR, KC = R / 32, KS = D / 32;
+  constexpr int CH = 16;  // tokens per wave per step
+
+  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
+  const int t0 = p * a.S;
+  const int t1 = min(t0 + a.S, len);
+  if (t0 >= t1) return;  // partition past the sequence: nothing to write
+  const int ntok = t1 - t0;
+
+  __shared__ RPartLds<R, G, D> lds;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int slot = lane / LPR, cc = lane % LPR;
+
+  const size_t row0 = ((size_t)b * a.Hkv + g) * (size_t)a.T + (size_t)t0;
+  const uint32_t nbytes = (uint32_t)ntok * Mg::kRowBytes;
+  const auto rk = make_rsrc(static_cast<const char*>(a.LK) + row0 * Mg::kRowBytes, nbytes);
+  const auto rv = make_rsrc(static_cast<const char*>(a.LV) + row0 * Mg::kRowBytes, nbytes);
+  const uint32_t koff = (uint32_t)((lane & 15) * Mg::kRowBytes + (lane >> 4) * 16);
+  const uint32_t voff = (uint32_t)(slot * Mg::kRowBytes + cc * 16);
+  const auto rr = kRot ? make_rsrc(a.rope, (uint32_t)a.T * D * 4u) : make_rsrc(nullptr, 0u);
+  // this lane's table offset: row t0 + l % 16, columns 16 n + 4 (l / 16)
+  const uint32_t rope_off = (uint32_t)((t0 + (lane & 15)) * D + 4 * (lane >> 4)) * 4u;
+
+  // ---- prologue: B_K[g] and q, both bf16, with every load issued at once
+  {
+    const auto rf = make_rsrc(static_cast<const uint16_t*>(a.BK) + (size_t)g * R * D,
+                              (uint32_t)(R * D) * 2u);
+    constexpr int kF = R * D / 8 / kThreads;  // 16-byte pieces of B_K per thread
+    u32x4 fw[kF];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    for (int off = LPR; off < 64; off <<= 1) {
+    for (int k = 0; k < kF; ++k)
+      fw[k] = __builtin_amdgcn_raw_buffer_load_b128(rf, (int)((tid + k * kThreads) * 16u), 0, 0);
+    const size_t q0 = ((size_t)b * a.Hq + (size_t)g * G) * D;
+    const auto rq = make_rsrc(static_cast<const uint16_t*>(a.q) + q0, (uint32_t)(G * D) * 2u);
+    // q pairs (j, j + D/2) of head h: thread handles pair index tid (and + 256)
+    constexpr int kPairs = G * D / 2, kPP = (kPairs + kThreads - 1) / kThreads;
+    uint32_t qlo[kPP], qhi[kPP];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
+    for (int k = 0; k < kPP; ++k) {
+      const int pi = tid + k * kThreads;
+      const int h = pi / (D / 2), j = pi - h * (D / 2);
+      const bool ok = pi < kPairs;
+      qlo[k] = __builtin_amdgcn_raw_buffer_load_b32(rq, (int)(ok ? (h * D + j) * 2u & ~3u : kOffNone), 0, 0);
+      qhi[k] = __builtin_amdgcn_raw_buffer_load_b32(rq, (int)(ok ? (h * D + j + D / 2) * 2u & ~3u : kOffNone), 0, 0);
+    }
+    float rc[kPP], rs[kPP];
+#pragma unroll
+    for (int k = 0; k < kPP; ++k) {
+      rc[k] = 1.f;
+      rs[k] = 0.f;
+      if constexpr (kRot) {
+        const int pi = tid + k * kThreads;
+        const int j = pi % (D / 2);
+        const uint32_t row = (uint32_t)(len - 1) * D * 4u;
+        rc[k] = bload4f(rr, row + 4u * j);
+        rs[k] = bload4f(rr, row + 4u * (D / 2 + j));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kF; ++k)
+      *reinterpret_cast<u32x4*>(&lds.stage[(tid + k * kThreads) * 8]) = fw[k];
+#pragma unroll
+    for (int k = 0; k < kPP; ++k) {
+      const int pi = tid + k * kThreads;
+      const int h = pi / (D / 2), j = pi - h * (D / 2);
+      const float x = (j & 1) ? bf16_hi(qlo[k]) : bf16_lo(qlo[k]);
+      const float y = (j & 1) ? bf16_hi(qhi[k]) : bf16_lo(qhi[k]);
+      float* dst = pi < kPairs ? lds.base.q + h * D + j : lds.base.q + G * kMaxHeadDim;
+      dst[0] = (x * rc[k] - y * rs[k]) * a.qscale;
+      dst[pi < kPairs ? D / 2 : 4] = (x * rs[k] + y * rc[k]) * a.qscale;
     }
   }
-  if (slot == 0) {
+  __syncthreads();
+  // B_K^T fragments: fragment (n, c) of lane l = B_K[32 c + 8 (l / 16) + j][16 n + l % 16]
+  for (int f = tid; f < D * R / 8; f += kThreads) {
+    const int fl = f & 63, nc = f >> 6;
+    const int n = nc / KC, c = nc - n * KC;
+    const int col = 16 * n + (fl & 15), k0 = 32 * c + 8 * (fl >> 4);
+    u32x4 w;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) lds.base.acc[(wave * G + h) * R + cc * 8 + e] = acc[h][e];
-    }
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)lds.stage[(k0 + 2 * j) * D + col] |
+             ((uint32_t)lds.stage[(k0 + 2 * j + 1) * D + col] << 16);
+    lds.frag[f] = w;
   }
-  if (lane == 0) {
+  // query operand: row lane % 16 is head (lane % 16) % G; step s supplies
+  // d = 32 s + 4 (l / 16) + i and 32 s + 16 + 4 (l / 16) + i
+  bf16x8 qa[3][KS];
+  {
+    const float* qrow = lds.base.q + ((lane & 15) % G) * D + 4 * (lane >> 4);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      lds.base.m[wave * G + h] = m[h];
-      lds.base.l[wave * G + h] = l[h];
+    for (int ks = 0; ks < KS; ++ks) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = qrow[32 * ks + i];
+        x[4 + i] = qrow[32 * ks + 16 + i];
+      }
+      bf16x8 t[3];
+      split3x8(x, t);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) qa[k][ks] = t[k];
     }
   }
   __syncthreads();
 
-  write_records<R, G>(a, b, g, p, lds.base.acc, lds.base.m, lds.base.l);
+  RStep<R, G, D, kRot> cur;
+  load_rstep(cur, wave * CH, koff, voff, rk, rv, rr, rope_off);
+
+  float mm[4], ll[4], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mm[i] = -FLT_MAX;
+    ll[i] = 0.f;
+  }
+  float* wl = lds.w + wave * CH * G;
+  for (int cb = wave * CH; cb < ntok; cb += kWaves * CH) {
+    float s[1][4];
+    if (cb + CH <= ntok)
+      rebuild_scores<R, G, D, kRot, false>(cur, cb, ntok, lane, lds.frag, qa, s);
+    else
+      rebuild_scores<R, G, D, kRot, true>(cur, cb, ntok, lane, lds.frag, qa, s);
+    softmax_values<R, G, 1>(s, cur.lat, lane, mm, ll, acc, wl);
+    load_rstep(cur, cb + kWaves * CH, koff, voff, rk, rv, rr, rope_off);
+  }
+  mfma_epilogue<R, G, 1>(a, b, g, p, mm, ll, acc, lds.base);
 }
 
 // ------------------------------------------------------------------ combine
@@ -1429,6 +1758,31 @@ hipError_t launch_pr(int rank, int group, const PartitionArgs& a, hipStream_t s)
   }
 }
 
+template <int R, int D>
+hipError_t launch_rg(int group, bool rot, const PartitionArgs& a, hipStream_t s) {
+  const dim3 grid(a.P, a.Hkv, a.B), block(kThreads);
+  switch (group) {
+    case 1:
+      if (rot) hipLaunchKernelGGL((partition_rebuild_kernel<R, 1, D, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((partition_rebuild_kernel<R, 1, D, false>), grid, block, 0, s, a);
+      break;
+    case 2:
+      if (rot) hipLaunchKernelGGL((partition_rebuild_kernel<R, 2, D, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((partition_rebuild_kernel<R, 2, D, false>), grid, block, 0, s, a);
+      break;
+    case 4:
+      if (rot) hipLaunchKernelGGL((partition_rebuild_kernel<R, 4, D, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((partition_rebuild_kernel<R, 4, D, false>), grid, block, 0, s, a);
+      break;
+    case 8:
+      if (rot) hipLaunchKernelGGL((partition_rebuild_kernel<R, 8, D, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((partition_rebuild_kernel<R, 8, D, false>), grid, block, 0, s, a);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int R>
 hipError_t launch_cg(const CombineArgs& a, hipStream_t s) {
   const dim3 grid(a.Hq, a.B), block(kThreads);
@@ -1470,6 +1824,21 @@ hipError_t launch_partition(int latent_dtype, int rank, int group, const Partiti
     case LRATTN_I8: return launch_pr<LatI8>(rank, group, a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+bool rebuild_supported(int head_dim, int rank, int group) {
+  return (head_dim == 64 || head_dim == 128) && (rank == 32 || rank == 64) &&
+         (group == 1 || group == 2 || group == 4 || group == 8);
+}
+
+hipError_t launch_rebuild(int head_dim, int rank, int group, const PartitionArgs& a,
+                          hipStream_t s) {
+  const bool rot = a.rope != nullptr;
+  if (head_dim == 64 && rank == 32) return launch_rg<32, 64>(group, rot, a, s);
+  if (head_dim == 64 && rank == 64) return launch_rg<64, 64>(group, rot, a, s);
+  if (head_dim == 128 && rank == 32) return launch_rg<32, 128>(group, rot, a, s);
+  if (head_dim == 128 && rank == 64) return launch_rg<64, 128>(group, rot, a, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_combine(int group, const CombineArgs& a, hipStream_t s) {

@@ -187,3 +187,25 @@ def test_dense_decode_validates_on_host():
     assert call(params(rank=128, latent_dtype=lr.F32)) == -4   # 512-byte rows
     assert L.lrattn_dense_decode(None, ALIGNED, ALIGNED, ALIGNED, None, ALIGNED, ALIGNED, ALIGNED,
                                  1 << 30, None) == -1
+
+
+def test_rebuild_decode_validates_on_host():
+    L = lr.lib()
+    def call(p, q=ALIGNED, lk=ALIGNED, lv=ALIGNED, bk=ALIGNED, bv=ALIGNED, rope=None,
+             seq=ALIGNED, out=ALIGNED, ws=ALIGNED, ws_bytes=0):
+        return L.lrattn_rebuild_decode(ctypes.byref(p), q, lk, lv, bk, bv, rope, seq, out, ws,
+                                       ws_bytes, None)
+    p = params()                                       # bf16, d 128, r 64, G 4
+    assert call(params(rank=48)) == -4                 # r not in {32, 64}
+    assert call(params(head_dim=256)) == -4
+    assert call(params(latent_dtype=lr.F16)) == -4     # bf16 only
+    assert call(params(q_dtype=lr.F32)) == -4
+    assert call(params(factor_dtype=lr.F16)) == -4
+    assert call(params(latent_dtype=lr.I8, rank=32)) == -4
+    assert call(p, lk=None) == -1
+    assert call(p, bv=None) == -1
+    assert call(p, rope=MISALIGNED) == -5
+    assert call(p, q=MISALIGNED) == -5
+    assert call(p, ws=None) == -6
+    assert call(p, rope=ALIGNED, ws_bytes=lr.workspace_size(p) - 1) == -6
+    assert call(params(max_seq_len=1 << 22), rope=ALIGNED) == -4   # T * d * 4 >= 2^31

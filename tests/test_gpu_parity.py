@@ -288,6 +288,103 @@ def test_dense_equals_factored_with_identity_factors(lt, G):
     assert torch.equal(a, b)
 
 
+def _rebuild_case(r, G, d, seed, lens=(700, 333, 17, 16, 1), T=700, pad="zero"):
+    return workloads.make("gqa_vlm", seed=seed, pad=pad, B=len(lens), Hq=2 * G, Hkv=2, d=d, r=r,
+                          T=T, seq_lens=list(lens), q_std=2.0, factor_std=1.0 / np.sqrt(r))
+
+
+def _rope(w, base=500.0):
+    import torch
+    tab = workloads.rope_table(w.max_seq_len, w.head_dim, base=base)
+    return tab, torch.from_numpy(tab).cuda()
+
+
+@pytest.mark.parametrize("r,G,d", [(64, 4, 128), (32, 1, 128), (64, 8, 64), (32, 2, 64),
+                                   (64, 1, 128), (32, 8, 128)])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_rebuild_decode_matches_oracle(r, G, d, rotate):
+    """Keys rebuilt on the matrix cores (exact products, fp32 sums), rotated
+    in fp32, scored with both operands split exactly into bf16 terms: the
+    result must match the oracle to fp32 accuracy, with and without rotation,
+    at every split count, including one-token partitions."""
+    import torch
+    import rank_kv_cache_head_amd as lr
+    w = _rebuild_case(r, G, d, seed=700 + r + G + d + rotate)
+    dev = to_device(w)
+    args = f64_args(w)
+    if rotate:
+        tab, rope = _rope(w)
+        ref = oracle.decode_rotated(*args[:6], tab.astype(np.float64), softmax_scale=w.softmax_scale)
+    else:
+        rope = None
+        ref = _full_oracle(w)
+    for splits in (1, 3, 0, 700):
+        say(f"rebuild r={r} G={G} d={d} rotate={rotate} splits={splits}")
+        got = lr.rebuild_decode(dev["q"], dev["L_K"], dev["L_V"], dev["B_K"], dev["B_V"],
+                                dev["seq_lens"], rope, softmax_scale=w.softmax_scale,
+                                num_splits=splits)
+        torch.cuda.synchronize()
+        err = rel_rowmax(got.cpu().numpy(), ref)
+        say(f"  err {err:.3e}")
+        assert err <= 2e-5, err
+
+
+def test_rebuild_equals_absorbed_without_rotation():
+    """Absorbed and rebuilt keys are the same quantity (associativity): the
+    two kernels agree to fp32 accuracy on the GPU."""
+    import torch
+    import rank_kv_cache_head_amd as lr
+    w = _rebuild_case(64, 4, 128, seed=801)
+    dev = to_device(w)
+    say("rebuilt == absorbed")
+    a = lr.rebuild_decode(dev["q"], dev["L_K"], dev["L_V"], dev["B_K"], dev["B_V"],
+                          dev["seq_lens"])
+    b = run_decode(w, dev)
+    torch.cuda.synchronize()
+    assert rel_rowmax(a.cpu().numpy(), b.cpu().numpy().astype(np.float64)) <= 2e-5
+
+
+def test_rebuild_nan_padding_and_determinism():
+    import torch
+    import rank_kv_cache_head_amd as lr
+    wz = _rebuild_case(64, 4, 128, seed=802, lens=(500, 77, 3), T=512)
+    wn = _rebuild_case(64, 4, 128, seed=802, lens=(500, 77, 3), T=512, pad="nan")
+    _, rope = _rope(wz)
+    say("rebuild NaN padding")
+    outs = []
+    for w in (wz, wn, wz):
+        dev = to_device(w)
+        o = lr.rebuild_decode(dev["q"], dev["L_K"], dev["L_V"], dev["B_K"], dev["B_V"],
+                              dev["seq_lens"], rope)
+        torch.cuda.synchronize()
+        outs.append(o.cpu().numpy())
+    assert np.isfinite(outs[1]).all()
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_rebuild_full_size_rotated():
+    """gqa_vlm at full size with rotation, default plan; sequences 0 and 15
+    checked against the oracle."""
+    import torch
+    import rank_kv_cache_head_amd as lr
+    say("rebuild full gqa_vlm: drawing inputs")
+    w = workloads.make("gqa_vlm")
+    dev = to_device(w)
+    tab, rope = _rope(w, base=10000.0)
+    say("rebuild full gqa_vlm: decode")
+    got = lr.rebuild_decode(dev["q"], dev["L_K"], dev["L_V"], dev["B_K"], dev["B_V"],
+                            dev["seq_lens"], rope).cpu().numpy()
+    assert np.isfinite(got).all()
+    sel = [0, w.batch - 1]
+    f = oracle.as_float64
+    ref = oracle.decode_rotated(f(w.q[sel], w.q_dtype), f(w.L_K[sel], w.latent_dtype),
+                                f(w.L_V[sel], w.latent_dtype), f(w.B_K, w.factor_dtype),
+                                f(w.B_V, w.factor_dtype), w.seq_lens[sel], tab.astype(np.float64))
+    err = rel_rowmax(got[sel], ref)
+    say(f"  err {err:.3e}")
+    assert err <= 2e-5, err
+
+
 def test_guard_bands_untouched():
     import torch
     import rank_kv_cache_head_amd as lr
