@@ -1068,26 +1068,28 @@ __device__ __forceinline__ void compute_mstep(
   softmax_values<R, G, MGeo<R, G>::kNT>(s, st, lane, mm, ll, acc, wl);
 }
 
-// x == hi + mid + lo exactly (bf16 bit patterns): each remainder is exact in
-// fp32 and the last one has at most 8 significant bits.
-__device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  hi = f32_to_bf16_rne(x);
-  const float r1 = x - __uint_as_float(hi << 16);
-  mid = f32_to_bf16_rne(r1);
-  lo = f32_to_bf16_rne(r1 - __uint_as_float(mid << 16));
+// Three bf16x8 operands holding the exact split of 8 fp32 values:
+// x == hi + mid + lo, each term rounded to nearest even by the packed
+// hardware conversion (v_cvt_pk_bf16_f32); each remainder is exact in fp32 and
+// the last one has at most 8 significant bits, so lo takes it exactly.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x2 cvt2(float a, float b) {
+  bf16x2 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return r;
 }
-
-// Three bf16x8 operands holding the exact split of 8 fp32 values.
 __device__ __forceinline__ void split3x8(const float (&x)[8], bf16x8 (&t)[3]) {
   u32x4 w[3];
 #pragma unroll
   for (int j = 0; j < 8; j += 2) {
-    uint32_t a0, a1, a2, b0, b1, b2;
-    split3(x[j], a0, a1, a2);
-    split3(x[j + 1], b0, b1, b2);
-    w[0][j / 2] = a0 | (b0 << 16);
-    w[1][j / 2] = a1 | (b1 << 16);
-    w[2][j / 2] = a2 | (b2 << 16);
+    const bf16x2 h = cvt2(x[j], x[j + 1]);
+    const float r0 = x[j] - (float)h[0], r1 = x[j + 1] - (float)h[1];
+    const bf16x2 m = cvt2(r0, r1);
+    const bf16x2 l = cvt2(r0 - (float)m[0], r1 - (float)m[1]);
+    w[0][j / 2] = __builtin_bit_cast(uint32_t, h);
+    w[1][j / 2] = __builtin_bit_cast(uint32_t, m);
+    w[2][j / 2] = __builtin_bit_cast(uint32_t, l);
   }
 #pragma unroll
   for (int k = 0; k < 3; ++k) t[k] = __builtin_bit_cast(bf16x8, w[k]);
@@ -1240,14 +1242,13 @@ void partition_mfma_kernel(PartitionArgs a) {
 //   rotate   pairs (j, j + d/2) are blocks n and n + d/32 of one lane and
 //            register; the cosines and sines of the token's position come
 //            from the caller's table row (loaded with the tile's latents).
-//   score    S (16 x 16) = Q' . K'^T with K' (fp32) and q' = qscale *
-//            rotate(q, seq_len - 1) (fp32) each split exactly into three
-//            bf16 terms.  Per 32-wide step s of d, lane l supplies blocks 2s
-//            and 2s + 1, i.e. d = 32 s + 4 (l / 16) + i and 32 s + 16 +
-//            4 (l / 16) + i, and the query operand uses the same order.  The
-//            six products above 2^-24 of the score (hi.hi, hi.mid, mid.hi,
-//            hi.lo, lo.hi, mid.mid) are summed in fp32; the three left out are
-//            below fp32 rounding.  The result layout is that of
+//   score    S (16 x 16) = Q' . K'^T in fp32 on the matrix cores
+//            (v_mfma_f32_16x16x4_f32, K = 4 per instruction), q' = qscale *
+//            rotate(q, seq_len - 1): for block n and register i, lane l's
+//            rebuilt value (d = 16 n + 4 (l / 16) + i of token l % 16) is the
+//            B operand for k = l / 16 as it stands, and the query operand
+//            holds q'[head][16 n + 4 (l / 16) + i].  No conversion, fp32
+//            products and sums.  The result layout is that of
 //            partition_mfma_kernel, whose softmax and value code follow.
 
 template <int R, int D>
@@ -1293,7 +1294,7 @@ __device__ __forceinline__ void load_rstep(RStep<R, G, D, kRot>& st, int cb, uin
 template <int R, int G, int D, bool kRot, bool kMask>
 __device__ __forceinline__ void rebuild_scores(const RStep<R, G, D, kRot>& st, int cb, int ntok,
                                                int lane, const u32x4* frag,
-                                               const bf16x8 (&qa)[3][D / 32], float (&s)[1][4]) {
+                                               const float (&qf)[D / 16][4], float (&s)[1][4]) {
   using Rg = RGeo<R, D>;
   constexpr int NB = Rg::kNB, KC = Rg::kKC;
   // rebuild the tile's keys, transposed
@@ -1321,24 +1322,13 @@ __device__ __forceinline__ void rebuild_scores(const RStep<R, G, D, kRot>& st, i
       }
     }
   }
-  // scores: six products per 32-wide step of d, smallest first
+  // scores: fp32 products, 4 per instruction
   f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) {
-    float x[8];
+  for (int n = 0; n < NB; ++n) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = kd[2 * ks][i];
-      x[4 + i] = kd[2 * ks + 1][i];
-    }
-    bf16x8 kt[3];
-    split3x8(x, kt);
-    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][ks], kt[1], d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[2][ks], kt[0], d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][ks], kt[2], d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][ks], kt[0], d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][ks], kt[1], d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][ks], kt[0], d, 0, 0, 0);
+    for (int i = 0; i < 4; ++i)
+      d = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[n][i], kd[n][i], d, 0, 0, 0);
   }
   const int tok = lane & 15;
 #pragma unroll
@@ -1359,10 +1349,10 @@ struct RPartLds {
 };
 
 template <int R, int G, int D, bool kRot>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G == 8 ? 1 : 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G == 8 ? 2 : 3)))
 void partition_rebuild_kernel(PartitionArgs a) {
   using Mg = MGeo<R, G, 1>;
-  constexpr int LPR = Mg::kLPR, KC = R / 32, KS = D / 32;
+  constexpr int LPR = Mg::kLPR, KC = R / 32;
   constexpr int CH = 16;  // tokens per wave per step
 
   const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -1448,23 +1438,15 @@ void partition_rebuild_kernel(PartitionArgs a) {
              ((uint32_t)lds.stage[(k0 + 2 * j + 1) * D + col] << 16);
     lds.frag[f] = w;
   }
-  // query operand: row lane % 16 is head (lane % 16) % G; step s supplies
-  // d = 32 s + 4 (l / 16) + i and 32 s + 16 + 4 (l / 16) + i
-  bf16x8 qa[3][KS];
+  // query operand: row lane % 16 is head (lane % 16) % G; block n,
+  // register i supplies d = 16 n + 4 (l / 16) + i
+  float qf[D / 16][4];
   {
     const float* qrow = lds.base.q + ((lane & 15) % G) * D + 4 * (lane >> 4);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      float x[8];
+    for (int n = 0; n < D / 16; ++n) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = qrow[32 * ks + i];
-        x[4 + i] = qrow[32 * ks + 16 + i];
-      }
-      bf16x8 t[3];
-      split3x8(x, t);
-#pragma unroll
-      for (int k = 0; k < 3; ++k) qa[k][ks] = t[k];
+      for (int i = 0; i < 4; ++i) qf[n][i] = qrow[16 * n + i];
     }
   }
   __syncthreads();
@@ -1487,9 +1469,9 @@ void partition_rebuild_kernel(PartitionArgs a) {
   for (int cb = wave * CH; cb < ntok; cb += kWaves * CH) {
     float s[1][4];
     if (cb + CH <= ntok)
-      rebuild_scores<R, G, D, kRot, false>(cur, cb, ntok, lane, lds.frag, qa, s);
+      rebuild_scores<R, G, D, kRot, false>(cur, cb, ntok, lane, lds.frag, qf, s);
     else
-      rebuild_scores<R, G, D, kRot, true>(cur, cb, ntok, lane, lds.frag, qa, s);
+      rebuild_scores<R, G, D, kRot, true>(cur, cb, ntok, lane, lds.frag, qf, s);
     softmax_values<R, G, 1>(s, cur.lat, lane, mm, ll, acc, wl);
     load_rstep(cur, cb + kWaves * CH, koff, voff, rk, rv, rr, rope_off);
   }
