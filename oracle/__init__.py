@@ -11,9 +11,11 @@ Modules
                   same with keys and query rotated by position (decode_rotated)
   brute           the same definition in 40-digit decimal, nested loops,
                   for tiny inputs
+  append          a new token's latent rows (projection, int8 quantization)
 
 Parity status: every function is pinned (see the CPU tests); none is
 "parity unpinned".
 """
 from .lowrank_decode import (as_float64, attend, decode, decode_absorbed,  # noqa: F401
                              decode_rotated, decode_rows, dequantize, rebuild, rotate)
+from . import append as append_step  # noqa: F401,E402
