@@ -263,6 +263,50 @@ int lrattn_rebuild_decode(const lrattn_params* p,
                           size_t workspace_bytes,
                           lrattn_stream stream);
 
+/*
+ * The append step: the new token's latent rows, written into the cache.
+ * WSVD page, section 2.A: each head's key (value) projection is factored per
+ * head, W_Kh = A_Kh . B_Kh with rank r, so a token with hidden state x enters
+ * the cache as its latent x . A_Kh; section 2.C keeps such latents in low
+ * precision.  For every sequence b < B and kv-head g, with p = positions[b]:
+ *   L_K[b,g,p,j] = sum_i x[b,i] A_K[g,j,i]     (likewise L_V with A_V)
+ *   x        [B, D]          x_dtype (BF16 or F16)
+ *   A_K, A_V [Hkv, r, D]     factor_dtype == x_dtype; row j holds the D
+ *                            weights of latent coordinate j (A_Kh transposed)
+ *   positions [B] int32      device; rows with p outside [0, T) are not written
+ *   L_K, L_V [B, Hkv, T, r]  latent_dtype (F32, BF16, F16 or I8): rounded to
+ *                            nearest even; I8: symmetric, per (b, g, p) and
+ *                            K / V: s = max_j |l_j| / 127, code = rint(l_j / s)
+ *                            (ties to even; s = 0 gives codes 0), s stored in
+ *   scales   [2, B, Hkv, T]  fp32 (index 0: K, 1: V); required iff I8
+ * The products are exact and summed in fp32 in a fixed order (bitwise
+ * reproducible); the int8 decision is taken in fp32 on those sums.
+ * Supported: r in {16, 32, 48, 64, 128}, 1 <= B <= 64, D a multiple of 128;
+ * else LRATTN_ERR_UNSUPPORTED.  All pointers 16-byte aligned.  Only the
+ * addressed rows (and scales) are written.  Asynchronous on `stream`, no
+ * allocation, no host synchronization.
+ */
+typedef struct lrattn_append_params {
+  int32_t batch;        /* B: sequences, one new token each */
+  int32_t num_kv_heads; /* Hkv */
+  int32_t model_dim;    /* D: width of x */
+  int32_t rank;         /* r */
+  int32_t max_seq_len;  /* T: token capacity (stride) of the cache */
+  int32_t x_dtype;      /* lrattn_dtype of x (and of A_K, A_V) */
+  int32_t factor_dtype; /* lrattn_dtype of A_K, A_V: equal to x_dtype */
+  int32_t latent_dtype; /* lrattn_dtype of the cache */
+} lrattn_append_params;
+
+int lrattn_append(const lrattn_append_params* p,
+                  const void* x,
+                  const void* A_K,
+                  const void* A_V,
+                  const int32_t* positions,
+                  void* L_K,
+                  void* L_V,
+                  float* scales,
+                  lrattn_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

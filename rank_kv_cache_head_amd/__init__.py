@@ -52,6 +52,13 @@ class Params(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float), ("num_splits", ctypes.c_int32)]
 
 
+class AppendParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("model_dim", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
+                ("factor_dtype", ctypes.c_int32), ("latent_dtype", ctypes.c_int32)]
+
+
 def library_path() -> str:
     return os.environ.get("LRATTN_LIBRARY", os.path.join(_PKG, "liblrattn.so"))
 
@@ -80,6 +87,8 @@ def lib() -> ctypes.CDLL:
                                           ctypes.c_size_t, _VP]
         L.lrattn_rebuild_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                             ctypes.c_size_t, _VP]
+        L.lrattn_append.argtypes = [ctypes.POINTER(AppendParams), _VP, _VP, _VP, _VP, _VP, _VP,
+                                    _VP, _VP]
         L.lrattn_partition_kernel.argtypes = [_PP]
         L.lrattn_partition_kernel.restype = ctypes.c_char_p
         L.lrattn_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -92,6 +101,7 @@ def lib() -> ctypes.CDLL:
         L.lrattn_probe_copy.argtypes = [_VP, _VP, ctypes.c_size_t, _VP]
         for fn in ("lrattn_plan", "lrattn_workspace_size", "lrattn_decode", "lrattn_partition",
                    "lrattn_combine", "lrattn_dense_decode", "lrattn_rebuild_decode",
+                   "lrattn_append",
                    "lrattn_probe_read",
                    "lrattn_probe_copy"):
             getattr(L, fn).restype = ctypes.c_int
@@ -286,6 +296,30 @@ def rebuild_decode(q, L_K, L_V, B_K, B_V, seq_lens, rope=None, *, out=None, work
                                      ws_bytes, _stream(stream))
     _check(st, "lrattn_rebuild_decode")
     return out
+
+
+def append(x, A_K, A_V, positions, L_K, L_V, scales=None, *, stream=None):
+    """lrattn_append: write each sequence's new latent rows (x . A_h^T) into
+    L_K / L_V (and int8 scales) at positions[b]; returns (L_K, L_V)."""
+    import torch
+    if x.dim() != 2 or A_K.dim() != 3 or L_K.dim() != 4:
+        raise ValueError("x [B,D], A [Hkv,r,D], L [B,Hkv,T,r] expected")
+    B, D = x.shape
+    Hkv, r, D2 = A_K.shape
+    if (D2 != D or tuple(A_V.shape) != tuple(A_K.shape) or L_K.shape[0] != B or
+            L_K.shape[1] != Hkv or L_K.shape[3] != r or L_V.shape != L_K.shape):
+        raise ValueError("shape mismatch")
+    if tuple(positions.shape) != (B,) or positions.dtype != torch.int32:
+        raise ValueError("positions must be int32 [B]")
+    if scales is not None and (tuple(scales.shape) != (2, B, Hkv, L_K.shape[2]) or
+                               scales.dtype != torch.float32):
+        raise ValueError("scales must be float32 [2, B, Hkv, T]")
+    p = AppendParams(B, Hkv, D, r, L_K.shape[2], _dtype_code(x), _dtype_code(A_K),
+                     _dtype_code(L_K))
+    st = lib().lrattn_append(ctypes.byref(p), _ptr(x), _ptr(A_K), _ptr(A_V), _ptr(positions),
+                             _ptr(L_K), _ptr(L_V), _ptr(scales), _stream(stream))
+    _check(st, "lrattn_append")
+    return L_K, L_V
 
 
 def partition(q, L_K, L_V, B_K, seq_lens, scales=None, *, workspace=None, softmax_scale=None,

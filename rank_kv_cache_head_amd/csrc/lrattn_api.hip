@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include "lrattn.h"
+#include "lrattn_append.hpp"
 #include "lrattn_internal.hpp"
 #include "lrattn_probe.h"
 
@@ -308,6 +309,35 @@ int lrattn_rebuild_decode(const lrattn_params* p, const void* q, const void* L_K
     return LRATTN_ERR_HIP;
   const auto ca = combine_args(p, pl, B_V, seq_lens, out, workspace);
   if (lrattn::launch_combine(group_of(p), ca, s) != hipSuccess) return LRATTN_ERR_HIP;
+  return LRATTN_OK;
+}
+
+int lrattn_append(const lrattn_append_params* p, const void* x, const void* A_K,
+                  const void* A_V, const int32_t* positions, void* L_K, void* L_V,
+                  float* scales, lrattn_stream stream) {
+  if (!p) return LRATTN_ERR_NULL;
+  if (p->batch <= 0 || p->num_kv_heads <= 0 || p->model_dim <= 0 || p->rank <= 0 ||
+      p->max_seq_len <= 0)
+    return LRATTN_ERR_SHAPE;
+  if ((p->x_dtype != LRATTN_BF16 && p->x_dtype != LRATTN_F16) || p->factor_dtype != p->x_dtype ||
+      esize(p->latent_dtype) == 0)
+    return LRATTN_ERR_DTYPE;
+  if (checked_mul({p->batch, p->num_kv_heads, p->max_seq_len, p->rank, 4}) < 0)
+    return LRATTN_ERR_SHAPE;
+  if (!lrattn::append_supported(p->rank, p->batch, p->model_dim) || p->num_kv_heads > 65535)
+    return LRATTN_ERR_UNSUPPORTED;
+  if (!x || !A_K || !A_V || !positions || !L_K || !L_V) return LRATTN_ERR_NULL;
+  if ((p->latent_dtype == LRATTN_I8) != (scales != nullptr)) return LRATTN_ERR_NULL;
+  if (!aligned16(x) || !aligned16(A_K) || !aligned16(A_V) || !aligned16(positions) ||
+      !aligned16(L_K) || !aligned16(L_V) || (scales && !aligned16(scales)))
+    return LRATTN_ERR_ALIGN;
+  lrattn::AppendArgs a;
+  a.x = x; a.AK = A_K; a.AV = A_V; a.positions = positions; a.LK = L_K; a.LV = L_V;
+  a.scales = scales;
+  a.B = p->batch; a.Hkv = p->num_kv_heads; a.D = p->model_dim; a.r = p->rank;
+  a.T = p->max_seq_len; a.x_dtype = p->x_dtype; a.latent_dtype = p->latent_dtype;
+  if (lrattn::launch_append(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return LRATTN_ERR_HIP;
   return LRATTN_OK;
 }
 

@@ -1,0 +1,190 @@
+// gfx950 kernel of the append step: a new token's latent rows.
+//
+// WSVD page, section 2.A: each head's key (value) projection is factored per
+// head, W_Kh = A_Kh . B_Kh, so a new token with hidden state x enters the
+// cache as its latent x . A_Kh (r values); section 2.C stores such latents in
+// low precision (int8 here, with one scale per token, kv-head and K / V).
+//
+// One workgroup per (kv-head g, K or V) forms the rows of all B sequences:
+//   Lat (B x r) = X (B x D) . A_g^T, A_g stored [r, D] (row j = the weights of
+//   latent coordinate j), on the matrix cores (v_mfma_f32_16x16x32_{bf16,f16}:
+//   exact products, fp32 sums).  Both operands load as 16 contiguous bytes per
+//   lane: lane l takes row l % 16 (a sequence of X, a latent coordinate of A)
+//   and elements 8 (l / 16) .. + 7 of each 32-wide step of D.  The four waves
+//   take a quarter of D each; their partial tiles are added in LDS in wave
+//   order (fixed, so results are bitwise reproducible).  Then each row is
+//   converted to the latent type (round to nearest even), or quantized:
+//   s = max |row| / 127, code = rint(row / s) in fp32 (ties to even), and
+//   written at the sequence's position; positions outside [0, T) are skipped.
+#include <float.h>
+
+#include "lrattn.h"
+#include "lrattn_append.hpp"
+
+namespace lrattn {
+namespace {
+
+constexpr int kThreads = 256, kWaves = 4;
+constexpr uint32_t kOffNone = 0x80000000u;  // past any resource: loads zero
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+template <int R, int RB, bool kF16>
+__global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
+  constexpr int NT = R / 16;  // 16-column tiles of the latent row
+  constexpr int U = 4;        // 32-wide steps of D whose loads are in flight together
+  const int g = blockIdx.x, kv = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const int D = a.D, B = a.B;
+
+  __shared__ float red[RB * 16][R];
+  __shared__ float rscale[RB * 16];
+  __shared__ int pos[RB * 16];
+
+  const auto ra = make_rsrc(static_cast<const uint16_t*>(kv ? a.AV : a.AK) + (size_t)g * R * D,
+                            (uint32_t)(R * D) * 2u);
+  const auto rx = make_rsrc(a.x, (uint32_t)(B * D) * 2u);
+  const int steps = D / (32 * kWaves);  // per wave
+  const int kbeg = wave * steps * 32;
+
+  f32x4 acc[RB][NT];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[rb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int s0 = 0; s0 < steps; s0 += U) {
+    u32x4 xf[U][RB], af[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = s0 + u < steps;
+      const int k0 = kbeg + 32 * (s0 + u) + 8 * kg;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int b = 16 * rb + row;
+        const uint32_t off = ok && b < B ? (uint32_t)(b * D + k0) * 2u : kOffNone;
+        xf[u][rb] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint32_t off = ok ? (uint32_t)((16 * t + row) * D + k0) * 2u : kOffNone;
+        af[u][t] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if constexpr (kF16)
+            acc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(f16x8, xf[u][rb]), __builtin_bit_cast(f16x8, af[u][t]),
+                acc[rb][t], 0, 0, 0);
+          else
+            acc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, xf[u][rb]), __builtin_bit_cast(bf16x8, af[u][t]),
+                acc[rb][t], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // waves' partial tiles added in wave order: lane l, register i holds
+  // (sequence 16 rb + 4 (l / 16) + i, coordinate 16 t + l % 16)
+  if (tid < RB * 16) pos[tid] = tid < B ? a.positions[tid] : -1;
+  for (int w = 0; w < kWaves; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float& dst = red[16 * rb + 4 * kg + i][16 * t + row];
+            dst = w == 0 ? acc[rb][t][i] : dst + acc[rb][t][i];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  const bool int8 = a.latent_dtype == LRATTN_I8;
+  if (int8 && tid < B) {
+    float m = 0.f;
+    for (int j = 0; j < R; ++j) m = fmaxf(m, fabsf(red[tid][j]));
+    const float sc = m / 127.0f;
+    rscale[tid] = sc;
+    const int p = pos[tid];
+    if (p >= 0 && p < a.T) a.scales[(((size_t)kv * B + tid) * a.Hkv + g) * a.T + p] = sc;
+  }
+  __syncthreads();
+  for (int e = tid; e < B * R; e += kThreads) {
+    const int b = e / R, j = e - b * R;
+    const int p = pos[b];
+    if (p < 0 || p >= a.T) continue;
+    const float v = red[b][j];
+    const size_t off = (((size_t)b * a.Hkv + g) * a.T + p) * R + j;
+    void* L = kv ? a.LV : a.LK;
+    switch (a.latent_dtype) {
+      case LRATTN_F32: static_cast<float*>(L)[off] = v; break;
+      case LRATTN_BF16: static_cast<__bf16*>(L)[off] = (__bf16)v; break;
+      case LRATTN_F16: static_cast<_Float16*>(L)[off] = (_Float16)v; break;
+      default: {
+        const float sc = rscale[b];
+        const float c = sc > 0.f ? fminf(fmaxf(rintf(v / sc), -127.f), 127.f) : 0.f;
+        static_cast<int8_t*>(L)[off] = (int8_t)c;
+      }
+    }
+  }
+}
+
+template <int R, bool kF16>
+hipError_t launch_r(const AppendArgs& a, hipStream_t s) {
+  const dim3 grid(a.Hkv, 2), block(kThreads);
+  switch ((a.B + 15) / 16) {
+    case 1: hipLaunchKernelGGL((append_kernel<R, 1, kF16>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((append_kernel<R, 2, kF16>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((append_kernel<R, 3, kF16>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((append_kernel<R, 4, kF16>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <bool kF16>
+hipError_t launch_t(const AppendArgs& a, hipStream_t s) {
+  switch (a.r) {
+    case 16: return launch_r<16, kF16>(a, s);
+    case 32: return launch_r<32, kF16>(a, s);
+    case 48: return launch_r<48, kF16>(a, s);
+    case 64: return launch_r<64, kF16>(a, s);
+    case 128: return launch_r<128, kF16>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool append_supported(int rank, int batch, int model_dim) {
+  const bool r_ok = rank == 16 || rank == 32 || rank == 48 || rank == 64 || rank == 128;
+  return r_ok && batch >= 1 && batch <= kAppendMaxBatch && model_dim >= 128 &&
+         model_dim % 128 == 0 && (int64_t)rank * model_dim * 2 < (int64_t(1) << 31) &&
+         (int64_t)batch * model_dim * 2 < (int64_t(1) << 31);
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  return a.x_dtype == LRATTN_F16 ? launch_t<true>(a, s) : launch_t<false>(a, s);
+}
+
+}  // namespace lrattn

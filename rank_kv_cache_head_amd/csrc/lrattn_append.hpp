@@ -1,0 +1,27 @@
+// Internal interface of the append-step kernel (lrattn_append.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lrattn {
+
+struct AppendArgs {
+  const void* x;            // [B, D]            x_dtype
+  const void* AK;           // [Hkv, r, D]       x_dtype
+  const void* AV;           // [Hkv, r, D]       x_dtype
+  const int32_t* positions; // [B]
+  void* LK;                 // [B, Hkv, T, r]    latent_dtype
+  void* LV;                 // [B, Hkv, T, r]    latent_dtype
+  float* scales;            // [2, B, Hkv, T] (int8 latents) or nullptr
+  int32_t B, Hkv, D, r, T;
+  int32_t x_dtype, latent_dtype;
+};
+
+// Largest batch one launch takes (four 16-row blocks of the matrix cores).
+constexpr int kAppendMaxBatch = 64;
+
+bool append_supported(int rank, int batch, int model_dim);
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+
+}  // namespace lrattn

@@ -209,3 +209,28 @@ def test_rebuild_decode_validates_on_host():
     assert call(p, ws=None) == -6
     assert call(p, rope=ALIGNED, ws_bytes=lr.workspace_size(p) - 1) == -6
     assert call(params(max_seq_len=1 << 22), rope=ALIGNED) == -4   # T * d * 4 >= 2^31
+
+
+def test_append_validates_on_host():
+    L = lr.lib()
+    def ap(**kw):
+        base = dict(batch=8, num_kv_heads=32, model_dim=4096, rank=32, max_seq_len=4096,
+                    x_dtype=lr.BF16, factor_dtype=lr.BF16, latent_dtype=lr.BF16)
+        base.update(kw)
+        return lr.AppendParams(**base)
+    def call(p, x=ALIGNED, ak=ALIGNED, av=ALIGNED, pos=ALIGNED, lk=ALIGNED, lv=ALIGNED, sc=None):
+        return L.lrattn_append(ctypes.byref(p), x, ak, av, pos, lk, lv, sc, None)
+    assert L.lrattn_append(None, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None,
+                           None) == -1
+    assert call(ap(batch=0)) == -2
+    assert call(ap(x_dtype=lr.F32, factor_dtype=lr.F32)) == -3
+    assert call(ap(factor_dtype=lr.F16)) == -3
+    assert call(ap(latent_dtype=7)) == -3
+    assert call(ap(rank=24)) == -4
+    assert call(ap(batch=65)) == -4
+    assert call(ap(model_dim=4000)) == -4
+    assert call(ap(), x=None) == -1
+    assert call(ap(), sc=ALIGNED) == -1                    # scales with bf16 latents
+    assert call(ap(latent_dtype=lr.I8)) == -1              # int8 without scales
+    assert call(ap(), lv=MISALIGNED) == -5
+    assert call(ap(latent_dtype=lr.I8), sc=MISALIGNED) == -5

@@ -1,0 +1,174 @@
+"""GPU parity of the append step (lrattn_append) against the fp64 oracle.
+
+Float latents: the kernel sums exact products in fp32 and rounds once to the
+storage type, so every stored value must be a faithful rounding of the exact
+latent (within one storage step plus the fp32 summation bound), and nearly all
+must equal the oracle's nearest-even rounding.  int8 latents: the code is a
+floating-point decision taken in fp32 on the fp32 sums; codes must equal the
+oracle's except by one step where the exact value of row / scale lies within
+the fp32 error of a rounding tie, and scales must agree to fp32 accuracy.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_helpers import say, tensor
+from oracle import append_step as ap
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = {"f32": 12345.0, "bf16": 0x4640, "f16": 0x6607, "i8": 77}
+
+
+def _run(B, Hkv, D, r, T, xdt, ldt, positions, seed):
+    import torch
+    import rank_kv_cache_head_amd as lr
+    inp = workloads.make_append(seed, B, Hkv, D, r, xdt)
+    x = tensor(inp["x"], xdt)
+    AK, AV = tensor(inp["A_K"], xdt), tensor(inp["A_V"], xdt)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "i8": torch.int8}[ldt]
+    shape = (B, Hkv, T, r)
+    if ldt == "bf16":
+        LK = torch.full(shape, SENTINEL[ldt], dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    elif ldt == "f16":
+        LK = torch.full(shape, SENTINEL[ldt], dtype=torch.int16, device="cuda").view(torch.float16)
+    else:
+        LK = torch.full(shape, SENTINEL[ldt], dtype=tdt, device="cuda")
+    LV = LK.clone()
+    sc = torch.full((2, B, Hkv, T), -1.0, device="cuda") if ldt == "i8" else None
+    pos = torch.tensor(positions, dtype=torch.int32, device="cuda")
+    lr.append(x, AK, AV, pos, LK, LV, sc)
+    torch.cuda.synchronize()
+    return inp, LK, LV, sc
+
+
+def _as_f64(t, ldt):
+    import torch
+    if ldt == "bf16":
+        return oracle.as_float64(t.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+    return t.cpu().numpy().astype(np.float64)
+
+
+def _round_to(x, ldt):
+    if ldt == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if ldt == "f16":
+        return x.astype(np.float16).astype(np.float64)
+    return oracle.as_float64(workloads.bf16_bits_from_f32(x.astype(np.float32)), "bf16")
+
+
+MANT = {"bf16": (7, -126), "f16": (10, -14), "f32": (23, -126)}
+
+
+def _ulp(e, ldt):
+    """One storage step at |e| (the subnormal step below the normal range)."""
+    mant, emin = MANT[ldt]
+    ex = np.floor(np.log2(np.maximum(np.abs(e), 1e-300)))
+    return np.exp2(np.maximum(ex, emin) - mant)
+
+
+def _check(inp, LK, LV, sc, positions, T, ldt):
+    xdt = inp["dtype"]
+    x = oracle.as_float64(inp["x"], xdt)
+    AK = oracle.as_float64(inp["A_K"], xdt)
+    AV = oracle.as_float64(inp["A_V"], xdt)
+    rows, scales, written = ap.append(x, AK, AV, positions, T, quantized=(ldt == "i8"))
+    exact = np.stack([ap.project(x, AK), ap.project(x, AV)])
+    # bound of the fp32 summation error: 2^-16 of the sum of |products|
+    bound = np.stack([np.einsum("bd,grd->bgr", np.abs(x), np.abs(AK)),
+                      np.einsum("bd,grd->bgr", np.abs(x), np.abs(AV))]) * 2.0 ** -16
+    B = x.shape[0]
+    got_all = [_as_f64(LK, ldt), _as_f64(LV, ldt)]
+    for kv in range(2):
+        got = got_all[kv]
+        for b in range(B):
+            p = positions[b]
+            if not written[b]:
+                continue
+            g = got[b, :, p, :]
+            e, bd = exact[kv, b], bound[kv, b]
+            if ldt == "i8":
+                s_ex = scales[kv, b]
+                s_got = sc[kv, b, :, p].cpu().numpy().astype(np.float64)
+                # the scale is the largest |latent| / 127: within the bound too
+                assert (np.abs(s_got - s_ex) <= (bd.max(axis=1) + 1e-7 * s_ex) / 127.0 * 2).all()
+                safe = np.where(s_ex > 0, s_ex, 1.0)[:, None]
+                ratio = e / safe
+                err = bd / safe + np.abs(ratio) * 1e-5      # fp32 sums, scale and division
+                near_tie = np.abs(np.abs(ratio) % 1.0 - 0.5) <= err
+                diff = g - rows[kv, b]
+                assert (np.abs(diff) <= 1).all(), (kv, b)
+                assert (diff[~near_tie] == 0).all(), (kv, b)
+            else:
+                assert (np.abs(g - e) <= _ulp(e, ldt) + bd).all(), (kv, b)
+                if ldt != "f32":   # fp32 storage keeps the fp32 sum itself
+                    same = (g == _round_to(e, ldt)).mean()
+                    assert same >= 0.98, same
+    return got_all
+
+
+def _untouched(got, positions, T, ldt):
+    sent = SENTINEL[ldt]
+    if ldt in ("bf16", "f16"):
+        sent = oracle.as_float64(np.array([sent], dtype=np.uint16), "bf16")[0] if ldt == "bf16" \
+            else float(np.array([sent], dtype=np.uint16).view(np.float16)[0])
+    for t in (got[0], got[1]):
+        mask = np.ones(t.shape[:1] + t.shape[2:3], dtype=bool)   # [B, T]
+        for b, p in enumerate(positions):
+            if 0 <= p < T:
+                mask[b, p] = False
+        assert (t.transpose(0, 2, 1, 3)[mask] == sent).all()
+
+
+@pytest.mark.parametrize("xdt", ["bf16", "f16"])
+@pytest.mark.parametrize("ldt", ["bf16", "f32", "f16", "i8"])
+@pytest.mark.parametrize("B,Hkv,D,r", [(5, 3, 256, 32), (17, 2, 1024, 64), (1, 4, 128, 16),
+                                       (64, 1, 512, 128), (33, 2, 384, 48)])
+def test_append_matches_oracle(B, Hkv, D, r, ldt, xdt):
+    T = 40
+    rng = np.random.default_rng(B + D + r)
+    positions = [int(v) for v in rng.integers(0, T, B)]
+    if B > 2:
+        positions[1], positions[2] = -1, T        # outside the cache: not written
+    say(f"append B={B} Hkv={Hkv} D={D} r={r} latent={ldt} x={xdt}")
+    inp, LK, LV, sc = _run(B, Hkv, D, r, T, xdt, ldt, positions, seed=900 + B + r)
+    got = _check(inp, LK, LV, sc, positions, T, ldt)
+    _untouched(got, positions, T, ldt)
+
+
+def test_append_deterministic_and_llm_shape():
+    """The 7B-like shape (D = 4096, 32 kv-heads, r = 32, B = 8), twice: bitwise equal."""
+    import torch
+    positions = list(range(100, 108))
+    say("append llm7b shape")
+    a = _run(8, 32, 4096, 32, 128, "bf16", "bf16", positions, seed=990)
+    b = _run(8, 32, 4096, 32, 128, "bf16", "bf16", positions, seed=990)
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    _check(a[0], a[1], a[2], a[3], positions, 128, "bf16")
+
+
+def test_append_then_decode():
+    """Append T tokens one position at a time, then decode the cache: the
+    decode of the appended cache equals the oracle's decode of the same cache."""
+    import torch
+    import rank_kv_cache_head_amd as lr
+    from gpu_helpers import rel_rowmax
+    B, Hkv, G, D, r, T, d = 3, 2, 4, 256, 32, 24, 64
+    lens = [24, 9, 1]
+    inp = [workloads.make_append(1000 + t, B, Hkv, D, r, "bf16") for t in range(T)]
+    AK, AV = tensor(inp[0]["A_K"], "bf16"), tensor(inp[0]["A_V"], "bf16")
+    LK = torch.zeros((B, Hkv, T, r), dtype=torch.bfloat16, device="cuda")
+    LV = torch.zeros_like(LK)
+    say("append then decode")
+    for t in range(T):
+        pos = torch.tensor([t if t < n else -1 for n in lens], dtype=torch.int32, device="cuda")
+        lr.append(tensor(inp[t]["x"], "bf16"), AK, AV, pos, LK, LV)
+    w = workloads.make("gqa_vlm", seed=1001, B=B, Hq=Hkv * G, Hkv=Hkv, d=d, r=r, T=T,
+                       seq_lens=lens, factor_std=1.0 / np.sqrt(r))
+    q, BK, BV = tensor(w.q, "bf16"), tensor(w.B_K, "bf16"), tensor(w.B_V, "bf16")
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = lr.decode(q, LK, LV, BK, BV, sl).cpu().numpy()
+    f = lambda t: oracle.as_float64(t.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+    ref = oracle.decode(f(q), f(LK), f(LV), f(BK), f(BV), np.array(lens))
+    assert rel_rowmax(out, ref) <= 2e-5

@@ -45,6 +45,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "CONFIG_ORDER", "SPECS", "make", "bf16_bits_from_f32", "rope_table",
+    "make_append",
     "storage_dtype", "fingerprint",
 ]
 
@@ -297,3 +298,18 @@ def rope_table(T: int, d: int, base: float = 10000.0, offset: int = 0) -> np.nda
     w = base ** (-2.0 * j / d)
     ang = (np.arange(T, dtype=np.float64)[:, None] + offset) * w[None, :]
     return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def make_append(seed: int, B: int, Hkv: int, D: int, r: int, x_dtype: str = "bf16",
+                x_std: float = 1.0) -> Dict[str, np.ndarray]:
+    """Inputs of the append step: hidden states x [B, D] ~ N(0, x_std^2) and
+    per-head projections A_K, A_V [Hkv, r, D] ~ N(0, 1/D) (so latents are
+    about N(0, x_std^2)), drawn in float32 and rounded to x_dtype storage
+    (bf16 as raw uint16 bits).  Child streams of SeedSequence(seed) in the
+    order x, A_K, A_V."""
+    sx, sk, sv = np.random.SeedSequence(seed).spawn(3)
+    x = _normal_block(sx, (B, D), x_std)
+    AK = _normal_block(sk, (Hkv, r, D), 1.0 / np.sqrt(D))
+    AV = _normal_block(sv, (Hkv, r, D), 1.0 / np.sqrt(D))
+    return dict(x=_to_storage(x, x_dtype), A_K=_to_storage(AK, x_dtype),
+                A_V=_to_storage(AV, x_dtype), dtype=x_dtype)
