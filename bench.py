@@ -57,6 +57,8 @@ def parse():
                     help="skip the dense-cache baseline (same workload, K and V of d columns)")
     ap.add_argument("--no-rebuild", action="store_true",
                     help="skip the rebuilt-key (and rotated-key) mode timing")
+    ap.add_argument("--no-append", action="store_true",
+                    help="skip the append-step timing")
     return ap.parse_args()
 
 
@@ -274,6 +276,8 @@ def main():
         line["dense_baseline"] = dense_baseline(w, torch, lr, args, ms_per_step)
     if not args.no_rebuild:
         line["rebuilt_keys"] = rebuilt_keys(w, torch, lr, args, base, sets, ms_per_step)
+    if not args.no_append:
+        line["append_step"] = append_step(w, torch, lr, args)
     if args.probe:
         line["probe"] = run_probe(torch, lr)
     if not args.no_cpu_baseline:
@@ -365,6 +369,48 @@ def rebuilt_keys(w, torch, lr, args, base, sets, absorbed_ms):
                          vs_absorbed=ms / absorbed_ms)
     res["kernel"] = "partition_rebuild_kernel"
     return res
+
+
+def append_step(w, torch, lr, args):
+    """The append step of one decode token per sequence at the workload's
+    shape: hidden width D = Hq * d (bf16 x and projections A_K, A_V
+    [Hkv, r, D]) into the workload's latent type.  Timed over K calls."""
+    import workloads
+    D = w.num_q_heads * w.head_dim
+    if D % 128 or w.batch > 64:
+        return None
+    inp = workloads.make_append(77, w.batch, w.num_kv_heads, D, w.rank, "bf16")
+    import numpy as np
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    x, AK, AV = t(inp["x"]), t(inp["A_K"]), t(inp["A_V"])
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
+           "i8": torch.int8}[w.latent_dtype]
+    T = 64
+    LK = torch.zeros((w.batch, w.num_kv_heads, T, w.rank), dtype=tdt, device="cuda")
+    LV = torch.zeros_like(LK)
+    sc = (torch.zeros((2, w.batch, w.num_kv_heads, T), device="cuda")
+          if w.latent_dtype == "i8" else None)
+    pos = torch.arange(w.batch, dtype=torch.int32, device="cuda") % T
+    p = lr.AppendParams(w.batch, w.num_kv_heads, D, w.rank, T, lr.BF16, lr.BF16,
+                        {"f32": lr.F32, "bf16": lr.BF16, "f16": lr.F16, "i8": lr.I8}[w.latent_dtype])
+    ws = torch.empty(lr.append_workspace_size(p), dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        lr.append(x, AK, AV, pos, LK, LV, sc, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        lr.append(x, AK, AV, pos, LK, LV, sc, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    esz = LK.element_size()
+    alg = (AK.nbytes + AV.nbytes + x.nbytes +
+           2 * w.batch * w.num_kv_heads * w.rank * esz + (0 if sc is None else 2 * w.batch * w.num_kv_heads * 4))
+    return dict(us_per_call=us, model_dim=D, bytes_per_call=alg, GBps=alg / (us / 1e6) / 1e9,
+                kernels="append_partial_kernel + append_finish_kernel")
 
 
 def run_probe(torch, lr):

@@ -283,8 +283,10 @@ int lrattn_rebuild_decode(const lrattn_params* p,
  * reproducible); the int8 decision is taken in fp32 on those sums.
  * Supported: r in {16, 32, 48, 64, 128}, 1 <= B <= 64, D a multiple of 128;
  * else LRATTN_ERR_UNSUPPORTED.  All pointers 16-byte aligned.  Only the
- * addressed rows (and scales) are written.  Asynchronous on `stream`, no
- * allocation, no host synchronization.
+ * addressed rows (and scales) are written.  Two launches on `stream` (partial
+ * sums over chunks of D into the caller's workspace, then the rows): no
+ * allocation, no host synchronization; workspace contents on entry do not
+ * matter.
  */
 typedef struct lrattn_append_params {
   int32_t batch;        /* B: sequences, one new token each */
@@ -297,6 +299,10 @@ typedef struct lrattn_append_params {
   int32_t latent_dtype; /* lrattn_dtype of the cache */
 } lrattn_append_params;
 
+/* Host-only.  Bytes of workspace lrattn_append needs for `p` (partial rows,
+ * fp32, a few MB at most). */
+int lrattn_append_workspace_size(const lrattn_append_params* p, size_t* bytes);
+
 int lrattn_append(const lrattn_append_params* p,
                   const void* x,
                   const void* A_K,
@@ -305,6 +311,8 @@ int lrattn_append(const lrattn_append_params* p,
                   void* L_K,
                   void* L_V,
                   float* scales,
+                  void* workspace,
+                  size_t workspace_bytes,
                   lrattn_stream stream);
 
 #ifdef __cplusplus

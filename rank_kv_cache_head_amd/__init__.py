@@ -88,7 +88,9 @@ def lib() -> ctypes.CDLL:
         L.lrattn_rebuild_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                             ctypes.c_size_t, _VP]
         L.lrattn_append.argtypes = [ctypes.POINTER(AppendParams), _VP, _VP, _VP, _VP, _VP, _VP,
-                                    _VP, _VP]
+                                    _VP, _VP, ctypes.c_size_t, _VP]
+        L.lrattn_append_workspace_size.argtypes = [ctypes.POINTER(AppendParams),
+                                                   ctypes.POINTER(ctypes.c_size_t)]
         L.lrattn_partition_kernel.argtypes = [_PP]
         L.lrattn_partition_kernel.restype = ctypes.c_char_p
         L.lrattn_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -101,7 +103,7 @@ def lib() -> ctypes.CDLL:
         L.lrattn_probe_copy.argtypes = [_VP, _VP, ctypes.c_size_t, _VP]
         for fn in ("lrattn_plan", "lrattn_workspace_size", "lrattn_decode", "lrattn_partition",
                    "lrattn_combine", "lrattn_dense_decode", "lrattn_rebuild_decode",
-                   "lrattn_append",
+                   "lrattn_append", "lrattn_append_workspace_size",
                    "lrattn_probe_read",
                    "lrattn_probe_copy"):
             getattr(L, fn).restype = ctypes.c_int
@@ -298,7 +300,14 @@ def rebuild_decode(q, L_K, L_V, B_K, B_V, seq_lens, rope=None, *, out=None, work
     return out
 
 
-def append(x, A_K, A_V, positions, L_K, L_V, scales=None, *, stream=None):
+def append_workspace_size(p: "AppendParams") -> int:
+    b = ctypes.c_size_t()
+    _check(lib().lrattn_append_workspace_size(ctypes.byref(p), ctypes.byref(b)),
+           "lrattn_append_workspace_size")
+    return b.value
+
+
+def append(x, A_K, A_V, positions, L_K, L_V, scales=None, *, workspace=None, stream=None):
     """lrattn_append: write each sequence's new latent rows (x . A_h^T) into
     L_K / L_V (and int8 scales) at positions[b]; returns (L_K, L_V)."""
     import torch
@@ -316,8 +325,13 @@ def append(x, A_K, A_V, positions, L_K, L_V, scales=None, *, stream=None):
         raise ValueError("scales must be float32 [2, B, Hkv, T]")
     p = AppendParams(B, Hkv, D, r, L_K.shape[2], _dtype_code(x), _dtype_code(A_K),
                      _dtype_code(L_K))
+    need = append_workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
     st = lib().lrattn_append(ctypes.byref(p), _ptr(x), _ptr(A_K), _ptr(A_V), _ptr(positions),
-                             _ptr(L_K), _ptr(L_V), _ptr(scales), _stream(stream))
+                             _ptr(L_K), _ptr(L_V), _ptr(scales), _ptr(workspace), ws_bytes,
+                             _stream(stream))
     _check(st, "lrattn_append")
     return L_K, L_V
 

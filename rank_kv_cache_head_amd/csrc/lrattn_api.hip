@@ -312,9 +312,8 @@ int lrattn_rebuild_decode(const lrattn_params* p, const void* q, const void* L_K
   return LRATTN_OK;
 }
 
-int lrattn_append(const lrattn_append_params* p, const void* x, const void* A_K,
-                  const void* A_V, const int32_t* positions, void* L_K, void* L_V,
-                  float* scales, lrattn_stream stream) {
+namespace {
+int check_append_params(const lrattn_append_params* p) {
   if (!p) return LRATTN_ERR_NULL;
   if (p->batch <= 0 || p->num_kv_heads <= 0 || p->model_dim <= 0 || p->rank <= 0 ||
       p->max_seq_len <= 0)
@@ -326,16 +325,42 @@ int lrattn_append(const lrattn_append_params* p, const void* x, const void* A_K,
     return LRATTN_ERR_SHAPE;
   if (!lrattn::append_supported(p->rank, p->batch, p->model_dim) || p->num_kv_heads > 65535)
     return LRATTN_ERR_UNSUPPORTED;
+  return LRATTN_OK;
+}
+
+size_t append_ws_for(const lrattn_append_params* p) {
+  return lrattn::append_workspace_bytes(p->num_kv_heads, p->batch, p->rank,
+                                        lrattn::append_chunks(p->num_kv_heads, p->model_dim));
+}
+}  // namespace
+
+int lrattn_append_workspace_size(const lrattn_append_params* p, size_t* bytes) {
+  if (!bytes) return LRATTN_ERR_NULL;
+  const int st = check_append_params(p);
+  if (st != LRATTN_OK) return st;
+  *bytes = append_ws_for(p);
+  return LRATTN_OK;
+}
+
+int lrattn_append(const lrattn_append_params* p, const void* x, const void* A_K,
+                  const void* A_V, const int32_t* positions, void* L_K, void* L_V,
+                  float* scales, void* workspace, size_t workspace_bytes, lrattn_stream stream) {
+  int st = check_append_params(p);
+  if (st != LRATTN_OK) return st;
   if (!x || !A_K || !A_V || !positions || !L_K || !L_V) return LRATTN_ERR_NULL;
   if ((p->latent_dtype == LRATTN_I8) != (scales != nullptr)) return LRATTN_ERR_NULL;
   if (!aligned16(x) || !aligned16(A_K) || !aligned16(A_V) || !aligned16(positions) ||
       !aligned16(L_K) || !aligned16(L_V) || (scales && !aligned16(scales)))
     return LRATTN_ERR_ALIGN;
+  if (!workspace) return LRATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LRATTN_ERR_ALIGN;
+  if (workspace_bytes < append_ws_for(p)) return LRATTN_ERR_WORKSPACE;
   lrattn::AppendArgs a;
   a.x = x; a.AK = A_K; a.AV = A_V; a.positions = positions; a.LK = L_K; a.LV = L_V;
-  a.scales = scales;
+  a.scales = scales; a.ws = static_cast<float*>(workspace);
   a.B = p->batch; a.Hkv = p->num_kv_heads; a.D = p->model_dim; a.r = p->rank;
   a.T = p->max_seq_len; a.x_dtype = p->x_dtype; a.latent_dtype = p->latent_dtype;
+  a.KS = lrattn::append_chunks(p->num_kv_heads, p->model_dim);
   if (lrattn::launch_append(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return LRATTN_ERR_HIP;
   return LRATTN_OK;

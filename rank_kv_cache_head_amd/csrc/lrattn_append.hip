@@ -5,17 +5,22 @@
 // cache as its latent x . A_Kh (r values); section 2.C stores such latents in
 // low precision (int8 here, with one scale per token, kv-head and K / V).
 //
-// One workgroup per (kv-head g, K or V) forms the rows of all B sequences:
-//   Lat (B x r) = X (B x D) . A_g^T, A_g stored [r, D] (row j = the weights of
-//   latent coordinate j), on the matrix cores (v_mfma_f32_16x16x32_{bf16,f16}:
-//   exact products, fp32 sums).  Both operands load as 16 contiguous bytes per
-//   lane: lane l takes row l % 16 (a sequence of X, a latent coordinate of A)
-//   and elements 8 (l / 16) .. + 7 of each 32-wide step of D.  The four waves
-//   take a quarter of D each; their partial tiles are added in LDS in wave
-//   order (fixed, so results are bitwise reproducible).  Then each row is
-//   converted to the latent type (round to nearest even), or quantized:
-//   s = max |row| / 127, code = rint(row / s) in fp32 (ties to even), and
-//   written at the sequence's position; positions outside [0, T) are skipped.
+// Two launches.  The partial kernel, one workgroup per (kv-head g, K or V,
+// chunk z of D), forms the chunk's contribution to the rows of all B
+// sequences: Lat_z (B x r) = X[:, chunk] . A_g[:, chunk]^T, A_g stored [r, D]
+// (row j = the weights of latent coordinate j), on the matrix cores
+// (v_mfma_f32_16x16x32_{bf16,f16}: exact products, fp32 sums).  Both operands
+// load as 16 contiguous bytes per lane: lane l takes row l % 16 (a sequence
+// of X, a latent coordinate of A) and elements 8 (l / 16) .. + 7 of each
+// 32-wide step of D.  The four waves take a quarter of the chunk each; their
+// tiles are added in LDS in wave order, and the chunk's rows go to the
+// workspace.  The finish kernel, one workgroup per (g, K or V), adds the
+// chunks in order z = 0, 1, ... (every order is fixed: bitwise reproducible)
+// and converts each row to the latent type (round to nearest even), or
+// quantizes it: s = max |row| / 127, code = rint(row / s) in fp32 (ties to
+// even); rows are written at the sequence's position, and positions outside
+// [0, T) are skipped.  Chunks are sized so the partial launch covers the chip
+// (the step reads A once: a few MB that few workgroups cannot stream).
 #include <float.h>
 
 #include "lrattn.h"
@@ -38,23 +43,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 template <int R, int RB, bool kF16>
-__global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
+__global__ __launch_bounds__(kThreads) void append_partial_kernel(AppendArgs a) {
   constexpr int NT = R / 16;  // 16-column tiles of the latent row
   constexpr int U = 4;        // 32-wide steps of D whose loads are in flight together
-  const int g = blockIdx.x, kv = blockIdx.y;
+  const int g = blockIdx.x, kv = blockIdx.y, z = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int D = a.D, B = a.B;
 
   __shared__ float red[RB * 16][R];
-  __shared__ float rscale[RB * 16];
-  __shared__ int pos[RB * 16];
 
   const auto ra = make_rsrc(static_cast<const uint16_t*>(kv ? a.AV : a.AK) + (size_t)g * R * D,
                             (uint32_t)(R * D) * 2u);
   const auto rx = make_rsrc(a.x, (uint32_t)(B * D) * 2u);
-  const int steps = D / (32 * kWaves);  // per wave
-  const int kbeg = wave * steps * 32;
+  const int chunk = D / a.KS;           // a multiple of 128
+  const int steps = chunk / (32 * kWaves);  // per wave
+  const int kbeg = z * chunk + wave * steps * 32;
 
   f32x4 acc[RB][NT];
 #pragma unroll
@@ -99,9 +103,8 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     }
   }
 
-  // waves' partial tiles added in wave order: lane l, register i holds
+  // waves' tiles added in wave order: lane l, register i holds
   // (sequence 16 rb + 4 (l / 16) + i, coordinate 16 t + l % 16)
-  if (tid < RB * 16) pos[tid] = tid < B ? a.positions[tid] : -1;
   for (int w = 0; w < kWaves; ++w) {
     if (wave == w) {
 #pragma unroll
@@ -118,47 +121,81 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     }
     __syncthreads();
   }
+  float* part = a.ws + (((size_t)g * 2 + kv) * a.KS + z) * B * R;
+  for (int e = tid; e < B * R; e += kThreads) part[e] = red[e / R][e % R];
+}
 
+// Rows [z RPB, (z + 1) RPB) of one (g, K or V): thread (row lb, coordinate j)
+// adds its KS chunk partials in order z = 0, 1, ..., 16 loads in flight at a
+// time (chunks past KS load zeros: adding +0 leaves every sum unchanged).
+template <int R>
+__global__ __launch_bounds__(kThreads) void append_finish_kernel(AppendArgs a) {
+  constexpr int RPB = kThreads / R;  // rows per workgroup
+  constexpr int Z = 16;
+  const int g = blockIdx.x, kv = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lb = tid / R, j = tid - lb * R;
+  const int b = blockIdx.z * RPB + lb;
+  const int B = a.B, KS = a.KS;
+  const bool active = lb < RPB && b < B;
+  __shared__ float rows[RPB * R];
+  __shared__ float rscale[RPB];
+
+  const auto rp = make_rsrc(a.ws + ((size_t)g * 2 + kv) * KS * B * R, (uint32_t)(KS * B * R) * 4u);
+  const uint32_t e = (uint32_t)(b * R + j);
+  float v = 0.f;
+  for (int z0 = 0; z0 < KS; z0 += Z) {
+    float t[Z];
+#pragma unroll
+    for (int u = 0; u < Z; ++u) {
+      const uint32_t off = active && z0 + u < KS ? ((uint32_t)(z0 + u) * B * R + e) * 4u : kOffNone;
+      t[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, (int)off, 0, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < Z; ++u) v = z0 + u == 0 ? t[u] : v + t[u];
+  }
+  if (lb < RPB) rows[tid] = v;
+  __syncthreads();
   const bool int8 = a.latent_dtype == LRATTN_I8;
-  if (int8 && tid < B) {
+  const int p = active ? a.positions[b] : -1;
+  if (int8 && active && j == 0) {
     float m = 0.f;
-    for (int j = 0; j < R; ++j) m = fmaxf(m, fabsf(red[tid][j]));
+    for (int k = 0; k < R; ++k) m = fmaxf(m, fabsf(rows[lb * R + k]));
     const float sc = m / 127.0f;
-    rscale[tid] = sc;
-    const int p = pos[tid];
-    if (p >= 0 && p < a.T) a.scales[(((size_t)kv * B + tid) * a.Hkv + g) * a.T + p] = sc;
+    rscale[lb] = sc;
+    if (p >= 0 && p < a.T) a.scales[(((size_t)kv * B + b) * a.Hkv + g) * a.T + p] = sc;
   }
   __syncthreads();
-  for (int e = tid; e < B * R; e += kThreads) {
-    const int b = e / R, j = e - b * R;
-    const int p = pos[b];
-    if (p < 0 || p >= a.T) continue;
-    const float v = red[b][j];
-    const size_t off = (((size_t)b * a.Hkv + g) * a.T + p) * R + j;
-    void* L = kv ? a.LV : a.LK;
-    switch (a.latent_dtype) {
-      case LRATTN_F32: static_cast<float*>(L)[off] = v; break;
-      case LRATTN_BF16: static_cast<__bf16*>(L)[off] = (__bf16)v; break;
-      case LRATTN_F16: static_cast<_Float16*>(L)[off] = (_Float16)v; break;
-      default: {
-        const float sc = rscale[b];
-        const float c = sc > 0.f ? fminf(fmaxf(rintf(v / sc), -127.f), 127.f) : 0.f;
-        static_cast<int8_t*>(L)[off] = (int8_t)c;
-      }
+  if (!active || p < 0 || p >= a.T) return;
+  void* L = kv ? a.LV : a.LK;
+  const size_t off = (((size_t)b * a.Hkv + g) * a.T + p) * R + j;
+  switch (a.latent_dtype) {
+    case LRATTN_F32: static_cast<float*>(L)[off] = v; break;
+    case LRATTN_BF16: static_cast<__bf16*>(L)[off] = (__bf16)v; break;
+    case LRATTN_F16: static_cast<_Float16*>(L)[off] = (_Float16)v; break;
+    default: {
+      const float sc = rscale[lb];
+      const float c = sc > 0.f ? fminf(fmaxf(rintf(v / sc), -127.f), 127.f) : 0.f;
+      static_cast<int8_t*>(L)[off] = (int8_t)c;
     }
   }
 }
 
 template <int R, bool kF16>
 hipError_t launch_r(const AppendArgs& a, hipStream_t s) {
-  const dim3 grid(a.Hkv, 2), block(kThreads);
+  const dim3 grid(a.Hkv, 2, a.KS), block(kThreads);
   switch ((a.B + 15) / 16) {
-    case 1: hipLaunchKernelGGL((append_kernel<R, 1, kF16>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((append_kernel<R, 2, kF16>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((append_kernel<R, 3, kF16>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((append_kernel<R, 4, kF16>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((append_partial_kernel<R, 1, kF16>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((append_partial_kernel<R, 2, kF16>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((append_partial_kernel<R, 3, kF16>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((append_partial_kernel<R, 4, kF16>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int RPB = kThreads / R;
+  hipLaunchKernelGGL((append_finish_kernel<R>), dim3(a.Hkv, 2, (a.B + RPB - 1) / RPB), block, 0,
+                     s, a);
   return hipGetLastError();
 }
 
@@ -181,6 +218,20 @@ bool append_supported(int rank, int batch, int model_dim) {
   return r_ok && batch >= 1 && batch <= kAppendMaxBatch && model_dim >= 128 &&
          model_dim % 128 == 0 && (int64_t)rank * model_dim * 2 < (int64_t(1) << 31) &&
          (int64_t)batch * model_dim * 2 < (int64_t(1) << 31);
+}
+
+int append_chunks(int num_kv_heads, int model_dim) {
+  const int pieces = model_dim / 128;  // the finest chunking
+  int ks = (512 + 2 * num_kv_heads - 1) / (2 * num_kv_heads);
+  if (ks > pieces) ks = pieces;
+  if (ks < 1) ks = 1;
+  while (pieces % ks) --ks;  // chunks divide D into multiples of 128
+  return ks;
+}
+
+size_t append_workspace_bytes(int num_kv_heads, int batch, int rank, int chunks) {
+  const size_t b = (size_t)num_kv_heads * 2 * chunks * batch * rank * 4;
+  return (b + 255) / 256 * 256;
 }
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {

@@ -14,7 +14,9 @@ struct AppendArgs {
   void* LK;                 // [B, Hkv, T, r]    latent_dtype
   void* LV;                 // [B, Hkv, T, r]    latent_dtype
   float* scales;            // [2, B, Hkv, T] (int8 latents) or nullptr
+  float* ws;                // partial rows [Hkv, 2, KS, B, r] fp32
   int32_t B, Hkv, D, r, T;
+  int32_t KS;               // chunks of D (one workgroup each)
   int32_t x_dtype, latent_dtype;
 };
 
@@ -22,6 +24,10 @@ struct AppendArgs {
 constexpr int kAppendMaxBatch = 64;
 
 bool append_supported(int rank, int batch, int model_dim);
+// Chunks of D for (Hkv, D): enough workgroups to cover the chip, chunks of at
+// least 128 elements that divide D.
+int append_chunks(int num_kv_heads, int model_dim);
+size_t append_workspace_bytes(int num_kv_heads, int batch, int rank, int chunks);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 
 }  // namespace lrattn

@@ -218,10 +218,16 @@ def test_append_validates_on_host():
                     x_dtype=lr.BF16, factor_dtype=lr.BF16, latent_dtype=lr.BF16)
         base.update(kw)
         return lr.AppendParams(**base)
-    def call(p, x=ALIGNED, ak=ALIGNED, av=ALIGNED, pos=ALIGNED, lk=ALIGNED, lv=ALIGNED, sc=None):
-        return L.lrattn_append(ctypes.byref(p), x, ak, av, pos, lk, lv, sc, None)
+    def call(p, x=ALIGNED, ak=ALIGNED, av=ALIGNED, pos=ALIGNED, lk=ALIGNED, lv=ALIGNED, sc=None,
+             ws=ALIGNED, ws_bytes=0):
+        return L.lrattn_append(ctypes.byref(p), x, ak, av, pos, lk, lv, sc, ws, ws_bytes, None)
     assert L.lrattn_append(None, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, None,
-                           None) == -1
+                           ALIGNED, 1 << 30, None) == -1
+    need = lr.append_workspace_size(ap())
+    assert 0 < need <= 4 << 20
+    assert call(ap(), ws=None, ws_bytes=need) == -6
+    assert call(ap(), ws=MISALIGNED, ws_bytes=need) == -5
+    assert call(ap(), ws_bytes=need - 1) == -6
     assert call(ap(batch=0)) == -2
     assert call(ap(x_dtype=lr.F32, factor_dtype=lr.F32)) == -3
     assert call(ap(factor_dtype=lr.F16)) == -3
