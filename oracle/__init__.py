@@ -17,5 +17,6 @@ Parity status: every function is pinned (see the CPU tests); none is
 "parity unpinned".
 """
 from .lowrank_decode import (as_float64, attend, decode, decode_absorbed,  # noqa: F401
-                             decode_rotated, decode_rows, dequantize, rebuild, rotate)
+                             decode_rotated, decode_rows, decode_shared, dequantize, rebuild,
+                             rotate)
 from . import append as append_step  # noqa: F401,E402

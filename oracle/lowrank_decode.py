@@ -42,7 +42,7 @@ from typing import Iterable, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = ["as_float64", "dequantize", "rebuild", "attend", "decode",
-           "decode_rows", "decode_absorbed", "rotate", "decode_rotated"]
+           "decode_rows", "decode_absorbed", "rotate", "decode_rotated", "decode_shared"]
 
 
 def as_float64(a: np.ndarray, tag: str) -> np.ndarray:
@@ -226,4 +226,42 @@ def decode_rotated(q, L_K, L_V, B_K, B_V, seq_lens, rope, scales=None,
             V = rebuild(dequantize(L_V[b, g, :n], sV), B_V[g])
             for h in range(g * group, (g + 1) * group):
                 out[b, h] = attend(rotate(q[b, h], rope[n - 1]), K, V, alpha)
+    return out
+
+
+# ------------------------------------------------------------ shared latent
+#
+# AttentionPack page, section 2.A (multi-head compression): the keys (values)
+# of all heads are joined along the head axis and factored once, so the cache
+# keeps one compressed row of R values per token, shared by the heads, and a
+# decompression matrix of R x (H d) whose column block h rebuilds head h.
+# Read here per latent stream: query head h attends to stream
+# s = h // (Hq / S) and rebuilds its keys (values) with its own block
+# B_K[h] (B_V[h]), R x d.  (S = 1 is the page's single shared cache.)
+
+
+def decode_shared(q, L_K, L_V, B_K, B_V, seq_lens, scales=None,
+                  softmax_scale: Optional[float] = None) -> np.ndarray:
+    """Decode over shared latent streams with per-query-head factors,
+    float64 [B, Hq, d].  L_K, L_V [B, S, T, R]; B_K, B_V [Hq, R, d]."""
+    Bsz, Hq, d = q.shape
+    _, S, T, R = L_K.shape
+    if L_V.shape != L_K.shape or B_K.shape != (Hq, R, d) or B_V.shape != B_K.shape:
+        raise ValueError("inconsistent shapes")
+    if Hq % S:
+        raise ValueError("Hq must be a multiple of the number of latent streams")
+    group = Hq // S
+    alpha = float(softmax_scale) if softmax_scale is not None else 1.0 / np.sqrt(d)
+    out = np.empty((Bsz, Hq, d), dtype=np.float64)
+    for b in range(Bsz):
+        n = int(seq_lens[b])
+        if n <= 0 or n > T:
+            raise ValueError(f"seq_len {n} out of range")
+        for h in range(Hq):
+            s_ = h // group
+            sK = scales[0, b, s_, :n] if scales is not None else None
+            sV = scales[1, b, s_, :n] if scales is not None else None
+            K = rebuild(dequantize(L_K[b, s_, :n], sK), B_K[h])
+            V = rebuild(dequantize(L_V[b, s_, :n], sV), B_V[h])
+            out[b, h] = attend(q[b, h], K, V, alpha)
     return out
