@@ -264,6 +264,38 @@ int lrattn_rebuild_decode(const lrattn_params* p,
                           lrattn_stream stream);
 
 /*
+ * Shared latent streams with per-query-head factors (AttentionPack page,
+ * section 2.A: the heads' keys and values are factored together, so the
+ * cache keeps one compressed row per token shared by the heads, and head h
+ * rebuilds with its own block of the decompression matrix).  For every b, h,
+ * with stream s = h / (Hq / S) (S = params.num_kv_heads streams; S = 1 is a
+ * single cache shared by all heads) and n = seq_lens[b]:
+ *   K[t] = Lk[t] . B_K[h]     V[t] = Lv[t] . B_V[h]      t < n
+ *   out[b,h,:] = sum_t softmax_t(softmax_scale * <q[b,h,:], K[t]>) V[t]
+ * with Lk[t] = L_K[b,s,t,:] (times scales[0,b,s,t] for int8), likewise Lv.
+ *   L_K, L_V [B, S, T, r]; scales [2, B, S, T] iff int8
+ *   B_K, B_V [Hq, r, d]   one block per query head
+ * Other tensors, dtypes, alignment, seq_lens handling, ownership, errors and
+ * determinism as in lrattn_decode; supported shapes as there, with the group
+ * Hq / S any multiple of 1, 2, 4 or 8 (heads run in groups of up to 8 that
+ * read the same stream).  Three launches: q~ for every head, the partitions,
+ * the combine.  The workspace holds the partial records and q~.
+ */
+int lrattn_shared_workspace_size(const lrattn_params* p, size_t* bytes);
+int lrattn_shared_decode(const lrattn_params* p,
+                         const void* q,
+                         const void* L_K,
+                         const void* L_V,
+                         const void* B_K,
+                         const void* B_V,
+                         const float* scales,
+                         const int32_t* seq_lens,
+                         void* out,
+                         void* workspace,
+                         size_t workspace_bytes,
+                         lrattn_stream stream);
+
+/*
  * The append step: the new token's latent rows, written into the cache.
  * WSVD page, section 2.A: each head's key (value) projection is factored per
  * head, W_Kh = A_Kh . B_Kh with rank r, so a token with hidden state x enters

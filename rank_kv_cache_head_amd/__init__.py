@@ -91,6 +91,9 @@ def lib() -> ctypes.CDLL:
                                     _VP, _VP, ctypes.c_size_t, _VP]
         L.lrattn_append_workspace_size.argtypes = [ctypes.POINTER(AppendParams),
                                                    ctypes.POINTER(ctypes.c_size_t)]
+        L.lrattn_shared_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                           ctypes.c_size_t, _VP]
+        L.lrattn_shared_workspace_size.argtypes = [_PP, ctypes.POINTER(ctypes.c_size_t)]
         L.lrattn_partition_kernel.argtypes = [_PP]
         L.lrattn_partition_kernel.restype = ctypes.c_char_p
         L.lrattn_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -104,6 +107,7 @@ def lib() -> ctypes.CDLL:
         for fn in ("lrattn_plan", "lrattn_workspace_size", "lrattn_decode", "lrattn_partition",
                    "lrattn_combine", "lrattn_dense_decode", "lrattn_rebuild_decode",
                    "lrattn_append", "lrattn_append_workspace_size",
+                   "lrattn_shared_decode", "lrattn_shared_workspace_size",
                    "lrattn_probe_read",
                    "lrattn_probe_copy"):
             getattr(L, fn).restype = ctypes.c_int
@@ -297,6 +301,53 @@ def rebuild_decode(q, L_K, L_V, B_K, B_V, seq_lens, rope=None, *, out=None, work
                                      _ptr(B_V), _ptr(rope), _ptr(seq_lens), _ptr(out), _ptr(ws),
                                      ws_bytes, _stream(stream))
     _check(st, "lrattn_rebuild_decode")
+    return out
+
+
+def shared_params_for(q, L_K, B_K, *, out_dtype=None, softmax_scale=None,
+                      num_splits: int = 0) -> Params:
+    """Parameter block for shared latent streams: q [B,Hq,d], L [B,S,T,r],
+    B_K [Hq,r,d] (one factor block per query head)."""
+    import torch
+    if q.dim() != 3 or L_K.dim() != 4 or B_K.dim() != 3:
+        raise ValueError("q [B,Hq,d], L [B,S,T,r], B [Hq,r,d] expected")
+    B, Hq, d = q.shape
+    B2, S, T, r = L_K.shape
+    if B2 != B or tuple(B_K.shape) != (Hq, r, d):
+        raise ValueError("shape mismatch")
+    od = F32 if out_dtype in (None, torch.float32) else (BF16 if out_dtype == torch.bfloat16 else -1)
+    return Params(B, Hq, S, d, r, T, _dtype_code(q), _dtype_code(L_K), _dtype_code(B_K), od,
+                  float(softmax_scale) if softmax_scale else 0.0, int(num_splits))
+
+
+def shared_workspace_size(p: Params) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().lrattn_shared_workspace_size(ctypes.byref(p), ctypes.byref(b)),
+           "lrattn_shared_workspace_size")
+    return b.value
+
+
+def shared_decode(q, L_K, L_V, B_K, B_V, seq_lens, scales=None, *, out=None, workspace=None,
+                  softmax_scale=None, num_splits: int = 0, out_dtype=None, stream=None):
+    """lrattn_shared_decode: shared latent streams, per-query-head factors."""
+    import torch
+    p = shared_params_for(q, L_K, B_K, out_dtype=out_dtype, softmax_scale=softmax_scale,
+                          num_splits=num_splits)
+    if tuple(L_V.shape) != tuple(L_K.shape) or tuple(B_V.shape) != tuple(B_K.shape):
+        raise ValueError("L_V / B_V shapes differ from L_K / B_K")
+    if tuple(seq_lens.shape) != (p.batch,) or seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32 [B]")
+    if out is None:
+        out = torch.empty((p.batch, p.num_q_heads, p.head_dim),
+                          dtype=torch.float32 if p.out_dtype == F32 else torch.bfloat16,
+                          device=q.device)
+    need = shared_workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib().lrattn_shared_decode(ctypes.byref(p), _ptr(q), _ptr(L_K), _ptr(L_V), _ptr(B_K),
+                                    _ptr(B_V), _ptr(scales), _ptr(seq_lens), _ptr(out),
+                                    _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "lrattn_shared_decode")
     return out
 
 

@@ -152,8 +152,11 @@ lrattn::PartitionArgs partition_args(const lrattn_params* p, const Plan& pl, con
   lrattn::PartitionArgs a;
   a.q = q; a.LK = LK; a.LV = LV; a.BK = BK; a.scales = scales; a.seq_lens = seq_lens;
   a.rope = nullptr;
+  a.qt_pre = nullptr;
   a.ws = static_cast<float*>(ws);
   a.B = p->batch; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.d = p->head_dim;
+  a.HG = p->num_kv_heads;                        // one group per kv-head
+  a.hps = p->num_q_heads / p->num_kv_heads;
   a.T = p->max_seq_len; a.P = pl.P; a.S = pl.S;
   a.q_dtype = p->q_dtype; a.f_dtype = p->factor_dtype;
   a.qscale = qscale_for(p);
@@ -166,6 +169,7 @@ lrattn::CombineArgs combine_args(const lrattn_params* p, const Plan& pl, const v
   a.seq_lens = seq_lens; a.ws = static_cast<const float*>(ws); a.merge = merge_args(p, BV, out);
   a.B = p->batch; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.d = p->head_dim;
   a.r = p->rank; a.T = p->max_seq_len; a.P = pl.P; a.S = pl.S;
+  a.factor_per_head = 0;
   return a;
 }
 
@@ -313,6 +317,30 @@ int lrattn_rebuild_decode(const lrattn_params* p, const void* q, const void* L_K
 }
 
 namespace {
+// Shared latent streams: query heads run in groups of up to 8 that read the
+// same stream; the plan is the grouped path's for that group size.
+int shared_group(const lrattn_params* p) {
+  const int hps = p->num_q_heads / p->num_kv_heads;
+  for (int g : {8, 4, 2, 1})
+    if (hps % g == 0) return g;
+  return 1;
+}
+
+int check_shared(const lrattn_params* p, lrattn_params* grouped, Plan* pl) {
+  if (!p) return LRATTN_ERR_NULL;
+  if (p->num_kv_heads <= 0 || p->num_q_heads <= 0 || p->num_q_heads % p->num_kv_heads)
+    return LRATTN_ERR_SHAPE;
+  *grouped = *p;
+  grouped->num_kv_heads = p->num_q_heads / shared_group(p);  // one "kv-head" per group
+  return check_params(grouped, pl);
+}
+
+size_t shared_ws_bytes(const lrattn_params* p, const Plan& pl) {
+  const size_t rec = lrattn::records_bytes(p->batch, p->num_q_heads, pl.P, p->rank);
+  const size_t qt = (size_t)p->batch * p->num_q_heads * p->rank * 4;
+  return rec + (qt + 255) / 256 * 256;
+}
+
 int check_append_params(const lrattn_append_params* p) {
   if (!p) return LRATTN_ERR_NULL;
   if (p->batch <= 0 || p->num_kv_heads <= 0 || p->model_dim <= 0 || p->rank <= 0 ||
@@ -363,6 +391,51 @@ int lrattn_append(const lrattn_append_params* p, const void* x, const void* A_K,
   a.KS = lrattn::append_chunks(p->num_kv_heads, p->model_dim);
   if (lrattn::launch_append(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return LRATTN_ERR_HIP;
+  return LRATTN_OK;
+}
+
+int lrattn_shared_workspace_size(const lrattn_params* p, size_t* bytes) {
+  if (!bytes) return LRATTN_ERR_NULL;
+  lrattn_params gp;
+  Plan pl;
+  const int st = check_shared(p, &gp, &pl);
+  if (st != LRATTN_OK) return st;
+  *bytes = shared_ws_bytes(p, pl);
+  return LRATTN_OK;
+}
+
+int lrattn_shared_decode(const lrattn_params* p, const void* q, const void* L_K, const void* L_V,
+                         const void* B_K, const void* B_V, const float* scales,
+                         const int32_t* seq_lens, void* out, void* workspace,
+                         size_t workspace_bytes, lrattn_stream stream) {
+  lrattn_params gp;
+  Plan pl;
+  int st = check_shared(p, &gp, &pl);
+  if (st == LRATTN_OK) st = check_partition_ptrs(p, q, L_K, L_V, B_K, scales, seq_lens);
+  if (st == LRATTN_OK) st = check_combine_ptrs(B_V, seq_lens, out);
+  if (st == LRATTN_OK && !workspace) st = LRATTN_ERR_WORKSPACE;
+  if (st == LRATTN_OK && !aligned16(workspace)) st = LRATTN_ERR_ALIGN;
+  if (st == LRATTN_OK && workspace_bytes < shared_ws_bytes(p, pl)) st = LRATTN_ERR_WORKSPACE;
+  if (st != LRATTN_OK) return st;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int G = shared_group(p);
+  float* qt = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       lrattn::records_bytes(p->batch, p->num_q_heads, pl.P,
+                                                             p->rank));
+  lrattn::AbsorbHeadsArgs ab;
+  ab.q = q; ab.BK = B_K; ab.qt = qt;
+  ab.B = p->batch; ab.Hq = p->num_q_heads; ab.d = p->head_dim; ab.r = p->rank;
+  ab.q_dtype = p->q_dtype; ab.f_dtype = p->factor_dtype; ab.qscale = qscale_for(p);
+  if (lrattn::launch_absorb_heads(ab, s) != hipSuccess) return LRATTN_ERR_HIP;
+  auto pa = partition_args(p, pl, q, L_K, L_V, B_K, scales, seq_lens, workspace);
+  pa.qt_pre = qt;
+  pa.HG = p->num_q_heads / G;                    // head groups
+  pa.hps = p->num_q_heads / p->num_kv_heads;     // heads per latent stream
+  if (lrattn::launch_partition(p->latent_dtype, p->rank, G, pa, s) != hipSuccess)
+    return LRATTN_ERR_HIP;
+  auto ca = combine_args(p, pl, B_V, seq_lens, out, workspace);
+  ca.factor_per_head = 1;
+  if (lrattn::launch_combine(G, ca, s) != hipSuccess) return LRATTN_ERR_HIP;
   return LRATTN_OK;
 }
 

@@ -45,8 +45,11 @@ struct PartitionArgs {
   const float* scales;     // [2, B, Hkv, T] or nullptr
   const int32_t* seq_lens; // [B]
   const float* rope;       // [T, d] cos | sin per position (rebuilt-key kernel), or nullptr
+  const float* qt_pre;     // [B, Hq, r] q~ already absorbed (per-head factors), or nullptr
   float* ws;               // [B, Hq, P, r + kRecPad]
   int32_t B, Hq, Hkv, d, T;
+  int32_t HG;              // head groups (grid y): query heads hg * G .. + G - 1
+  int32_t hps;             // query heads per latent stream: group hg reads stream hg * G / hps
   int32_t P, S;            // partitions, tokens per partition
   int32_t q_dtype, f_dtype;
   float qscale;            // softmax_scale * log2(e)
@@ -58,6 +61,7 @@ struct CombineArgs {
   MergeArgs merge;
   int32_t B, Hq, Hkv, d, r, T;
   int32_t P, S;
+  int32_t factor_per_head;  // B_V indexed by query head (shared latent streams)
 };
 
 // True when a partition kernel is compiled for (latent dtype, rank, group).
@@ -74,6 +78,18 @@ hipError_t launch_combine(int group, const CombineArgs& a, hipStream_t s);
 // {64, 128}, r in {32, 64}, group in {1, 2, 4, 8}); a.rope selects the
 // rotating instantiation.  Same grid and records as launch_partition.
 bool rebuild_supported(int head_dim, int rank, int group);
+
+// q~ per query head with its own factor (shared latent streams):
+// qt[b][h][j] = qscale * sum_i q[b][h][i] * B_K[h][j][i], fp32.
+struct AbsorbHeadsArgs {
+  const void* q;    // [B, Hq, d]
+  const void* BK;   // [Hq, r, d]
+  float* qt;        // [B, Hq, r]
+  int32_t B, Hq, d, r;
+  int32_t q_dtype, f_dtype;
+  float qscale;
+};
+hipError_t launch_absorb_heads(const AbsorbHeadsArgs& a, hipStream_t s);
 hipError_t launch_rebuild(int head_dim, int rank, int group, const PartitionArgs& a,
                           hipStream_t s);
 

@@ -683,10 +683,36 @@ __device__ __forceinline__ void identity_finish(const PartitionArgs& a, AbsorbIn
 // The partition prologue: q~ into qt_lds (fp32 [G][R]), with `issue` (the
 // first latent loads) placed at position kAfter: 0 first, 1 once q is in
 // flight / staged, 2 after the absorption.
+// q~ absorbed beforehand (per-query-head factors): the G rows of heads
+// hg * G .. + G - 1, fp32, straight into qt_lds.
+template <int R, int G>
+__device__ __forceinline__ u32x4 pre_issue(const PartitionArgs& a, int b, int hg) {
+  const auto rq = make_rsrc(a.qt_pre + ((size_t)b * a.Hq + (size_t)hg * G) * R,
+                            (uint32_t)(G * R) * 4u);
+  return __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(threadIdx.x * 16u), 0, 0);
+}
+
+template <int R, int G>
+__device__ __forceinline__ void pre_finish(const u32x4& w, float* qt_lds) {
+  static_assert(G * R <= 4 * kThreads, "one 16-byte piece per thread");
+  const int i = threadIdx.x * 4;
+  // threads past the G * R values store into the padding
+  float* dst = i < G * R ? qt_lds + i : qt_lds + G * R;
+  dst[0] = __uint_as_float(w[0]);
+  dst[1] = __uint_as_float(w[1]);
+  dst[2] = __uint_as_float(w[2]);
+  dst[3] = __uint_as_float(w[3]);
+  __syncthreads();
+}
+
 template <int R, int G, int kAfter, class Issue>
-__device__ __forceinline__ void prologue(const PartitionArgs& a, int b, int g, float* q_lds,
-                                         float* qt_lds, Issue&& issue) {
-  if (a.BK == nullptr) {
+__device__ __forceinline__ void prologue(const PartitionArgs& a, int b, int hg, int g,
+                                         float* q_lds, float* qt_lds, Issue&& issue) {
+  if (a.qt_pre != nullptr) {
+    const u32x4 w = pre_issue<R, G>(a, b, hg);
+    if constexpr (kAfter < 2) issue();
+    pre_finish<R, G>(w, qt_lds);
+  } else if (a.BK == nullptr) {
     AbsorbIn<R, G> in;
     identity_issue<R, G>(a, b, g, in);
     if constexpr (kAfter < 2) issue();
@@ -720,11 +746,11 @@ struct PartLds {
 // per query head of the group: acc[0..R), m, l.  red_acc [wave][h][R],
 // red_m and red_l [wave][h] are in LDS; the caller has synchronized.
 template <int R, int G>
-__device__ __forceinline__ void write_records(const PartitionArgs& a, int b, int g, int p,
+__device__ __forceinline__ void write_records(const PartitionArgs& a, int b, int hg, int p,
                                               const float* red_acc, const float* red_m,
                                               const float* red_l) {
   const int tid = threadIdx.x;
-  float* const rec0 = a.ws + ((size_t)b * a.Hq + (size_t)g * G) * (size_t)a.P * (R + kRecPad);
+  float* const rec0 = a.ws + ((size_t)b * a.Hq + (size_t)hg * G) * (size_t)a.P * (R + kRecPad);
   for (int it = tid; it < G * R; it += kThreads) {
     const int h = it / R, j = it - h * R;
     float M = red_m[h];
@@ -754,7 +780,9 @@ void partition_kernel(PartitionArgs a) {
   constexpr int EPL = Gm::kEPL, LPR = Gm::kLPR, CH = Gm::kChunk;
   constexpr bool kInt8 = std::is_same<LT, LatI8>::value;
 
-  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // head group hg (its G query heads) reads latent stream g
+  const int p = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  const int g = hg * G / a.hps;
   // seq_lens[b] is one value for the whole workgroup; keeping it in a scalar
   // register keeps the buffer descriptors below scalar (a descriptor the
   // compiler must treat as per-lane costs a readfirstlane loop per load)
@@ -788,7 +816,7 @@ void partition_kernel(PartitionArgs a) {
   // q and B_K are requested first, then the first step's latents; the
   // absorption then runs while the latents are in flight.
   Step<LT, R, G> cur;
-  prologue<R, G, LRATTN_LATENTS_AFTER>(a, b, g, q_lds, qt_lds, [&]() {
+  prologue<R, G, LRATTN_LATENTS_AFTER>(a, b, hg, g, q_lds, qt_lds, [&]() {
     load_step(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv);
   });
 
@@ -864,7 +892,7 @@ void partition_kernel(PartitionArgs a) {
   }
   __syncthreads();
 
-  write_records<R, G>(a, b, g, p, lds.acc, lds.m, lds.l);
+  write_records<R, G>(a, b, hg, p, lds.acc, lds.m, lds.l);
 }
 
 // ------------------------------------------------ partition, matrix-core scores
@@ -1099,7 +1127,7 @@ __device__ __forceinline__ void split3x8(const float (&x)[8], bf16x8 (&t)[3]) {
 // lanes, its accumulators over the slots (one reference per head for the
 // whole wave: plain sums), then the fixed-order merge of the waves.
 template <int R, int G, int NT>
-__device__ __forceinline__ void mfma_epilogue(const PartitionArgs& a, int b, int g, int p,
+__device__ __forceinline__ void mfma_epilogue(const PartitionArgs& a, int b, int hg, int p,
                                               const float (&mm)[4], const float (&ll)[4],
                                               float (&acc)[G][8], PartLds<R, G>& lds) {
   using Mg = MGeo<R, G, NT>;
@@ -1139,7 +1167,7 @@ __device__ __forceinline__ void mfma_epilogue(const PartitionArgs& a, int b, int
     }
   }
   __syncthreads();
-  write_records<R, G>(a, b, g, p, lds.acc, lds.m, lds.l);
+  write_records<R, G>(a, b, hg, p, lds.acc, lds.m, lds.l);
 }
 
 template <int R, int G>
@@ -1155,7 +1183,9 @@ void partition_mfma_kernel(PartitionArgs a) {
   using Mg = MGeo<R, G>;
   constexpr int KC = Mg::kKC, LPR = Mg::kLPR, CH = Mg::kChunk;
 
-  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // head group hg (its G query heads) reads latent stream g
+  const int p = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  const int g = hg * G / a.hps;
   const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
   const int t0 = p * a.S;
   const int t1 = min(t0 + a.S, len);
@@ -1176,7 +1206,7 @@ void partition_mfma_kernel(PartitionArgs a) {
   const uint32_t voff = (uint32_t)(slot * Mg::kRowBytes + cc * 16);
 
   MStep<R, G> cur;
-  prologue<R, G, LRATTN_MFMA_LATENTS_AFTER>(a, b, g, lds.base.q, lds.base.qt, [&]() {
+  prologue<R, G, LRATTN_MFMA_LATENTS_AFTER>(a, b, hg, g, lds.base.q, lds.base.qt, [&]() {
     load_mstep(cur, wave * CH, koff, voff, rk, rv);
   });
 
@@ -1219,7 +1249,7 @@ void partition_mfma_kernel(PartitionArgs a) {
     else load_mstep(cur, cb + kWaves * CH, koff, voff, rk, rv);
   }
 
-  mfma_epilogue<R, G, Mg::kNT>(a, b, g, p, mm, ll, acc, lds.base);
+  mfma_epilogue<R, G, Mg::kNT>(a, b, hg, p, mm, ll, acc, lds.base);
 }
 
 // --------------------------------------- partition, rebuilt (and rotated) keys
@@ -1355,7 +1385,9 @@ void partition_rebuild_kernel(PartitionArgs a) {
   constexpr int LPR = Mg::kLPR, KC = R / 32;
   constexpr int CH = 16;  // tokens per wave per step
 
-  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // head group hg (its G query heads) reads latent stream g
+  const int p = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  const int g = hg * G / a.hps;
   const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
   const int t0 = p * a.S;
   const int t1 = min(t0 + a.S, len);
@@ -1475,7 +1507,7 @@ void partition_rebuild_kernel(PartitionArgs a) {
     softmax_values<R, G, 1>(s, cur.lat, lane, mm, ll, acc, wl);
     load_rstep(cur, cb + kWaves * CH, koff, voff, rk, rv, rr, rope_off);
   }
-  mfma_epilogue<R, G, 1>(a, b, g, p, mm, ll, acc, lds.base);
+  mfma_epilogue<R, G, 1>(a, b, hg, p, mm, ll, acc, lds.base);
 }
 
 // ------------------------------------------------------------------ combine
@@ -1541,7 +1573,8 @@ void combine_kernel(CombineArgs a) {
   constexpr int NB = kThreads / D, RB = R / NB;
   static_assert(NB * D == kThreads && RB * NB == R, "combine tiling");
   const int hq = blockIdx.x, b = blockIdx.y;
-  const int g = hq / (a.Hq / a.Hkv);
+  // B_V block: per kv-head, or per query head (shared latent streams)
+  const int g = a.factor_per_head ? hq : hq / (a.Hq / a.Hkv);
   const int tid = threadIdx.x;
   const MergeArgs& mg = a.merge;
 
@@ -1705,7 +1738,7 @@ constexpr bool mfma_scores(int latent_dtype, int rank, int group) {
 
 template <class LT, int R>
 hipError_t launch_pg(int group, const PartitionArgs& a, hipStream_t s) {
-  const dim3 grid(a.P, a.Hkv, a.B), block(kThreads);
+  const dim3 grid(a.P, a.HG, a.B), block(kThreads);
   if constexpr (mfma_scores(std::is_same<LT, LatBF16>::value ? LRATTN_BF16 : -1, R, 4)) {
     if (group == 4) {
       hipLaunchKernelGGL((partition_mfma_kernel<R, 4>), grid, block, 0, s, a);
@@ -1742,7 +1775,7 @@ hipError_t launch_pr(int rank, int group, const PartitionArgs& a, hipStream_t s)
 
 template <int R, int D>
 hipError_t launch_rg(int group, bool rot, const PartitionArgs& a, hipStream_t s) {
-  const dim3 grid(a.P, a.Hkv, a.B), block(kThreads);
+  const dim3 grid(a.P, a.HG, a.B), block(kThreads);
   switch (group) {
     case 1:
       if (rot) hipLaunchKernelGGL((partition_rebuild_kernel<R, 1, D, true>), grid, block, 0, s, a);

@@ -240,3 +240,24 @@ def test_append_validates_on_host():
     assert call(ap(latent_dtype=lr.I8)) == -1              # int8 without scales
     assert call(ap(), lv=MISALIGNED) == -5
     assert call(ap(latent_dtype=lr.I8), sc=MISALIGNED) == -5
+
+
+def test_shared_decode_validates_on_host():
+    L = lr.lib()
+    def call(p, ws=ALIGNED, ws_bytes=0, **kw):
+        a = dict(q=ALIGNED, lk=ALIGNED, lv=ALIGNED, bk=ALIGNED, bv=ALIGNED, sc=None, seq=ALIGNED,
+                 out=ALIGNED)
+        a.update(kw)
+        return L.lrattn_shared_decode(ctypes.byref(p), a["q"], a["lk"], a["lv"], a["bk"], a["bv"],
+                                      a["sc"], a["seq"], a["out"], ws, ws_bytes, None)
+    one = params(num_q_heads=32, num_kv_heads=1)        # one stream shared by 32 heads
+    need = lr.shared_workspace_size(one)
+    P, _ = lr.plan(params(num_q_heads=32, num_kv_heads=4))   # grouped in 8s: 4 groups
+    assert need >= 2 * 32 * P * 68 * 4 + 2 * 32 * 64 * 4
+    assert call(params(num_q_heads=30, num_kv_heads=4)) == -2
+    assert call(params(num_q_heads=12, num_kv_heads=1), ws_bytes=0) == -6   # group of 4s
+    assert call(params(num_q_heads=6, num_kv_heads=2, rank=24)) == -4
+    assert call(one, bk=None) == -1
+    assert call(one, bv=MISALIGNED) == -5
+    assert call(one, ws=None, ws_bytes=need) == -6
+    assert call(one, ws_bytes=need - 1) == -6

@@ -385,6 +385,62 @@ def test_rebuild_full_size_rotated():
     assert err <= 2e-5, err
 
 
+@pytest.mark.parametrize("lt,S,Hq,r,d", [("bf16", 1, 32, 64, 128), ("bf16", 1, 12, 48, 128),
+                                         ("f16", 2, 16, 32, 64), ("i8", 1, 40, 32, 128),
+                                         ("f32", 1, 8, 16, 64), ("bf16", 3, 3, 32, 128)])
+def test_shared_decode_matches_oracle(lt, S, Hq, r, d):
+    """Shared latent streams (AttentionPack's multi-head compression) with a
+    factor block per query head: q~ per head, partitions over head groups of
+    up to 8 reading the same stream, combine with each head's B_V."""
+    import torch
+    import rank_kv_cache_head_amd as lr
+    base = "int8" if lt == "i8" else "gqa_vlm"
+    lens = [300, 97, 16, 1]
+    kw = dict(B=len(lens), Hq=Hq, Hkv=Hq, d=d, r=r, T=300, seq_lens=lens,
+              factor_std=1.0 / np.sqrt(r))
+    if lt != "i8":
+        kw["latent_dtype"] = lt
+    if lt == "f32":
+        kw.update(q_dtype="f32", factor_dtype="f32")
+    w = workloads.make(base, seed=1100 + Hq + r, **kw)
+    dev = to_device(w)
+    LK = dev["L_K"][:, :S].contiguous()
+    LV = dev["L_V"][:, :S].contiguous()
+    sc = None if dev["scales"] is None else dev["scales"][:, :, :S].contiguous()
+    f = oracle.as_float64
+    ref = oracle.decode_shared(f(w.q, w.q_dtype), f(w.L_K, w.latent_dtype)[:, :S],
+                               f(w.L_V, w.latent_dtype)[:, :S], f(w.B_K, w.factor_dtype),
+                               f(w.B_V, w.factor_dtype), w.seq_lens,
+                               scales=None if w.scales is None else w.scales[:, :, :S].astype(np.float64),
+                               softmax_scale=w.softmax_scale)
+    for splits in (0, 3):
+        say(f"shared {lt} S={S} Hq={Hq} r={r} d={d} splits={splits}")
+        got = lr.shared_decode(dev["q"], LK, LV, dev["B_K"], dev["B_V"], dev["seq_lens"], sc,
+                               softmax_scale=w.softmax_scale, num_splits=splits)
+        torch.cuda.synchronize()
+        err = rel_rowmax(got.cpu().numpy(), ref)
+        say(f"  err {err:.3e}")
+        assert err <= 2e-5, err
+
+
+def test_shared_equals_per_head_cache():
+    """A stream shared by G heads gives the result of a per-head cache that
+    repeats the stream's latents for each head (same factors)."""
+    import torch
+    import rank_kv_cache_head_amd as lr
+    w = workloads.make("gqa_vlm", seed=1200, B=2, Hq=16, Hkv=16, d=128, r=64, T=256,
+                       seq_lens=[256, 100], factor_std=0.125)
+    dev = to_device(w)
+    LK1, LV1 = dev["L_K"][:, :1].contiguous(), dev["L_V"][:, :1].contiguous()
+    say("shared == per-head replicated")
+    a = lr.shared_decode(dev["q"], LK1, LV1, dev["B_K"], dev["B_V"], dev["seq_lens"])
+    b = lr.decode(dev["q"], LK1.expand(2, 16, 256, 64).contiguous(),
+                  LV1.expand(2, 16, 256, 64).contiguous(), dev["B_K"], dev["B_V"],
+                  dev["seq_lens"])
+    torch.cuda.synchronize()
+    assert rel_rowmax(a.cpu().numpy(), b.cpu().numpy().astype(np.float64)) <= 2e-5
+
+
 def test_guard_bands_untouched():
     import torch
     import rank_kv_cache_head_amd as lr
