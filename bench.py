@@ -59,6 +59,8 @@ def parse():
                     help="skip the rebuilt-key (and rotated-key) mode timing")
     ap.add_argument("--no-append", action="store_true",
                     help="skip the append-step timing")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="skip the shared-latent (one stream for all heads) timing")
     return ap.parse_args()
 
 
@@ -278,6 +280,8 @@ def main():
         line["rebuilt_keys"] = rebuilt_keys(w, torch, lr, args, base, sets, ms_per_step)
     if not args.no_append:
         line["append_step"] = append_step(w, torch, lr, args)
+    if not args.no_shared:
+        line["shared_latent"] = shared_latent(w, torch, lr, args, ms_per_step)
     if args.probe:
         line["probe"] = run_probe(torch, lr)
     if not args.no_cpu_baseline:
@@ -411,6 +415,47 @@ def append_step(w, torch, lr, args):
            2 * w.batch * w.num_kv_heads * w.rank * esz + (0 if sc is None else 2 * w.batch * w.num_kv_heads * 4))
     return dict(us_per_call=us, model_dim=D, bytes_per_call=alg, GBps=alg / (us / 1e6) / 1e9,
                 kernels="append_partial_kernel + append_finish_kernel")
+
+
+def shared_latent(w, torch, lr, args, grouped_ms):
+    """The workload's batch, query heads and lengths over one latent stream of
+    R = 128 bf16 values per token shared by all heads, each head with its own
+    factor blocks (AttentionPack's multi-head compression), timed like the
+    main loop.  Random values drawn on the device."""
+    if w.latent_dtype == "i8" or w.num_q_heads < 8:
+        return None
+    R, d, Hq = 128, w.head_dim, w.num_q_heads
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2024)
+    shp = (w.batch, 1, w.max_seq_len, R)
+    LK = torch.randn(shp, generator=g, device="cuda").to(torch.bfloat16)
+    LV = torch.randn(shp, generator=g, device="cuda").to(torch.bfloat16)
+    BK = (torch.randn((Hq, R, d), generator=g, device="cuda") / math.sqrt(R)).to(torch.bfloat16)
+    BV = (torch.randn((Hq, R, d), generator=g, device="cuda") / math.sqrt(R)).to(torch.bfloat16)
+    q = torch.randn((w.batch, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    import numpy as np
+    sl = torch.from_numpy(w.seq_lens.astype(np.int32)).cuda()
+    p = lr.shared_params_for(q, LK, BK, num_splits=args.num_splits)
+    ws = torch.empty(lr.shared_workspace_size(p), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, Hq, d), device="cuda")
+    run = lambda: lr.shared_decode(q, LK, LV, BK, BV, sl, out=out, workspace=ws,
+                                   num_splits=args.num_splits)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    valid = int(w.seq_lens.sum())
+    lat = valid * 2 * R * 2
+    res = dict(ms_per_step=ms, tokens_per_s=w.batch / (ms / 1e3), rank=R, streams=1,
+               latent_bytes_per_step=lat, latent_GBps=lat / (ms / 1e3) / 1e9,
+               head_groups=Hq // 8, vs_grouped=ms / grouped_ms)
+    del LK, LV
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_probe(torch, lr):

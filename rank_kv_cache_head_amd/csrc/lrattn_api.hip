@@ -157,6 +157,7 @@ lrattn::PartitionArgs partition_args(const lrattn_params* p, const Plan& pl, con
   a.B = p->batch; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.d = p->head_dim;
   a.HG = p->num_kv_heads;                        // one group per kv-head
   a.hps = p->num_q_heads / p->num_kv_heads;
+  a.xcd_group = 0;
   a.T = p->max_seq_len; a.P = pl.P; a.S = pl.S;
   a.q_dtype = p->q_dtype; a.f_dtype = p->factor_dtype;
   a.qscale = qscale_for(p);
@@ -431,6 +432,8 @@ int lrattn_shared_decode(const lrattn_params* p, const void* q, const void* L_K,
   pa.qt_pre = qt;
   pa.HG = p->num_q_heads / G;                    // head groups
   pa.hps = p->num_q_heads / p->num_kv_heads;     // heads per latent stream
+  // the head groups of a tile share its latents: keep them on one XCD
+  pa.xcd_group = pa.HG > 1 && (int64_t)8 * pa.HG * ((pl.P * (int64_t)p->batch + 7) / 8) < (1LL << 31);
   if (lrattn::launch_partition(p->latent_dtype, p->rank, G, pa, s) != hipSuccess)
     return LRATTN_ERR_HIP;
   auto ca = combine_args(p, pl, B_V, seq_lens, out, workspace);

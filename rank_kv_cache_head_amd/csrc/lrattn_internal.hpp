@@ -51,6 +51,7 @@ struct PartitionArgs {
   int32_t HG;              // head groups (grid y): query heads hg * G .. + G - 1
   int32_t hps;             // query heads per latent stream: group hg reads stream hg * G / hps
   int32_t P, S;            // partitions, tokens per partition
+  int32_t xcd_group;       // 1: one-dimensional grid, head groups of a tile on one XCD
   int32_t q_dtype, f_dtype;
   float qscale;            // softmax_scale * log2(e)
 };

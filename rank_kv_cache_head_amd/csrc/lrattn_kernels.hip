@@ -233,16 +233,18 @@ struct Geo {
   static_assert(kAct <= 16, "latent row wider than 16 lane loads");
 };
 
-// One lane load of kWords 32-bit words (16 or 8 bytes), streaming cache policy.
-template <int kWords>
+// One lane load of kWords 32-bit words (16 or 8 bytes) with cache policy kAux:
+// LRATTN_LOAD_AUX (non-temporal) for latents read once, 0 where other
+// workgroups of the same XCD read the same latents (shared streams).
+template <int kWords, int kAux = LRATTN_LOAD_AUX>
 __device__ __forceinline__ void load_words(uint32_t (&w)[kWords], __amdgpu_buffer_rsrc_t r,
                                            uint32_t off) {
   if constexpr (kWords == 4) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, LRATTN_LOAD_AUX);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kAux);
     w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
   } else {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, LRATTN_LOAD_AUX);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kAux);
     w[0] = v[0]; w[1] = v[1];
   }
 }
@@ -257,7 +259,7 @@ struct Step {
   float sv[Geo<LT, R, G>::kU];
 };
 
-template <class LT, int R, int G>
+template <class LT, int R, int G, int kAux = LRATTN_LOAD_AUX>
 __device__ __forceinline__ void load_step(Step<LT, R, G>& st, int cb, int slot, uint32_t lane_off,
                                           __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                           __amdgpu_buffer_rsrc_t rsk, __amdgpu_buffer_rsrc_t rsv) {
@@ -265,10 +267,10 @@ __device__ __forceinline__ void load_step(Step<LT, R, G>& st, int cb, int slot, 
   constexpr int U = Gm::kU, RPW = Gm::kRPW;
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    load_words<Gm::kWords>(st.k[u], rk, (uint32_t)(cb + u * RPW) * Gm::kRowBytes + lane_off);
+    load_words<Gm::kWords, kAux>(st.k[u], rk, (uint32_t)(cb + u * RPW) * Gm::kRowBytes + lane_off);
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    load_words<Gm::kWords>(st.v[u], rv, (uint32_t)(cb + u * RPW) * Gm::kRowBytes + lane_off);
+    load_words<Gm::kWords, kAux>(st.v[u], rv, (uint32_t)(cb + u * RPW) * Gm::kRowBytes + lane_off);
   if constexpr (std::is_same<LT, LatI8>::value) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -369,6 +371,26 @@ __device__ __forceinline__ void compute_step(
       for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(w[u][h], x[e], acc[h][e]);
     }
   }
+}
+
+// The workgroup's (partition p, head group hg, sequence b).  Normally the
+// grid is (P, HG, B).  With a.xcd_group the grid is one-dimensional and the
+// HG head groups of one (p, b) tile take linear ids 8 apart: workgroups are
+// handed to the 8 XCDs in turn by linear id, so those groups run on one XCD,
+// close in time, and the tile's latents (read by every head group of a shared
+// stream) are fetched from HBM once and then served by that XCD's L2.
+// Returns false for the padding workgroups of the last round of tiles.
+__device__ __forceinline__ bool tile_of(const PartitionArgs& a, int& p, int& hg, int& b) {
+  if (!a.xcd_group) {
+    p = blockIdx.x; hg = blockIdx.y; b = blockIdx.z;
+    return true;
+  }
+  const int L = blockIdx.x, x = L & 7, k = L >> 3;
+  hg = k % a.HG;
+  const int t = 8 * (k / a.HG) + x;  // tile: p fastest
+  p = t % a.P;
+  b = t / a.P;
+  return b < a.B;
 }
 
 // Sum of `x` over aligned groups of n lanes, n in {8, 16, 32} (runtime, uniform).
@@ -772,7 +794,7 @@ __device__ __forceinline__ void write_records(const PartitionArgs& a, int b, int
   }
 }
 
-template <class LT, int R, int G>
+template <class LT, int R, int G, int kAux = LRATTN_LOAD_AUX>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Geo<LT, R, G>::kWavesPerEU)))
 void partition_kernel(PartitionArgs a) {
@@ -781,7 +803,8 @@ void partition_kernel(PartitionArgs a) {
   constexpr bool kInt8 = std::is_same<LT, LatI8>::value;
 
   // head group hg (its G query heads) reads latent stream g
-  const int p = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  int p, hg, b;
+  if (!tile_of(a, p, hg, b)) return;
   const int g = hg * G / a.hps;
   // seq_lens[b] is one value for the whole workgroup; keeping it in a scalar
   // register keeps the buffer descriptors below scalar (a descriptor the
@@ -817,7 +840,7 @@ void partition_kernel(PartitionArgs a) {
   // absorption then runs while the latents are in flight.
   Step<LT, R, G> cur;
   prologue<R, G, LRATTN_LATENTS_AFTER>(a, b, hg, g, q_lds, qt_lds, [&]() {
-    load_step(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv);
+    load_step<LT, R, G, kAux>(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv);
   });
 
   QtView<LT, R, G> qt;
@@ -845,7 +868,7 @@ void partition_kernel(PartitionArgs a) {
     if constexpr (LRATTN_PREFETCH) {
       // double buffering: step i+1 is in flight while step i computes; past
       // the partition the loads return zero without touching memory
-      load_step(nxt, cb + kWaves * CH, slot, lane_off, rk, rv, rsk, rsv);
+      load_step<LT, R, G, kAux>(nxt, cb + kWaves * CH, slot, lane_off, rk, rv, rsk, rsv);
     }
     if (cb + CH <= ntok)
       compute_step<LT, R, G, false>(cur, cb, ntok, slot, qt, m, l, acc);
@@ -854,7 +877,7 @@ void partition_kernel(PartitionArgs a) {
     if constexpr (LRATTN_PREFETCH) {
       cur = nxt;
     } else {
-      load_step(cur, cb + kWaves * CH, slot, lane_off, rk, rv, rsk, rsv);
+      load_step<LT, R, G, kAux>(cur, cb + kWaves * CH, slot, lane_off, rk, rv, rsk, rsv);
     }
   }
 
@@ -937,7 +960,7 @@ struct MStep {
   uint32_t v[NT][MGeo<R, G, NT>::kVU][4];
 };
 
-template <int R, int G, int NT>
+template <int R, int G, int NT, int kAux = LRATTN_LOAD_AUX>
 __device__ __forceinline__ void load_mstep(MStep<R, G, NT>& st, int cb, uint32_t koff,
                                            uint32_t voff, __amdgpu_buffer_rsrc_t rk,
                                            __amdgpu_buffer_rsrc_t rv) {
@@ -946,14 +969,14 @@ __device__ __forceinline__ void load_mstep(MStep<R, G, NT>& st, int cb, uint32_t
   for (int t = 0; t < Mg::kNT; ++t) {
     const uint32_t base = (uint32_t)(cb + 16 * t) * Mg::kRowBytes;
 #pragma unroll
-    for (int c = 0; c < Mg::kKC; ++c) load_words<4>(st.k[t][c], rk, base + koff + 64u * c);
+    for (int c = 0; c < Mg::kKC; ++c) load_words<4, kAux>(st.k[t][c], rk, base + koff + 64u * c);
   }
 #pragma unroll
   for (int t = 0; t < Mg::kNT; ++t) {
     const uint32_t base = (uint32_t)(cb + 16 * t) * Mg::kRowBytes;
 #pragma unroll
     for (int u = 0; u < Mg::kVU; ++u)
-      load_words<4>(st.v[t][u], rv, base + voff + (uint32_t)(u * Mg::kRPW) * Mg::kRowBytes);
+      load_words<4, kAux>(st.v[t][u], rv, base + voff + (uint32_t)(u * Mg::kRPW) * Mg::kRowBytes);
   }
 }
 
@@ -1176,7 +1199,7 @@ struct MPartLds {
   float w[kWaves * MGeo<R, G>::kChunk * G];
 };
 
-template <int R, int G>
+template <int R, int G, int kAux = LRATTN_LOAD_AUX>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(MGeo<R, G>::kWavesPerEU)))
 void partition_mfma_kernel(PartitionArgs a) {
@@ -1184,7 +1207,8 @@ void partition_mfma_kernel(PartitionArgs a) {
   constexpr int KC = Mg::kKC, LPR = Mg::kLPR, CH = Mg::kChunk;
 
   // head group hg (its G query heads) reads latent stream g
-  const int p = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  int p, hg, b;
+  if (!tile_of(a, p, hg, b)) return;
   const int g = hg * G / a.hps;
   const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
   const int t0 = p * a.S;
@@ -1207,7 +1231,7 @@ void partition_mfma_kernel(PartitionArgs a) {
 
   MStep<R, G> cur;
   prologue<R, G, LRATTN_MFMA_LATENTS_AFTER>(a, b, hg, g, lds.base.q, lds.base.qt, [&]() {
-    load_mstep(cur, wave * CH, koff, voff, rk, rv);
+    load_mstep<R, G, Mg::kNT, kAux>(cur, wave * CH, koff, voff, rk, rv);
   });
 
   // A operands: row lane % 16 is head (lane % 16) % G; k-group lane / 16
@@ -1240,13 +1264,13 @@ void partition_mfma_kernel(PartitionArgs a) {
   float* wl = lds.w + wave * CH * G;
   for (int cb = wave * CH; cb < ntok; cb += kWaves * CH) {
     MStep<R, G> nxt;
-    if constexpr (LRATTN_PREFETCH) load_mstep(nxt, cb + kWaves * CH, koff, voff, rk, rv);
+    if constexpr (LRATTN_PREFETCH) load_mstep<R, G, Mg::kNT, kAux>(nxt, cb + kWaves * CH, koff, voff, rk, rv);
     if (cb + CH <= ntok)
       compute_mstep<R, G, false>(cur, cb, ntok, lane, qa, mm, ll, acc, wl);
     else
       compute_mstep<R, G, true>(cur, cb, ntok, lane, qa, mm, ll, acc, wl);
     if constexpr (LRATTN_PREFETCH) cur = nxt;
-    else load_mstep(cur, cb + kWaves * CH, koff, voff, rk, rv);
+    else load_mstep<R, G, Mg::kNT, kAux>(cur, cb + kWaves * CH, koff, voff, rk, rv);
   }
 
   mfma_epilogue<R, G, Mg::kNT>(a, b, hg, p, mm, ll, acc, lds.base);
@@ -1386,7 +1410,8 @@ void partition_rebuild_kernel(PartitionArgs a) {
   constexpr int CH = 16;  // tokens per wave per step
 
   // head group hg (its G query heads) reads latent stream g
-  const int p = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  int p, hg, b;
+  if (!tile_of(a, p, hg, b)) return;
   const int g = hg * G / a.hps;
   const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
   const int t0 = p * a.S;
@@ -1736,24 +1761,37 @@ constexpr bool mfma_scores(int latent_dtype, int rank, int group) {
          (group == 4 || group == 8);
 }
 
+// Head groups sharing a latent stream (a.xcd_group) keep the latents in L2
+// for each other: cache policy 0 instead of non-temporal, for groups of 4 or
+// 8 heads (the shared-stream groups; smaller groups keep the default).
 template <class LT, int R>
 hipError_t launch_pg(int group, const PartitionArgs& a, hipStream_t s) {
-  const dim3 grid(a.P, a.HG, a.B), block(kThreads);
+  const dim3 grid = a.xcd_group ? dim3(8 * a.HG * ((a.P * a.B + 7) / 8)) : dim3(a.P, a.HG, a.B);
+  const dim3 block(kThreads);
+  const bool keep = a.xcd_group != 0;
   if constexpr (mfma_scores(std::is_same<LT, LatBF16>::value ? LRATTN_BF16 : -1, R, 4)) {
     if (group == 4) {
-      hipLaunchKernelGGL((partition_mfma_kernel<R, 4>), grid, block, 0, s, a);
+      if (keep) hipLaunchKernelGGL((partition_mfma_kernel<R, 4, 0>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((partition_mfma_kernel<R, 4>), grid, block, 0, s, a);
       return hipGetLastError();
     }
     if (group == 8) {
-      hipLaunchKernelGGL((partition_mfma_kernel<R, 8>), grid, block, 0, s, a);
+      if (keep) hipLaunchKernelGGL((partition_mfma_kernel<R, 8, 0>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((partition_mfma_kernel<R, 8>), grid, block, 0, s, a);
       return hipGetLastError();
     }
   }
   switch (group) {
     case 1: hipLaunchKernelGGL((partition_kernel<LT, R, 1>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((partition_kernel<LT, R, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((partition_kernel<LT, R, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((partition_kernel<LT, R, 8>), grid, block, 0, s, a); break;
+    case 4:
+      if (keep) hipLaunchKernelGGL((partition_kernel<LT, R, 4, 0>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((partition_kernel<LT, R, 4>), grid, block, 0, s, a);
+      break;
+    case 8:
+      if (keep) hipLaunchKernelGGL((partition_kernel<LT, R, 8, 0>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((partition_kernel<LT, R, 8>), grid, block, 0, s, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1775,7 +1813,8 @@ hipError_t launch_pr(int rank, int group, const PartitionArgs& a, hipStream_t s)
 
 template <int R, int D>
 hipError_t launch_rg(int group, bool rot, const PartitionArgs& a, hipStream_t s) {
-  const dim3 grid(a.P, a.HG, a.B), block(kThreads);
+  const dim3 grid = a.xcd_group ? dim3(8 * a.HG * ((a.P * a.B + 7) / 8)) : dim3(a.P, a.HG, a.B);
+  const dim3 block(kThreads);
   switch (group) {
     case 1:
       if (rot) hipLaunchKernelGGL((partition_rebuild_kernel<R, 1, D, true>), grid, block, 0, s, a);
