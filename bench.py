@@ -372,6 +372,7 @@ def rebuilt_keys(w, torch, lr, args, base, sets, absorbed_ms):
         res[name] = dict(ms_per_step=ms, tokens_per_s=w.batch / (ms / 1e3),
                          vs_absorbed=ms / absorbed_ms)
     res["kernel"] = "partition_rebuild_kernel"
+    res["num_splits"], res["split_tokens"] = lr.rebuild_plan(decs[0].params)
     return res
 
 

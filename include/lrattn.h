@@ -247,9 +247,15 @@ int lrattn_dense_decode(const lrattn_params* p,
  * T * d * 4 < 2^31 when rope is given; anything else returns
  * LRATTN_ERR_UNSUPPORTED.  The keys are rebuilt with exact bf16 products and
  * fp32 sums; rotation, scores, softmax and accumulation run in fp32.
- * Workspace, plan, ownership, seq_lens handling, errors and determinism are
- * those of lrattn_decode.
+ * Plan and workspace are this call's own: one wave streams one sequence's
+ * partition (four sequences per workgroup share the rotation table's rows),
+ * so by default T is split into more partitions than lrattn_decode uses;
+ * lrattn_rebuild_plan reports them (num_splits > 0 is used as given) and the
+ * workspace must hold lrattn_rebuild_workspace_size bytes.  Ownership,
+ * seq_lens handling, errors and determinism are those of lrattn_decode.
  */
+int lrattn_rebuild_plan(const lrattn_params* p, int32_t* num_splits, int32_t* split_tokens);
+int lrattn_rebuild_workspace_size(const lrattn_params* p, size_t* bytes);
 int lrattn_rebuild_decode(const lrattn_params* p,
                           const void* q,
                           const void* L_K,

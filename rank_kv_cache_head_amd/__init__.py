@@ -87,6 +87,9 @@ def lib() -> ctypes.CDLL:
                                           ctypes.c_size_t, _VP]
         L.lrattn_rebuild_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                             ctypes.c_size_t, _VP]
+        L.lrattn_rebuild_plan.argtypes = [_PP, ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.POINTER(ctypes.c_int32)]
+        L.lrattn_rebuild_workspace_size.argtypes = [_PP, ctypes.POINTER(ctypes.c_size_t)]
         L.lrattn_append.argtypes = [ctypes.POINTER(AppendParams), _VP, _VP, _VP, _VP, _VP, _VP,
                                     _VP, _VP, ctypes.c_size_t, _VP]
         L.lrattn_append_workspace_size.argtypes = [ctypes.POINTER(AppendParams),
@@ -106,6 +109,7 @@ def lib() -> ctypes.CDLL:
         L.lrattn_probe_copy.argtypes = [_VP, _VP, ctypes.c_size_t, _VP]
         for fn in ("lrattn_plan", "lrattn_workspace_size", "lrattn_decode", "lrattn_partition",
                    "lrattn_combine", "lrattn_dense_decode", "lrattn_rebuild_decode",
+                   "lrattn_rebuild_plan", "lrattn_rebuild_workspace_size",
                    "lrattn_append", "lrattn_append_workspace_size",
                    "lrattn_shared_decode", "lrattn_shared_workspace_size",
                    "lrattn_probe_read",
@@ -204,9 +208,9 @@ def workspace_size(p: Params) -> int:
     return b.value
 
 
-def _workspace(p: Params, workspace, device):
+def _workspace(p: Params, workspace, device, need=None):
     import torch
-    need = workspace_size(p)
+    need = workspace_size(p) if need is None else need
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
     return workspace, workspace.numel() * workspace.element_size()
@@ -283,6 +287,22 @@ def _check_rope(p: Params, rope):
         raise ValueError("rope must be float32 [T, d]")
 
 
+def rebuild_plan(p: Params) -> Tuple[int, int]:
+    """(partitions, tokens per partition) of lrattn_rebuild_decode."""
+    n = ctypes.c_int32()
+    s = ctypes.c_int32()
+    _check(lib().lrattn_rebuild_plan(ctypes.byref(p), ctypes.byref(n), ctypes.byref(s)),
+           "lrattn_rebuild_plan")
+    return n.value, s.value
+
+
+def rebuild_workspace_size(p: Params) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().lrattn_rebuild_workspace_size(ctypes.byref(p), ctypes.byref(b)),
+           "lrattn_rebuild_workspace_size")
+    return b.value
+
+
 def rebuild_decode(q, L_K, L_V, B_K, B_V, seq_lens, rope=None, *, out=None, workspace=None,
                    softmax_scale=None, num_splits: int = 0, out_dtype=None, stream=None):
     """lrattn_rebuild_decode: keys rebuilt on chip, rotated by position when
@@ -296,7 +316,7 @@ def rebuild_decode(q, L_K, L_V, B_K, B_V, seq_lens, rope=None, *, out=None, work
         out = torch.empty((p.batch, p.num_q_heads, p.head_dim),
                           dtype=torch.float32 if p.out_dtype == F32 else torch.bfloat16,
                           device=q.device)
-    ws, ws_bytes = _workspace(p, workspace, q.device)
+    ws, ws_bytes = _workspace(p, workspace, q.device, rebuild_workspace_size(p))
     st = lib().lrattn_rebuild_decode(ctypes.byref(p), _ptr(q), _ptr(L_K), _ptr(L_V), _ptr(B_K),
                                      _ptr(B_V), _ptr(rope), _ptr(seq_lens), _ptr(out), _ptr(ws),
                                      ws_bytes, _stream(stream))
@@ -524,9 +544,9 @@ class RebuildDecoder:
             out = torch.empty((p.batch, p.num_q_heads, p.head_dim),
                               dtype=torch.float32 if p.out_dtype == F32 else torch.bfloat16,
                               device=q.device)
-        ws, ws_bytes = _workspace(p, workspace, q.device)
+        ws, ws_bytes = _workspace(p, workspace, q.device, rebuild_workspace_size(p))
         self.params, self.out, self.workspace = p, out, ws
-        self.plan = plan(p)
+        self.plan = rebuild_plan(p)
         self._keep = (q, L_K, L_V, B_K, B_V, seq_lens, rope)
         self._fn = lib().lrattn_rebuild_decode
         self._args = (ctypes.byref(p), _ptr(q), _ptr(L_K), _ptr(L_V), _ptr(B_K), _ptr(B_V),

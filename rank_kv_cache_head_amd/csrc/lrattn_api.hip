@@ -290,17 +290,64 @@ int lrattn_dense_decode(const lrattn_params* p, const void* q, const void* K, co
   return LRATTN_OK;
 }
 
+namespace {
+// Rebuilt keys: each wave owns one sequence's partition, four sequences per
+// workgroup, so the default plan splits T into enough partitions for the grid
+// (partitions x kv-heads x quads of sequences) to give every CU about three
+// workgroups; a partition is a whole number of 32-token steps, at least
+// kRebuildMinTokens.  An explicit num_splits is used as given.
+constexpr int64_t kRebuildBlocks = 768;
+constexpr int64_t kRebuildMinTokens = 128;
+
+int rebuild_plan(const lrattn_params* p, Plan* pl) {
+  int st = check_params(p, pl);
+  if (st != LRATTN_OK) return st;
+  if (p->q_dtype != LRATTN_BF16 || p->latent_dtype != LRATTN_BF16 ||
+      p->factor_dtype != LRATTN_BF16 ||
+      !lrattn::rebuild_supported(p->head_dim, p->rank, group_of(p)))
+    return LRATTN_ERR_UNSUPPORTED;
+  if (p->num_splits > 0) return LRATTN_OK;
+  const int64_t T = p->max_seq_len;
+  const int64_t cells = (int64_t)p->num_kv_heads * ((p->batch + 3) / 4);
+  const int64_t want = (kRebuildBlocks + cells - 1) / cells;
+  int64_t S = (T + want - 1) / want;
+  S = (S + 31) / 32 * 32;
+  if (S < kRebuildMinTokens) S = kRebuildMinTokens;
+  if (S > T) S = T;
+  if (S * p->rank * 2 >= (int64_t(1) << 30)) return LRATTN_ERR_UNSUPPORTED;
+  pl->S = (int32_t)S;
+  pl->P = (int32_t)((T + S - 1) / S);
+  if (checked_mul({p->batch, p->num_q_heads, pl->P, p->rank + kRecPad, 4}) < 0)
+    return LRATTN_ERR_SHAPE;
+  return LRATTN_OK;
+}
+}  // namespace
+
+int lrattn_rebuild_plan(const lrattn_params* p, int32_t* num_splits, int32_t* split_tokens) {
+  Plan pl;
+  const int st = rebuild_plan(p, &pl);
+  if (st != LRATTN_OK) return st;
+  if (num_splits) *num_splits = pl.P;
+  if (split_tokens) *split_tokens = pl.S;
+  return LRATTN_OK;
+}
+
+int lrattn_rebuild_workspace_size(const lrattn_params* p, size_t* bytes) {
+  if (!bytes) return LRATTN_ERR_NULL;
+  Plan pl;
+  const int st = rebuild_plan(p, &pl);
+  if (st != LRATTN_OK) return st;
+  *bytes = workspace_bytes_for(p, pl);
+  return LRATTN_OK;
+}
+
 int lrattn_rebuild_decode(const lrattn_params* p, const void* q, const void* L_K,
                           const void* L_V, const void* B_K, const void* B_V, const float* rope,
                           const int32_t* seq_lens, void* out, void* workspace,
                           size_t workspace_bytes, lrattn_stream stream) {
   Plan pl;
-  int st = check_params(p, &pl);
-  if (st == LRATTN_OK &&
-      (p->q_dtype != LRATTN_BF16 || p->latent_dtype != LRATTN_BF16 ||
-       p->factor_dtype != LRATTN_BF16 ||
-       !lrattn::rebuild_supported(p->head_dim, p->rank, group_of(p)) ||
-       (rope && (int64_t)p->max_seq_len * p->head_dim * 4 >= (int64_t(1) << 31))))
+  int st = rebuild_plan(p, &pl);
+  if (st == LRATTN_OK && rope && (int64_t)p->max_seq_len * p->head_dim * 4 >= (int64_t(1) << 31))
     st = LRATTN_ERR_UNSUPPORTED;
   if (st == LRATTN_OK) st = check_partition_ptrs(p, q, L_K, L_V, B_K, nullptr, seq_lens);
   if (st == LRATTN_OK) st = check_combine_ptrs(B_V, seq_lens, out);

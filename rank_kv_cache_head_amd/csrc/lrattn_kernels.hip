@@ -1283,8 +1283,8 @@ void partition_mfma_kernel(PartitionArgs a) {
 // by position before scoring (a position-dependent rotation is what the
 // absorbed form q . B_K^T cannot carry), and scores them against the query
 // rotated by its own position.  Values are not rotated, so they stay in the
-// latent space: the value side, the records and the combine are those of the
-// absorbed path.  bf16 q, latents and factors; d in {64, 128}; r in {32, 64}.
+// latent space: the value side and the records are those of the absorbed
+// path.  bf16 q, latents and factors; d in {64, 128}; r in {32, 64}.
 //
 //   rebuild  K^T (d x 16) = B_K^T (d x r) . L_K^T (r x 16): per 16-row block n
 //            of d and 32-row step c of r one v_mfma_f32_16x16x32_bf16.
@@ -1295,110 +1295,144 @@ void partition_mfma_kernel(PartitionArgs a) {
 //            products, fp32 sums.
 //   rotate   pairs (j, j + d/2) are blocks n and n + d/32 of one lane and
 //            register; the cosines and sines of the token's position come
-//            from the caller's table row (loaded with the tile's latents).
-//   score    S (16 x 16) = Q' . K'^T in fp32 on the matrix cores
-//            (v_mfma_f32_16x16x4_f32, K = 4 per instruction), q' = qscale *
-//            rotate(q, seq_len - 1): for block n and register i, lane l's
-//            rebuilt value (d = 16 n + 4 (l / 16) + i of token l % 16) is the
-//            B operand for k = l / 16 as it stands, and the query operand
-//            holds q'[head][16 n + 4 (l / 16) + i].  No conversion, fp32
-//            products and sums.  The result layout is that of
-//            partition_mfma_kernel, whose softmax and value code follow.
+//            from the caller's table.
+//   score    S = Q' . K'^T in fp32 on the matrix cores with the 16-block
+//            4 x 4 instruction (v_mfma_f32_4x4x1_16b_f32), q' = qscale *
+//            rotate(q, seq_len - 1).  Block l / 4 pairs a quad of 4 heads
+//            (rows, from the query operand) with the 4 tokens of lanes
+//            4 (l / 4) .. + 3 (columns); lane l's rebuilt value for block n,
+//            register i is its column's entry as it stands.  The 16 x 16
+//            instruction would spend 12 of its 16 rows on repeats when 4 heads
+//            share a key; the 4 x 4 one has the same rate per product and no
+//            repeats.  Each block sums one quarter of d; two lane swaps add
+//            the quarters.  No conversion, fp32 products and sums.  The result
+//            layout is that of partition_mfma_kernel, whose softmax and value
+//            code follow.
+//
+// Work split: the rotation table is the same for every sequence and head,
+// and per token it is larger than the latents (512 bytes for d = 128 against
+// 2 r bf16 values, twice).  So the four waves of a workgroup take four
+// sequences (b = 4 z + wave) of one kv-head over the same positions: each
+// tile's table rows are loaded once, by all four waves together, into LDS
+// (two buffers, one barrier per tile), and each wave owns its sequence's
+// partition and writes its own records.  The B_K^T fragments serve all four.
 
 template <int R, int D>
 struct RGeo {
   static constexpr int kNB = D / 16;   // 16-row blocks of d
   static constexpr int kKC = R / 32;   // 32-row steps of r
-  static constexpr int kKS = D / 32;   // 32-wide score steps of d
   static constexpr int kHalf = D / 32; // blocks per half of d (rotation pairs)
+  static constexpr int kRopeEntries = D / 16 * 64;  // 16-byte table pieces per tile
 };
 
-// One tile of keys' table values: cosines and sines of d = 16 n + 4 (l / 16)
-// + i (i < 4) for the blocks n of the first half of d.
-template <int D, bool kRot>
-struct RopeTile {
-  u32x4 c[kRot ? D / 32 : 1];
-  u32x4 s[kRot ? D / 32 : 1];
+// No rotation.
+struct RopeNone {};
+
+// A tile's table values in LDS, [pair n][cos, sin][lane]: lane l's cosines
+// (sines) of d = 16 n + 4 (l / 16) + i, i < 4, for its token l % 16.
+struct RopeLds {
+  const u32x4* base;
+  int lane;
+  __device__ u32x4 cos(int n) const { return base[(2 * n) * 64 + lane]; }
+  __device__ u32x4 sin(int n) const { return base[(2 * n + 1) * 64 + lane]; }
 };
 
-template <int R, int G, int D, bool kRot>
-struct RStep {
-  MStep<R, G, 1> lat;
-  RopeTile<D, kRot> rope;
-};
-
-template <int R, int G, int D, bool kRot>
-__device__ __forceinline__ void load_rstep(RStep<R, G, D, kRot>& st, int cb, uint32_t koff,
-                                           uint32_t voff, __amdgpu_buffer_rsrc_t rk,
-                                           __amdgpu_buffer_rsrc_t rv, __amdgpu_buffer_rsrc_t rr,
-                                           uint32_t rope_off) {
-  load_mstep<R, G, 1>(st.lat, cb, koff, voff, rk, rv);
-  if constexpr (kRot) {
-    // table row of this lane's token (position t0 + cb + l % 16); rows past
-    // the table load zeros (masked tokens)
-    const uint32_t row = rope_off + (uint32_t)cb * D * 4u;
-#pragma unroll
-    for (int n = 0; n < D / 32; ++n) {
-      st.rope.c[n] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(row + 64u * n), 0, 0);
-      st.rope.s[n] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(row + 64u * n + 2u * D), 0, 0);
-    }
-  }
+// Adds x over the lanes l, l ^ 16, l ^ 32 and l ^ 48 in the order
+// (x_a + x_b) + (x_c + x_d), with a, b and c, d the pairs l ^ 16 joins; every
+// lane of the four gets the same bits.
+__device__ __forceinline__ float sum_quarters(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-template <int R, int G, int D, bool kRot, bool kMask>
-__device__ __forceinline__ void rebuild_scores(const RStep<R, G, D, kRot>& st, int cb, int ntok,
-                                               int lane, const u32x4* frag,
-                                               const float (&qf)[D / 16][4], float (&s)[1][4]) {
+// head quads of the score instruction: heads 0..3, and 4..7 for G = 8
+template <int G>
+struct RQuads {
+  static constexpr int kQ = G == 8 ? 2 : 1;
+};
+
+template <int R, int G, int D, class Rope>
+__device__ __forceinline__ void rebuild_scores(const MStep<R, G, 1>& lat, const Rope& rope,
+                                               int cb, int ntok, int lane, const u32x4* frag,
+                                               const float (&qf)[RQuads<G>::kQ][D / 16][4],
+                                               float (&s)[1][4]) {
   using Rg = RGeo<R, D>;
-  constexpr int NB = Rg::kNB, KC = Rg::kKC;
-  // rebuild the tile's keys, transposed
-  f32x4 kd[NB];
+  constexpr int KC = Rg::kKC, NH = Rg::kHalf, QH = RQuads<G>::kQ;
+  constexpr bool kRot = !std::is_same<Rope, RopeNone>::value;
+  // Per rotary pair of 16-row blocks (n, n + d/32): rebuild both blocks of
+  // the tile's keys, transposed, rotate them, and add them into the scores.
+  //
+  // Scores on v_mfma_f32_4x4x1_16b_f32: block l / 4 is token quad (l % 16) / 4
+  // of d-quarter l / 16; its rows are the 4 heads of a quad, its columns the
+  // quad's tokens, and each instruction adds one d of the quarter
+  // (d = 16 n + 4 (l / 16) + i, lane l's own rebuilt value); then the four
+  // quarters are added across lanes.
+  f32x4 sd[QH];
 #pragma unroll
-  for (int n = 0; n < NB; ++n) {
-    kd[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int qh = 0; qh < QH; ++qh) sd[qh] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const u32x4 bk = frag[(n * KC + c) * 64 + lane];
-      const u32x4 lk = {st.lat.k[0][c][0], st.lat.k[0][c][1], st.lat.k[0][c][2], st.lat.k[0][c][3]};
-      kd[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bk),
-                                                      __builtin_bit_cast(bf16x8, lk), kd[n], 0, 0, 0);
+  for (int n = 0; n < NH; ++n) {
+    f32x4 kd[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int nb = n + hf * NH;
+      kd[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const u32x4 bk = frag[(nb * KC + c) * 64 + lane];
+        const u32x4 lk = {lat.k[0][c][0], lat.k[0][c][1], lat.k[0][c][2], lat.k[0][c][3]};
+        kd[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bk),
+                                                         __builtin_bit_cast(bf16x8, lk), kd[hf], 0, 0, 0);
+      }
     }
-  }
-  if constexpr (kRot) {
-#pragma unroll
-    for (int n = 0; n < D / 32; ++n) {
+    if constexpr (kRot) {
+      const u32x4 cw = rope.cos(n), sw = rope.sin(n);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float c = __uint_as_float(st.rope.c[n][i]), sn = __uint_as_float(st.rope.s[n][i]);
-        const float x = kd[n][i], y = kd[n + D / 32][i];
-        kd[n][i] = x * c - y * sn;
-        kd[n + D / 32][i] = x * sn + y * c;
+        const float c = __uint_as_float(cw[i]), sn = __uint_as_float(sw[i]);
+        const float x = kd[0][i], y = kd[1][i];
+        kd[0][i] = x * c - y * sn;
+        kd[1][i] = x * sn + y * c;
+      }
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int qh = 0; qh < QH; ++qh)
+          sd[qh] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[qh][n + hf * NH][i], kd[hf][i], sd[qh], 0, 0, 0);
       }
     }
   }
-  // scores: fp32 products, 4 per instruction
-  f32x4 d = {0.f, 0.f, 0.f, 0.f};
+  float sq[QH][4];
 #pragma unroll
-  for (int n = 0; n < NB; ++n) {
+  for (int qh = 0; qh < QH; ++qh) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      d = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[n][i], kd[n][i], d, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) sq[qh][i] = sum_quarters(sd[qh][i]);
   }
+  // lane l keeps heads 4 (l / 16 % 2) + i for G = 8 (the score layout of
+  // partition_mfma_kernel), heads i % G otherwise
+  const bool hi_half = G == 8 && ((lane >> 4) & 1);
   const int tok = lane & 15;
+  const bool masked = cb + tok >= ntok;  // a select, not a branch
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    s[0][i] = d[i];
-    if constexpr (kMask) {
-      if (cb + tok >= ntok) s[0][i] = -INFINITY;
-    }
+    const float x = (QH == 2 && hi_half) ? sq[QH - 1][i] : sq[0][i];
+    s[0][i] = masked ? -INFINITY : x;
   }
 }
 
 template <int R, int G, int D>
 struct RPartLds {
-  PartLds<R, G> base;          // q holds q' = qscale * rotate(q) [G][D]
+  union {
+    uint16_t stage[R * D];                         // B_K[g] as stored, for the gather
+    u32x4 rope[2][RGeo<R, D>::kRopeEntries / 64][64];  // table tiles, two buffers
+  };
   u32x4 frag[D * R / 8];       // B_K^T fragments [n][c][lane]
-  uint16_t stage[R * D];       // B_K[g] as stored, for the fragment gather
+  float q[kWaves][G * D];      // q' = qscale * rotate(q, seq_len - 1) of each wave's sequence
   float w[kWaves * 16 * G];
 };
 
@@ -1406,34 +1440,51 @@ template <int R, int G, int D, bool kRot>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G == 8 ? 2 : 3)))
 void partition_rebuild_kernel(PartitionArgs a) {
   using Mg = MGeo<R, G, 1>;
-  constexpr int LPR = Mg::kLPR, KC = R / 32;
-  constexpr int CH = 16;  // tokens per wave per step
+  using Rg = RGeo<R, D>;
+  constexpr int LPR = Mg::kLPR, KC = R / 32, CH = 16;
+  constexpr int EPT = Rg::kRopeEntries / kThreads;  // table pieces per thread and tile
+  static_assert(Rg::kRopeEntries % kThreads == 0, "table tile split");
 
-  // head group hg (its G query heads) reads latent stream g
-  int p, hg, b;
-  if (!tile_of(a, p, hg, b)) return;
+  // workgroup: kv-head group hg, partition p, sequences 4 z .. 4 z + 3
+  const int p = blockIdx.x, hg = blockIdx.y, z = blockIdx.z;
   const int g = hg * G / a.hps;
-  const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = p * a.S;
-  const int t1 = min(t0 + a.S, len);
-  if (t0 >= t1) return;  // partition past the sequence: nothing to write
-  const int ntok = t1 - t0;
+  int nmax = 0, len = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int bw = kWaves * z + w;
+    const int lw = bw < a.B ? min(max(a.seq_lens[bw], 0), a.T) : 0;
+    nmax = max(nmax, min(t0 + a.S, lw) - t0);
+    len = w == wave ? lw : len;
+  }
+  if (nmax <= 0) return;  // every sequence of the quad ends before this partition
+  len = __builtin_amdgcn_readfirstlane(len);
+  const int b = kWaves * z + wave;
+  const int bs = min(b, a.B - 1);                  // in range for the address arithmetic
+  const int ntok = max(min(t0 + a.S, len) - t0, 0);  // 0: the wave adds and writes nothing
 
   __shared__ RPartLds<R, G, D> lds;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = lane / LPR, cc = lane % LPR;
 
-  const size_t row0 = ((size_t)b * a.Hkv + g) * (size_t)a.T + (size_t)t0;
+  const size_t row0 = ((size_t)bs * a.Hkv + g) * (size_t)a.T + (size_t)t0;
   const uint32_t nbytes = (uint32_t)ntok * Mg::kRowBytes;
   const auto rk = make_rsrc(static_cast<const char*>(a.LK) + row0 * Mg::kRowBytes, nbytes);
   const auto rv = make_rsrc(static_cast<const char*>(a.LV) + row0 * Mg::kRowBytes, nbytes);
   const uint32_t koff = (uint32_t)((lane & 15) * Mg::kRowBytes + (lane >> 4) * 16);
   const uint32_t voff = (uint32_t)(slot * Mg::kRowBytes + cc * 16);
   const auto rr = kRot ? make_rsrc(a.rope, (uint32_t)a.T * D * 4u) : make_rsrc(nullptr, 0u);
-  // this lane's table offset: row t0 + l % 16, columns 16 n + 4 (l / 16)
-  const uint32_t rope_off = (uint32_t)((t0 + (lane & 15)) * D + 4 * (lane >> 4)) * 4u;
+  // this thread's table pieces e = tid + k * kThreads of a tile: pair n,
+  // cos|sin part cs, reader lane l -> row t0 + cb + l % 16, column
+  // cs * d/2 + 16 n + 4 (l / 16); rows past the table load zeros
+  uint32_t roff[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = tid + k * kThreads, j = e >> 6, l = e & 63;
+    roff[k] = (uint32_t)(((t0 + (l & 15)) * D + (j & 1) * (D / 2) + 16 * (j >> 1) + 4 * (l >> 4)) * 4);
+  }
 
-  // ---- prologue: B_K[g] and q, both bf16, with every load issued at once
+  // ---- prologue: B_K[g] (all threads) and q' of this wave's sequence
   {
     const auto rf = make_rsrc(static_cast<const uint16_t*>(a.BK) + (size_t)g * R * D,
                               (uint32_t)(R * D) * 2u);
@@ -1442,28 +1493,23 @@ void partition_rebuild_kernel(PartitionArgs a) {
 #pragma unroll
     for (int k = 0; k < kF; ++k)
       fw[k] = __builtin_amdgcn_raw_buffer_load_b128(rf, (int)((tid + k * kThreads) * 16u), 0, 0);
-    const size_t q0 = ((size_t)b * a.Hq + (size_t)g * G) * D;
+    const size_t q0 = ((size_t)bs * a.Hq + (size_t)hg * G) * D;
     const auto rq = make_rsrc(static_cast<const uint16_t*>(a.q) + q0, (uint32_t)(G * D) * 2u);
-    // q pairs (j, j + D/2) of head h: thread handles pair index tid (and + 256)
-    constexpr int kPairs = G * D / 2, kPP = (kPairs + kThreads - 1) / kThreads;
+    // pairs (j, j + D/2) of head h: lane handles pair index lane + 64 k
+    constexpr int kPairs = G * D / 2, kPP = (kPairs + 63) / 64;
     uint32_t qlo[kPP], qhi[kPP];
+    float rc[kPP], rs[kPP];
 #pragma unroll
     for (int k = 0; k < kPP; ++k) {
-      const int pi = tid + k * kThreads;
+      const int pi = lane + 64 * k;
       const int h = pi / (D / 2), j = pi - h * (D / 2);
       const bool ok = pi < kPairs;
       qlo[k] = __builtin_amdgcn_raw_buffer_load_b32(rq, (int)(ok ? (h * D + j) * 2u & ~3u : kOffNone), 0, 0);
       qhi[k] = __builtin_amdgcn_raw_buffer_load_b32(rq, (int)(ok ? (h * D + j + D / 2) * 2u & ~3u : kOffNone), 0, 0);
-    }
-    float rc[kPP], rs[kPP];
-#pragma unroll
-    for (int k = 0; k < kPP; ++k) {
       rc[k] = 1.f;
       rs[k] = 0.f;
       if constexpr (kRot) {
-        const int pi = tid + k * kThreads;
-        const int j = pi % (D / 2);
-        const uint32_t row = (uint32_t)(len - 1) * D * 4u;
+        const uint32_t row = (uint32_t)max(len - 1, 0) * D * 4u;
         rc[k] = bload4f(rr, row + 4u * j);
         rs[k] = bload4f(rr, row + 4u * (D / 2 + j));
       }
@@ -1471,15 +1517,17 @@ void partition_rebuild_kernel(PartitionArgs a) {
 #pragma unroll
     for (int k = 0; k < kF; ++k)
       *reinterpret_cast<u32x4*>(&lds.stage[(tid + k * kThreads) * 8]) = fw[k];
+    float* qw = lds.q[wave];
 #pragma unroll
     for (int k = 0; k < kPP; ++k) {
-      const int pi = tid + k * kThreads;
-      const int h = pi / (D / 2), j = pi - h * (D / 2);
-      const float x = (j & 1) ? bf16_hi(qlo[k]) : bf16_lo(qlo[k]);
-      const float y = (j & 1) ? bf16_hi(qhi[k]) : bf16_lo(qhi[k]);
-      float* dst = pi < kPairs ? lds.base.q + h * D + j : lds.base.q + G * kMaxHeadDim;
-      dst[0] = (x * rc[k] - y * rs[k]) * a.qscale;
-      dst[pi < kPairs ? D / 2 : 4] = (x * rs[k] + y * rc[k]) * a.qscale;
+      const int pi = lane + 64 * k;
+      if (pi < kPairs) {
+        const int h = pi / (D / 2), j = pi - h * (D / 2);
+        const float x = (j & 1) ? bf16_hi(qlo[k]) : bf16_lo(qlo[k]);
+        const float y = (j & 1) ? bf16_hi(qhi[k]) : bf16_lo(qhi[k]);
+        qw[h * D + j] = (x * rc[k] - y * rs[k]) * a.qscale;
+        qw[h * D + j + D / 2] = (x * rs[k] + y * rc[k]) * a.qscale;
+      }
     }
   }
   __syncthreads();
@@ -1495,21 +1543,47 @@ void partition_rebuild_kernel(PartitionArgs a) {
              ((uint32_t)lds.stage[(k0 + 2 * j + 1) * D + col] << 16);
     lds.frag[f] = w;
   }
-  // query operand: row lane % 16 is head (lane % 16) % G; block n,
-  // register i supplies d = 16 n + 4 (l / 16) + i
-  float qf[D / 16][4];
-  {
-    const float* qrow = lds.base.q + ((lane & 15) % G) * D + 4 * (lane >> 4);
+  // query operand of the score instruction: lane l is row l % 4 of its block,
+  // head (l % 4) % G of quad qh; instruction (n, i) takes d = 16 n + 4 (l / 16) + i
+  float qf[RQuads<G>::kQ][D / 16][4];
+#pragma unroll
+  for (int qh = 0; qh < RQuads<G>::kQ; ++qh) {
+    const float* qrow = lds.q[wave] + (4 * qh + (lane & 3) % G) * D + 4 * (lane >> 4);
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qf[n][i] = qrow[16 * n + i];
+      for (int i = 0; i < 4; ++i) qf[qh][n][i] = qrow[16 * n + i];
     }
   }
-  __syncthreads();
+  __syncthreads();  // the stage is free: its space holds the table tiles
 
-  RStep<R, G, D, kRot> cur;
-  load_rstep(cur, wave * CH, koff, voff, rk, rv, rr, rope_off);
+  // ---- the tiles.  Two tiles of latents in flight per wave: the loads of
+  // tile k + 2 are issued as soon as tile k is done, so each tile's latency is
+  // covered by a whole tile of work.  The table tile k + 1 is loaded into
+  // registers during tile k and written to the other LDS buffer at its end.
+  // The loop runs to the quad's longest partition (every wave takes part in
+  // every barrier); a wave past its own end, or an odd last tile, sees loads
+  // that return zeros (outside its buffer's range) and scores masked to -inf,
+  // and adds nothing.  The scheduling barriers keep the issue order, which
+  // the waits on in-order load returns rely on.
+  u32x4 rp[EPT];
+  if constexpr (kRot) {
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) rp[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)roff[k], 0, 0);
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) (&lds.rope[0][0][0])[tid + k * kThreads] = rp[k];
+  }
+  MStep<R, G, 1> l0, l1;
+  load_mstep<R, G, 1>(l0, 0, koff, voff, rk, rv);
+  if constexpr (kRot) {
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+      rp[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(roff[k] + CH * D * 4u), 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  load_mstep<R, G, 1>(l1, CH, koff, voff, rk, rv);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kRot) __syncthreads();
 
   float mm[4], ll[4], acc[G][8];
 #pragma unroll
@@ -1523,16 +1597,66 @@ void partition_rebuild_kernel(PartitionArgs a) {
     ll[i] = 0.f;
   }
   float* wl = lds.w + wave * CH * G;
-  for (int cb = wave * CH; cb < ntok; cb += kWaves * CH) {
+  // one tile: scores, softmax and values; then the next table tile into the
+  // other buffer, the loads two tiles ahead, and the barrier
+  auto tile = [&](MStep<R, G, 1>& lt, int cb, int buf) {
     float s[1][4];
-    if (cb + CH <= ntok)
-      rebuild_scores<R, G, D, kRot, false>(cur, cb, ntok, lane, lds.frag, qf, s);
+    if constexpr (kRot)
+      rebuild_scores<R, G, D>(lt, RopeLds{&lds.rope[buf][0][0], lane}, cb, ntok, lane, lds.frag, qf, s);
     else
-      rebuild_scores<R, G, D, kRot, true>(cur, cb, ntok, lane, lds.frag, qf, s);
-    softmax_values<R, G, 1>(s, cur.lat, lane, mm, ll, acc, wl);
-    load_rstep(cur, cb + kWaves * CH, koff, voff, rk, rv, rr, rope_off);
+      rebuild_scores<R, G, D>(lt, RopeNone{}, cb, ntok, lane, lds.frag, qf, s);
+    softmax_values<R, G, 1>(s, lt, lane, mm, ll, acc, wl);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kRot) {
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) (&lds.rope[buf ^ 1][0][0])[tid + k * kThreads] = rp[k];
+#pragma unroll
+      for (int k = 0; k < EPT; ++k)
+        rp[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(roff[k] + (uint32_t)(cb + 2 * CH) * D * 4u), 0, 0);
+    }
+    load_mstep<R, G, 1>(lt, cb + 2 * CH, koff, voff, rk, rv);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kRot) __syncthreads();
+  };
+  for (int cb = 0; cb < nmax; cb += 2 * CH) {
+    tile(l0, cb, 0);
+    tile(l1, cb + CH, 1);
   }
-  mfma_epilogue<R, G, 1>(a, b, hg, p, mm, ll, acc, lds.base);
+
+  // ---- this wave's records: (acc, m, l) of its G heads
+  float m[G], l[G];
+#pragma unroll
+  for (int i = 0; i < Mg::kHL; ++i) {
+    const float x = group_sum<16>(ll[i]);
+    l[i] = readlane_f(x, 0);
+    m[i] = readlane_f(mm[i], 0);
+    if constexpr (G == 8) {
+      l[4 + i] = readlane_f(x, 16);
+      m[4 + i] = readlane_f(mm[i], 16);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
+    }
+  }
+  if (ntok > 0) {
+    float* const rec0 = a.ws + ((size_t)b * a.Hq + (size_t)hg * G) * (size_t)a.P * (R + kRecPad);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float* rec = rec0 + ((size_t)h * a.P + p) * (R + kRecPad);
+      if (slot == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rec[cc * 8 + e] = acc[h][e];
+      }
+      if (lane == 0) {
+        rec[R] = m[h];
+        rec[R + 1] = l[h];
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------ combine
@@ -1813,7 +1937,8 @@ hipError_t launch_pr(int rank, int group, const PartitionArgs& a, hipStream_t s)
 
 template <int R, int D>
 hipError_t launch_rg(int group, bool rot, const PartitionArgs& a, hipStream_t s) {
-  const dim3 grid = a.xcd_group ? dim3(8 * a.HG * ((a.P * a.B + 7) / 8)) : dim3(a.P, a.HG, a.B);
+  // partitions x kv-head groups x quads of sequences (one wave per sequence)
+  const dim3 grid(a.P, a.HG, (a.B + kWaves - 1) / kWaves);
   const dim3 block(kThreads);
   switch (group) {
     case 1:

@@ -207,8 +207,28 @@ def test_rebuild_decode_validates_on_host():
     assert call(p, rope=MISALIGNED) == -5
     assert call(p, q=MISALIGNED) == -5
     assert call(p, ws=None) == -6
-    assert call(p, rope=ALIGNED, ws_bytes=lr.workspace_size(p) - 1) == -6
+    assert call(p, rope=ALIGNED, ws_bytes=lr.rebuild_workspace_size(p) - 1) == -6
     assert call(params(max_seq_len=1 << 22), rope=ALIGNED) == -4   # T * d * 4 >= 2^31
+
+
+def test_rebuild_plan():
+    """One wave per sequence partition, four sequences per workgroup: the
+    default plan gives about 768 workgroups of whole 32-token steps."""
+    for kw, want in [(dict(batch=16, num_q_heads=32, num_kv_heads=8, rank=64, max_seq_len=16384),
+                      (24, 704)),                 # 8 kv-heads x 4 quads x 24 partitions
+                     (dict(batch=8, num_q_heads=32, num_kv_heads=32, rank=32, max_seq_len=4096),
+                      (12, 352)),                 # 32 x 2 x 12
+                     (dict(batch=5, num_q_heads=8, num_kv_heads=2, rank=64, max_seq_len=700),
+                      (6, 128)),                  # floor of 128 tokens
+                     (dict(batch=5, num_q_heads=8, num_kv_heads=2, rank=64, max_seq_len=700,
+                           num_splits=3), (3, 234))]:   # explicit splits as given
+        p = params(**kw)
+        P, S = lr.rebuild_plan(p)
+        assert (P, S) == want, (kw, P, S)
+        rec = p.batch * p.num_q_heads * P * (p.rank + 4) * 4   # records, rounded to 256 bytes
+        assert lr.rebuild_workspace_size(p) == (rec + 255) // 256 * 256
+    with pytest.raises(lr.LrattnError):
+        lr.rebuild_plan(params(latent_dtype=lr.I8, rank=32))
 
 
 def test_append_validates_on_host():
