@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="gqa_vlm",
                     choices=["tiny", "llm7b", "gqa_vlm", "int8", "ragged"])
-    ap.add_argument("--num-splits", type=int, default=0, help="0 = library heuristic")
+    ap.add_argument("--num-splits", type=int, default=0,
+                    help="0 = the workload's own (ragged: 256), else the library heuristic")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -169,6 +170,8 @@ def main():
     import rank_kv_cache_head_amd as lr
 
     lr.lib()  # fail loudly if the library is missing
+    if args.num_splits == 0:
+        args.num_splits = workloads.SPLITS.get(args.config, 0)
     t_gen = time.perf_counter()
     w = workloads.make(args.config)
     ab = w.algorithmic_bytes()

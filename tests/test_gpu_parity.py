@@ -56,7 +56,7 @@ def test_full_size(name):
     w = workloads.make(name)
     say(f"full {name}: decode B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
         f"T={w.max_seq_len} r={w.rank}")
-    got = run_decode(w).cpu().numpy()
+    got = run_decode(w, num_splits=workloads.SPLITS.get(name, 0)).cpu().numpy()
     assert np.isfinite(got).all()
     if name in ("tiny", "llm7b"):
         ref = _full_oracle(w)

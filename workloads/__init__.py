@@ -83,6 +83,12 @@ SPECS: Dict[str, dict] = {
 }
 CONFIG_ORDER = ["tiny", "llm7b", "gqa_vlm", "int8", "ragged"]
 
+# Partitions per (sequence, kv-head) a workload names for its launch: the
+# ragged long-context workload asks for split-K across at least 256
+# partitions per head (over T = 131072, 512 tokens each).  Others: 0, the
+# library's default plan.
+SPLITS = {"ragged": 256}
+
 _STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.float16, "i8": np.int8}
 _ESIZE = {"f32": 4, "bf16": 2, "f16": 2, "i8": 1}
 
