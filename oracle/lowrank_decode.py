@@ -42,7 +42,8 @@ from typing import Iterable, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = ["as_float64", "dequantize", "rebuild", "attend", "decode",
-           "decode_rows", "decode_absorbed", "rotate", "decode_rotated", "decode_shared"]
+           "decode_rows", "decode_absorbed", "rotate", "decode_rotated", "decode_shared",
+           "decode_modal"]
 
 
 def as_float64(a: np.ndarray, tag: str) -> np.ndarray:
@@ -263,5 +264,45 @@ def decode_shared(q, L_K, L_V, B_K, B_V, seq_lens, scales=None,
             sV = scales[1, b, s_, :n] if scales is not None else None
             K = rebuild(dequantize(L_K[b, s_, :n], sK), B_K[h])
             V = rebuild(dequantize(L_V[b, s_, :n], sV), B_V[h])
+            out[b, h] = attend(q[b, h], K, V, alpha)
+    return out
+
+
+def decode_modal(q, L_K, L_V, B_K, B_V, seq_lens, image_tokens: int, scales=None,
+                 softmax_scale: Optional[float] = None) -> np.ndarray:
+    """Decode with one pair of factors for the image block and another for
+    the text, float64 [B, Hq, d].
+
+    AttentionPack page, section 2.A: visual and textual tokens are compressed
+    separately, since their statistics differ.  Reading: every sequence
+    starts with an image block of `image_tokens` tokens (the same count for
+    all sequences, as in the gqa_vlm workload's 576-token block); token t of a
+    sequence uses factor set 0 when t < image_tokens and set 1 otherwise, for
+    both K and V.  B_K, B_V [2, Hkv, r, d]; other arguments as in decode().
+    Keys and values are rebuilt per token with the token's set, then the
+    ordinary softmax attention of attend() runs over all of them.
+    """
+    Bsz, Hq, d = q.shape
+    _, Hkv, T, r = L_K.shape
+    if B_K.shape != (2, Hkv, r, d) or B_V.shape != B_K.shape or L_V.shape != L_K.shape:
+        raise ValueError("B_K, B_V [2, Hkv, r, d] and L [B, Hkv, T, r] expected")
+    if image_tokens < 0:
+        raise ValueError("image_tokens must be >= 0")
+    group = Hq // Hkv
+    alpha = float(softmax_scale) if softmax_scale is not None else 1.0 / np.sqrt(d)
+    out = np.empty((Bsz, Hq, d), dtype=np.float64)
+    for b in range(Bsz):
+        n = int(seq_lens[b])
+        if n <= 0 or n > T:
+            raise ValueError(f"seq_len {n} out of range")
+        ni = min(int(image_tokens), n)
+        for h in range(Hq):
+            g = h // group
+            sK = scales[0, b, g, :n] if scales is not None else None
+            sV = scales[1, b, g, :n] if scales is not None else None
+            Lk = dequantize(L_K[b, g, :n], sK)
+            Lv = dequantize(L_V[b, g, :n], sV)
+            K = np.concatenate([rebuild(Lk[:ni], B_K[0, g]), rebuild(Lk[ni:], B_K[1, g])])
+            V = np.concatenate([rebuild(Lv[:ni], B_V[0, g]), rebuild(Lv[ni:], B_V[1, g])])
             out[b, h] = attend(q[b, h], K, V, alpha)
     return out
