@@ -60,6 +60,8 @@ def parse():
                     help="skip the rebuilt-key (and rotated-key) mode timing")
     ap.add_argument("--no-append", action="store_true",
                     help="skip the append-step timing")
+    ap.add_argument("--no-modal", action="store_true",
+                    help="skip the separate image/text factor timing")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the shared-latent (one stream for all heads) timing")
     return ap.parse_args()
@@ -285,6 +287,8 @@ def main():
         line["append_step"] = append_step(w, torch, lr, args)
     if not args.no_shared:
         line["shared_latent"] = shared_latent(w, torch, lr, args, ms_per_step)
+    if not args.no_modal:
+        line["modal_factors"] = modal_factors(w, torch, lr, args, base, sets, ms_per_step)
     if args.probe:
         line["probe"] = run_probe(torch, lr)
     if not args.no_cpu_baseline:
@@ -419,6 +423,40 @@ def append_step(w, torch, lr, args):
            2 * w.batch * w.num_kv_heads * w.rank * esz + (0 if sc is None else 2 * w.batch * w.num_kv_heads * 4))
     return dict(us_per_call=us, model_dim=D, bytes_per_call=alg, GBps=alg / (us / 1e6) / 1e9,
                 kernels="append_partial_kernel + append_finish_kernel")
+
+
+def modal_factors(w, torch, lr, args, base, sets, one_set_ms):
+    """The same step with separate factors for the workload's image block and
+    its text (AttentionPack's modal separation): the image tokens and the
+    text in partitions of their own, one latent-space sum per set in the
+    combine.  None for workloads without an image block; the second factor
+    set is drawn on the device (its values do not change the work)."""
+    import workloads
+    ni = int(workloads.SPECS[w.name].get("image_tokens", 0))
+    if ni <= 0:
+        return None
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2025)
+    BK = torch.stack([base["B_K"], (torch.randn(base["B_K"].shape, generator=g, device="cuda") *
+                                    base["B_K"].float().std()).to(base["B_K"].dtype)])
+    BV = torch.stack([base["B_V"], (torch.randn(base["B_V"].shape, generator=g, device="cuda") *
+                                    base["B_V"].float().std()).to(base["B_V"].dtype)])
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    decs = [lr.ModalDecoder(base["q"], lk, lv, BK, BV, base["seq_lens"], ni, sc, out=out,
+                            num_splits=args.num_splits)
+            for lk, lv, sc in sets]
+    n = len(decs)
+    for i in range(args.warmup):
+        decs[i % n]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        decs[i % n]()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    return dict(ms_per_step=ms, tokens_per_s=w.batch / (ms / 1e3), image_tokens=ni,
+                vs_one_set=ms / one_set_ms,
+                records=lr.modal_workspace_size(decs[0].params, ni))
 
 
 def shared_latent(w, torch, lr, args, grouped_ms):

@@ -270,6 +270,40 @@ int lrattn_rebuild_decode(const lrattn_params* p,
                           lrattn_stream stream);
 
 /*
+ * Separate factors for the image block and the text (AttentionPack page,
+ * section 2.A: visual and textual tokens are compressed apart, as their
+ * statistics differ).  Every sequence starts with an image block of
+ * image_tokens tokens; token t uses factor set 0 when t < image_tokens and
+ * set 1 otherwise.  For every b, h with g = h / (Hq / Hkv), n = seq_lens[b]:
+ *   K[t] = Lk[t] . B_K[m(t), g]     V[t] = Lv[t] . B_V[m(t), g]     t < n
+ *   out[b,h,:] = sum_t softmax_t(softmax_scale * <q[b,h,:], K[t]>) V[t]
+ * with m(t) = 0 for t < image_tokens, else 1; Lk, Lv as in lrattn_decode.
+ *   B_K, B_V [2, Hkv, r, d]   set 0 (image) then set 1 (text)
+ *   image_tokens >= 0 (0: every token uses set 1; >= T: every token set 0)
+ * The image tokens and the text are split into partitions apart, so no
+ * partition mixes the sets; the combine keeps one latent-space sum per set
+ * under the common log-sum-exp and projects each with its own B_V.  Other
+ * tensors, dtypes, alignment, seq_lens handling, ownership, errors and
+ * determinism as in lrattn_decode; head_dim in {64, 128} and rank <= 64,
+ * else LRATTN_ERR_UNSUPPORTED.  The workspace must hold
+ * lrattn_modal_workspace_size bytes.
+ */
+int lrattn_modal_workspace_size(const lrattn_params* p, int32_t image_tokens, size_t* bytes);
+int lrattn_modal_decode(const lrattn_params* p,
+                        int32_t image_tokens,
+                        const void* q,
+                        const void* L_K,
+                        const void* L_V,
+                        const void* B_K,
+                        const void* B_V,
+                        const float* scales,
+                        const int32_t* seq_lens,
+                        void* out,
+                        void* workspace,
+                        size_t workspace_bytes,
+                        lrattn_stream stream);
+
+/*
  * Shared latent streams with per-query-head factors (AttentionPack page,
  * section 2.A: the heads' keys and values are factored together, so the
  * cache keeps one compressed row per token shared by the heads, and head h

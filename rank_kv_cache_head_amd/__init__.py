@@ -87,6 +87,10 @@ def lib() -> ctypes.CDLL:
                                           ctypes.c_size_t, _VP]
         L.lrattn_rebuild_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                             ctypes.c_size_t, _VP]
+        L.lrattn_modal_decode.argtypes = [_PP, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                          _VP, _VP, ctypes.c_size_t, _VP]
+        L.lrattn_modal_workspace_size.argtypes = [_PP, ctypes.c_int32,
+                                                  ctypes.POINTER(ctypes.c_size_t)]
         L.lrattn_rebuild_plan.argtypes = [_PP, ctypes.POINTER(ctypes.c_int32),
                                           ctypes.POINTER(ctypes.c_int32)]
         L.lrattn_rebuild_workspace_size.argtypes = [_PP, ctypes.POINTER(ctypes.c_size_t)]
@@ -110,6 +114,7 @@ def lib() -> ctypes.CDLL:
         for fn in ("lrattn_plan", "lrattn_workspace_size", "lrattn_decode", "lrattn_partition",
                    "lrattn_combine", "lrattn_dense_decode", "lrattn_rebuild_decode",
                    "lrattn_rebuild_plan", "lrattn_rebuild_workspace_size",
+                   "lrattn_modal_decode", "lrattn_modal_workspace_size",
                    "lrattn_append", "lrattn_append_workspace_size",
                    "lrattn_shared_decode", "lrattn_shared_workspace_size",
                    "lrattn_probe_read",
@@ -247,6 +252,78 @@ def decode(q, L_K, L_V, B_K, B_V, seq_lens, scales=None, *, out=None, workspace=
                              _stream(stream))
     _check(st, "lrattn_decode")
     return out
+
+
+def modal_params_for(q, L_K, B_K, *, out_dtype=None, softmax_scale=None,
+                     num_splits: int = 0) -> Params:
+    """Parameter block for two factor sets: B_K [2, Hkv, r, d] (image, text)."""
+    if B_K.dim() != 4 or B_K.shape[0] != 2:
+        raise ValueError("B_K [2, Hkv, r, d] expected (image set, text set)")
+    return params_for(q, L_K, B_K[0], out_dtype=out_dtype, softmax_scale=softmax_scale,
+                      num_splits=num_splits)
+
+
+def modal_workspace_size(p: Params, image_tokens: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().lrattn_modal_workspace_size(ctypes.byref(p), int(image_tokens), ctypes.byref(b)),
+           "lrattn_modal_workspace_size")
+    return b.value
+
+
+def _check_modal(p: Params, B_K, B_V):
+    if tuple(B_V.shape) != tuple(B_K.shape) or not (B_K.is_contiguous() and B_V.is_contiguous()):
+        raise ValueError("B_K, B_V must both be contiguous [2, Hkv, r, d]")
+
+
+def modal_decode(q, L_K, L_V, B_K, B_V, seq_lens, image_tokens: int, scales=None, *, out=None,
+                 workspace=None, softmax_scale=None, num_splits: int = 0, out_dtype=None,
+                 stream=None):
+    """lrattn_modal_decode: factor set 0 for the first image_tokens tokens of
+    every sequence, set 1 for the rest; B_K, B_V [2, Hkv, r, d]."""
+    import torch
+    p = modal_params_for(q, L_K, B_K, out_dtype=out_dtype, softmax_scale=softmax_scale,
+                         num_splits=num_splits)
+    _check_shapes(p, L_V, B_V[0], scales, seq_lens)
+    _check_modal(p, B_K, B_V)
+    if out is None:
+        out = torch.empty((p.batch, p.num_q_heads, p.head_dim),
+                          dtype=torch.float32 if p.out_dtype == F32 else torch.bfloat16,
+                          device=q.device)
+    ws, ws_bytes = _workspace(p, workspace, q.device, modal_workspace_size(p, image_tokens))
+    st = lib().lrattn_modal_decode(ctypes.byref(p), int(image_tokens), _ptr(q), _ptr(L_K),
+                                   _ptr(L_V), _ptr(B_K), _ptr(B_V), _ptr(scales),
+                                   _ptr(seq_lens), _ptr(out), _ptr(ws), ws_bytes,
+                                   _stream(stream))
+    _check(st, "lrattn_modal_decode")
+    return out
+
+
+class ModalDecoder:
+    """lrattn_modal_decode on fixed buffers, marshalled once (see Decoder)."""
+
+    def __init__(self, q, L_K, L_V, B_K, B_V, seq_lens, image_tokens: int, scales=None, *,
+                 out=None, workspace=None, softmax_scale=None, num_splits: int = 0,
+                 out_dtype=None, stream=None):
+        import torch
+        p = modal_params_for(q, L_K, B_K, out_dtype=out_dtype, softmax_scale=softmax_scale,
+                             num_splits=num_splits)
+        _check_shapes(p, L_V, B_V[0], scales, seq_lens)
+        _check_modal(p, B_K, B_V)
+        if out is None:
+            out = torch.empty((p.batch, p.num_q_heads, p.head_dim),
+                              dtype=torch.float32 if p.out_dtype == F32 else torch.bfloat16,
+                              device=q.device)
+        ws, ws_bytes = _workspace(p, workspace, q.device, modal_workspace_size(p, image_tokens))
+        self.params, self.out, self.workspace = p, out, ws
+        self._keep = (q, L_K, L_V, B_K, B_V, seq_lens, scales)
+        self._fn = lib().lrattn_modal_decode
+        self._args = (ctypes.byref(p), int(image_tokens), _ptr(q), _ptr(L_K), _ptr(L_V),
+                      _ptr(B_K), _ptr(B_V), _ptr(scales), _ptr(seq_lens), _ptr(out), _ptr(ws),
+                      ws_bytes, _stream(stream))
+
+    def __call__(self):
+        _check(self._fn(*self._args), "lrattn_modal_decode")
+        return self.out
 
 
 def dense_params_for(q, K, *, out_dtype=None, softmax_scale=None, num_splits: int = 0) -> Params:

@@ -159,6 +159,8 @@ lrattn::PartitionArgs partition_args(const lrattn_params* p, const Plan& pl, con
   a.hps = p->num_q_heads / p->num_kv_heads;
   a.xcd_group = 0;
   a.T = p->max_seq_len; a.P = pl.P; a.S = pl.S;
+  a.t_lo = 0; a.t_hi = p->max_seq_len; a.p_off = 0; a.P_rec = pl.P;
+  a.BK1 = nullptr; a.n_img = 0; a.P_img = 0; a.S_img = 1;
   a.q_dtype = p->q_dtype; a.f_dtype = p->factor_dtype;
   a.qscale = qscale_for(p);
   return a;
@@ -171,6 +173,7 @@ lrattn::CombineArgs combine_args(const lrattn_params* p, const Plan& pl, const v
   a.B = p->batch; a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.d = p->head_dim;
   a.r = p->rank; a.T = p->max_seq_len; a.P = pl.P; a.S = pl.S;
   a.factor_per_head = 0;
+  a.BV1 = nullptr; a.n_img = 0; a.P_img = 0; a.S_img = 1;
   return a;
 }
 
@@ -286,6 +289,77 @@ int lrattn_dense_decode(const lrattn_params* p, const void* q, const void* K, co
   if (lrattn::launch_partition(p->latent_dtype, p->rank, group_of(p), pa, s) != hipSuccess)
     return LRATTN_ERR_HIP;
   const auto ca = combine_args(p, pl, nullptr, seq_lens, out, workspace);
+  if (lrattn::launch_combine(group_of(p), ca, s) != hipSuccess) return LRATTN_ERR_HIP;
+  return LRATTN_OK;
+}
+
+namespace {
+// Image block, then text (AttentionPack page, section 2.A: the modalities are
+// compressed apart, each with its own factors).  Tokens [0, ni) and [ni, T)
+// are planned apart, each in parts of at most the decode plan's S, so that no
+// partition mixes the two factor sets: records [0, P_img) hold the image
+// parts, [P_img, P_img + P_txt) the text parts.
+struct ModalPlan {
+  int32_t ni, P_img, S_img, P_txt, S_txt;
+};
+
+int modal_plan(const lrattn_params* p, int32_t image_tokens, Plan* pl, ModalPlan* mp) {
+  int st = check_params(p, pl);
+  if (st != LRATTN_OK) return st;
+  if (image_tokens < 0) return LRATTN_ERR_SHAPE;
+  if (!lrattn::modal_supported(p->head_dim, p->rank)) return LRATTN_ERR_UNSUPPORTED;
+  const int64_t T = p->max_seq_len, S = pl->S;
+  const int64_t ni = image_tokens < T ? image_tokens : T, nt = T - ni;
+  const int64_t P_img = (ni + S - 1) / S, P_txt = (nt + S - 1) / S;
+  mp->ni = (int32_t)ni;
+  mp->P_img = (int32_t)P_img;
+  mp->S_img = P_img ? (int32_t)((ni + P_img - 1) / P_img) : 1;
+  mp->P_txt = (int32_t)P_txt;
+  mp->S_txt = P_txt ? (int32_t)((nt + P_txt - 1) / P_txt) : 1;
+  pl->P = (int32_t)(P_img + P_txt);
+  if (pl->P > 65535) return LRATTN_ERR_UNSUPPORTED;  // grid z: partitions
+  if (checked_mul({p->batch, p->num_q_heads, pl->P, p->rank + kRecPad, 4}) < 0)
+    return LRATTN_ERR_SHAPE;
+  return LRATTN_OK;
+}
+}  // namespace
+
+int lrattn_modal_workspace_size(const lrattn_params* p, int32_t image_tokens, size_t* bytes) {
+  if (!bytes) return LRATTN_ERR_NULL;
+  Plan pl;
+  ModalPlan mp;
+  const int st = modal_plan(p, image_tokens, &pl, &mp);
+  if (st != LRATTN_OK) return st;
+  *bytes = workspace_bytes_for(p, pl);
+  return LRATTN_OK;
+}
+
+int lrattn_modal_decode(const lrattn_params* p, int32_t image_tokens, const void* q,
+                        const void* L_K, const void* L_V, const void* B_K, const void* B_V,
+                        const float* scales, const int32_t* seq_lens, void* out,
+                        void* workspace, size_t workspace_bytes, lrattn_stream stream) {
+  Plan pl;
+  ModalPlan mp;
+  int st = modal_plan(p, image_tokens, &pl, &mp);
+  if (st == LRATTN_OK) st = check_partition_ptrs(p, q, L_K, L_V, B_K, scales, seq_lens);
+  if (st == LRATTN_OK) st = check_combine_ptrs(B_V, seq_lens, out);
+  if (st == LRATTN_OK) st = check_workspace(p, pl, workspace, workspace_bytes);
+  if (st != LRATTN_OK) return st;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // set 1 (text) follows set 0 (image) in B_K and B_V: [2, Hkv, r, d]
+  const size_t fset = (size_t)p->num_kv_heads * p->rank * p->head_dim * esize(p->factor_dtype);
+  // one launch over both segments: partitions [0, P_img) the image tokens
+  // with set 0, the rest the text with set 1
+  auto pa = partition_args(p, pl, q, L_K, L_V, B_K, scales, seq_lens, workspace);
+  pa.S = mp.S_txt;
+  pa.BK1 = static_cast<const char*>(B_K) + fset;
+  pa.n_img = mp.ni; pa.P_img = mp.P_img; pa.S_img = mp.S_img;
+  if (lrattn::launch_partition(p->latent_dtype, p->rank, group_of(p), pa, s) != hipSuccess)
+    return LRATTN_ERR_HIP;
+  auto ca = combine_args(p, pl, B_V, seq_lens, out, workspace);
+  ca.S = mp.S_txt;
+  ca.BV1 = static_cast<const char*>(B_V) + fset;
+  ca.n_img = mp.ni; ca.P_img = mp.P_img; ca.S_img = mp.S_img;
   if (lrattn::launch_combine(group_of(p), ca, s) != hipSuccess) return LRATTN_ERR_HIP;
   return LRATTN_OK;
 }

@@ -51,6 +51,15 @@ struct PartitionArgs {
   int32_t HG;              // head groups (grid y): query heads hg * G .. + G - 1
   int32_t hps;             // query heads per latent stream: group hg reads stream hg * G / hps
   int32_t P, S;            // partitions, tokens per partition
+  // token window and record slots of this launch: partition p covers tokens
+  // [t_lo + p S, t_lo + (p + 1) S) clipped to min(seq_len, t_hi) and writes
+  // record slot p_off + p of P_rec per head (defaults 0, T, 0, P)
+  int32_t t_lo, t_hi, p_off, P_rec;
+  // two factor sets (BK1 non-null): partitions [0, P_img) take the image
+  // tokens [0, n_img) in parts of S_img with BK, the others the text from
+  // n_img in parts of S with BK1 (record slots unchanged)
+  const void* BK1;
+  int32_t n_img, P_img, S_img;
   int32_t xcd_group;       // 1: one-dimensional grid, head groups of a tile on one XCD
   int32_t q_dtype, f_dtype;
   float qscale;            // softmax_scale * log2(e)
@@ -63,8 +72,15 @@ struct CombineArgs {
   int32_t B, Hq, Hkv, d, r, T;
   int32_t P, S;
   int32_t factor_per_head;  // B_V indexed by query head (shared latent streams)
+  // two factor sets (image block, then text): merge.BV is the image set and
+  // BV1 the text set; records [0, P_img) cover tokens [0, n_img) in parts of
+  // S_img, records [P_img, P) the rest in parts of S (BV1 null: one set)
+  const void* BV1;
+  int32_t n_img, P_img, S_img;
 };
 
+// True when the combine has a two-factor-set (image, text) form for (d, r).
+bool modal_supported(int head_dim, int rank);
 // True when a partition kernel is compiled for (latent dtype, rank, group).
 bool partition_supported(int latent_dtype, int rank, int group);
 // Name of the partition kernel launch_partition uses for these arguments

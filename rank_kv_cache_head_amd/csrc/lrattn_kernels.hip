@@ -380,7 +380,31 @@ __device__ __forceinline__ void compute_step(
 // close in time, and the tile's latents (read by every head group of a shared
 // stream) are fetched from HBM once and then served by that XCD's L2.
 // Returns false for the padding workgroups of the last round of tiles.
+// Two factor sets (image block, then text) in one launch: partitions
+// [0, P_img) cover the image tokens [0, n_img) in parts of S_img with B_K,
+// the rest cover the text from n_img in parts of S with BK1, writing record
+// slots P_img + .. .  Uniform per workgroup.
+__device__ __forceinline__ void modal_segment(PartitionArgs& a, int& p) {
+  if (a.BK1 == nullptr) return;
+  if (p < a.P_img) {
+    a.t_hi = a.n_img;
+    a.S = a.S_img;
+  } else {
+    p -= a.P_img;
+    a.p_off = a.P_img;
+    a.t_lo = a.n_img;
+    a.BK = a.BK1;
+  }
+}
+
 __device__ __forceinline__ bool tile_of(const PartitionArgs& a, int& p, int& hg, int& b) {
+  if (a.BK1 != nullptr) {
+    // two factor sets: grid (HG, B, P), partitions slowest, so the short
+    // image partitions are dispatched first, one per CU, and the text
+    // partitions then spread evenly over all CUs
+    hg = blockIdx.x; b = blockIdx.y; p = blockIdx.z;
+    return true;
+  }
   if (!a.xcd_group) {
     p = blockIdx.x; hg = blockIdx.y; b = blockIdx.z;
     return true;
@@ -772,7 +796,7 @@ __device__ __forceinline__ void write_records(const PartitionArgs& a, int b, int
                                               const float* red_acc, const float* red_m,
                                               const float* red_l) {
   const int tid = threadIdx.x;
-  float* const rec0 = a.ws + ((size_t)b * a.Hq + (size_t)hg * G) * (size_t)a.P * (R + kRecPad);
+  float* const rec0 = a.ws + ((size_t)b * a.Hq + (size_t)hg * G) * (size_t)a.P_rec * (R + kRecPad);
   for (int it = tid; it < G * R; it += kThreads) {
     const int h = it / R, j = it - h * R;
     float M = red_m[h];
@@ -785,7 +809,7 @@ __device__ __forceinline__ void write_records(const PartitionArgs& a, int b, int
       sacc = fmaf(f, red_acc[(w * G + h) * R + j], sacc);
       L = fmaf(f, red_l[w * G + h], L);
     }
-    float* rec = rec0 + ((size_t)h * a.P + p) * (R + kRecPad);
+    float* rec = rec0 + ((size_t)h * a.P_rec + a.p_off + p) * (R + kRecPad);
     rec[j] = sacc;
     if (j == 0) {
       rec[R] = M;
@@ -805,13 +829,14 @@ void partition_kernel(PartitionArgs a) {
   // head group hg (its G query heads) reads latent stream g
   int p, hg, b;
   if (!tile_of(a, p, hg, b)) return;
+  modal_segment(a, p);
   const int g = hg * G / a.hps;
   // seq_lens[b] is one value for the whole workgroup; keeping it in a scalar
   // register keeps the buffer descriptors below scalar (a descriptor the
   // compiler must treat as per-lane costs a readfirstlane loop per load)
   const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
-  const int t0 = p * a.S;
-  const int t1 = min(t0 + a.S, len);
+  const int t0 = a.t_lo + p * a.S;
+  const int t1 = min(t0 + a.S, min(len, a.t_hi));
   if (t0 >= t1) return;  // partition past the sequence: nothing to write
   const int ntok = t1 - t0;
 
@@ -1209,10 +1234,11 @@ void partition_mfma_kernel(PartitionArgs a) {
   // head group hg (its G query heads) reads latent stream g
   int p, hg, b;
   if (!tile_of(a, p, hg, b)) return;
+  modal_segment(a, p);
   const int g = hg * G / a.hps;
   const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
-  const int t0 = p * a.S;
-  const int t1 = min(t0 + a.S, len);
+  const int t0 = a.t_lo + p * a.S;
+  const int t1 = min(t0 + a.S, min(len, a.t_hi));
   if (t0 >= t1) return;  // partition past the sequence: nothing to write
   const int ntok = t1 - t0;
 
@@ -1712,7 +1738,11 @@ __device__ __forceinline__ void load_chunk(const float* rec0, int p0, int n,
   }
 }
 
-template <int R, int D>
+// Two factor sets (kModal: image block, then text; AttentionPack page,
+// section 2.A compresses the modalities apart): the records of each set fold
+// into their own latent-space sum under the common running max and
+// denominator, and out = (acc_img . B_V_img[g] + acc_txt . B_V_txt[g]) / L.
+template <int R, int D, bool kModal>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void combine_kernel(CombineArgs a) {
   using CL = CombineLds<R>;
@@ -1720,6 +1750,7 @@ void combine_kernel(CombineArgs a) {
   constexpr int kNPG = CL::kNPG, kChunk = CL::kChunk;
   constexpr int kPer = CL::kStage / 4 / kThreads;
   constexpr int NB = kThreads / D, RB = R / NB;
+  constexpr int NSET = kModal ? 2 : 1;
   static_assert(NB * D == kThreads && RB * NB == R, "combine tiling");
   const int hq = blockIdx.x, b = blockIdx.y;
   // B_V block: per kv-head, or per query head (shared latent streams)
@@ -1734,18 +1765,28 @@ void combine_kernel(CombineArgs a) {
   const uint32_t fes = fdt == LRATTN_F32 ? 4u : 2u;
   // dense cache (no B_V, r == d): an empty resource, every load returns zero
   const bool dense = mg.BV == nullptr;
-  const auto rbv = dense ? make_rsrc(nullptr, 0u)
-                         : make_rsrc(static_cast<const char*>(mg.BV) + (size_t)g * R * D * fes,
-                                     (uint32_t)(R * D) * fes);
+  __amdgpu_buffer_rsrc_t rbv[NSET];
+#pragma unroll
+  for (int st = 0; st < NSET; ++st) {
+    const void* bv = st == 0 ? mg.BV : a.BV1;
+    rbv[st] = dense ? make_rsrc(nullptr, 0u)
+                    : make_rsrc(static_cast<const char*>(bv) + (size_t)g * R * D * fes,
+                                (uint32_t)(R * D) * fes);
+  }
   // at most 64 words in flight per thread (r = 128 with d = 256 takes four
-  // batches of 32, the later ones loaded at the projection)
-  constexpr int kB = RB <= 64 ? RB : 32;
-  uint32_t bw[kB];
+  // batches of 32, the later ones loaded at the projection; two sets take
+  // one batch of up to 32 each, else batches of 16)
+  constexpr int kB = !kModal ? (RB <= 64 ? RB : 32) : (RB <= 32 ? RB : 16);
+  static_assert(RB % kB == 0, "projection batches");
+  uint32_t bw[NSET][kB];
   auto load_bv = [&](int k0) {
 #pragma unroll
-    for (int k = 0; k < kB; ++k) {
-      const uint32_t off = (uint32_t)((jb * RB + k0 + k) * D + i_col) * fes;
-      bw[k] = __builtin_amdgcn_raw_buffer_load_b32(rbv, (int)(off & ~3u), 0, 0);
+    for (int st = 0; st < NSET; ++st) {
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const uint32_t off = (uint32_t)((jb * RB + k0 + k) * D + i_col) * fes;
+        bw[st][k] = __builtin_amdgcn_raw_buffer_load_b32(rbv[st], (int)(off & ~3u), 0, 0);
+      }
     }
   };
   load_bv(0);
@@ -1757,40 +1798,62 @@ void combine_kernel(CombineArgs a) {
   // with nothing to fold and writes a zero row.  A branch here would let the
   // compiler move the loads above behind the seq_lens round trip.
   const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
-  const int np = (len + a.S - 1) / a.S;
+  // record ranges [beg, beg + cnt) of each set
+  int beg[NSET], cnt[NSET];
+  if constexpr (kModal) {
+    const int ni = min(len, a.n_img);
+    beg[0] = 0;
+    cnt[0] = (ni + a.S_img - 1) / a.S_img;
+    beg[1] = a.P_img;
+    cnt[1] = (max(len - a.n_img, 0) + a.S - 1) / a.S;
+  } else {
+    beg[0] = 0;
+    cnt[0] = (len + a.S - 1) / a.S;
+  }
+  int np = 0;
+#pragma unroll
+  for (int st = 0; st < NSET; ++st) np += cnt[st];
   const size_t out_row0 = ((size_t)b * a.Hq + hq) * D;
 
   __shared__ CL sm;
+  __shared__ float vt1[kModal ? kNPG * R + R : 1];  // second set: group sums, then v~
   const float* stage = reinterpret_cast<const float*>(sm.stage);
   // kNPG * R <= kThreads (r = 48 leaves 16 threads without a group)
   const int pg = tid / R, j = tid - pg * R;
   const bool folds = pg < kNPG;
-  float m = -FLT_MAX, L = 0.f, acc = 0.f;
-  for (int p0 = 0; p0 < np; p0 += kChunk) {
-    if (p0 > 0) {
-      __syncthreads();  // previous chunk consumed
-      load_chunk<R>(rec0, p0, min(kChunk, np - p0), v4);
-    }
-    // 2. stage (every slot is written: zeros past the chunk)
+  float m = -FLT_MAX, L = 0.f, acc[NSET];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) sm.stage[tid + k * kThreads] = v4[k];
-    __syncthreads();
-    // 3. fold this chunk's partitions pg, pg + NPG, ...
-    const int pc = folds ? min(kChunk, np - p0) : 0;
-    for (int pp = pg; pp < pc; pp += kNPG) {
-      const float* rec = stage + pp * RS;
-      const float mp = rec[R];
-      const float nm = fmaxf(m, mp);
-      const float fa = fast_exp2(m - nm), fb = fast_exp2(mp - nm);
-      L = fmaf(L, fa, rec[R + 1] * fb);
-      acc = fmaf(acc, fa, rec[j] * fb);
-      m = nm;
+  for (int st = 0; st < NSET; ++st) acc[st] = 0.f;
+#pragma unroll
+  for (int st = 0; st < NSET; ++st) {
+    for (int p0 = 0; p0 < cnt[st]; p0 += kChunk) {
+      if (st > 0 || p0 > 0) {
+        __syncthreads();  // previous chunk consumed
+        load_chunk<R>(rec0, beg[st] + p0, min(kChunk, cnt[st] - p0), v4);
+      }
+      // 2. stage (every slot is written: zeros past the chunk)
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) sm.stage[tid + k * kThreads] = v4[k];
+      __syncthreads();
+      // 3. fold this chunk's partitions pg, pg + NPG, ... into set st
+      const int pc = folds ? min(kChunk, cnt[st] - p0) : 0;
+      for (int pp = pg; pp < pc; pp += kNPG) {
+        const float* rec = stage + pp * RS;
+        const float mp = rec[R];
+        const float nm = fmaxf(m, mp);
+        const float fa = fast_exp2(m - nm), fb = fast_exp2(mp - nm);
+        L = fmaf(L, fa, rec[R + 1] * fb);
+#pragma unroll
+        for (int u = 0; u < NSET; ++u) acc[u] = u == st ? fmaf(acc[u], fa, rec[j] * fb) : acc[u] * fa;
+        m = nm;
+      }
     }
   }
   if (folds) {
     sm.m[tid] = m;
     sm.l[tid] = L;
-    sm.v[tid] = acc;
+    sm.v[tid] = acc[0];
+    if constexpr (kModal) vt1[tid] = acc[1];
   }
   __syncthreads();
   if (tid < R) {
@@ -1801,14 +1864,16 @@ void combine_kernel(CombineArgs a) {
       const float nm = fmaxf(m, mp);
       const float fa = fast_exp2(m - nm), fb = fast_exp2(mp - nm);
       L = fmaf(L, fa, sm.l[item] * fb);
-      acc = fmaf(acc, fa, sm.v[item] * fb);
+      acc[0] = fmaf(acc[0], fa, sm.v[item] * fb);
+      if constexpr (kModal) acc[1] = fmaf(acc[1], fa, vt1[item] * fb);
       m = nm;
     }
-    sm.vt[tid] = np > 0 ? acc / L : 0.f;
+    sm.vt[tid] = np > 0 ? acc[0] / L : 0.f;
+    if constexpr (kModal) vt1[kNPG * R + tid] = np > 0 ? acc[1] / L : 0.f;
   }
   __syncthreads();
 
-  // 4. row-block partial of out[i] = sum_j v~[j] * B_V[g][j][i]
+  // 4. row-block partial of out[i] = sum_j v~[j] * B_V[g][j][i] (each set)
   const bool odd = i_col & 1;
   float o = 0.f;
 #pragma unroll
@@ -1818,11 +1883,15 @@ void combine_kernel(CombineArgs a) {
       load_bv(k0);
     }
 #pragma unroll
-    for (int k = 0; k < kB; ++k) {
-      const uint32_t w = bw[k];
-      const float two = fdt == LRATTN_BF16 ? (odd ? bf16_hi(w) : bf16_lo(w))
-                                           : (odd ? f16_hi(w) : f16_lo(w));
-      o = fmaf(sm.vt[jb * RB + k0 + k], fdt == LRATTN_F32 ? __uint_as_float(w) : two, o);
+    for (int st = 0; st < NSET; ++st) {
+      const float* vt = st == 0 ? sm.vt : vt1 + kNPG * R;
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const uint32_t w = bw[st][k];
+        const float two = fdt == LRATTN_BF16 ? (odd ? bf16_hi(w) : bf16_lo(w))
+                                             : (odd ? f16_hi(w) : f16_lo(w));
+        o = fmaf(vt[jb * RB + k0 + k], fdt == LRATTN_F32 ? __uint_as_float(w) : two, o);
+      }
     }
   }
   sm.part[jb * D + i_col] = o;
@@ -1890,7 +1959,8 @@ constexpr bool mfma_scores(int latent_dtype, int rank, int group) {
 // 8 heads (the shared-stream groups; smaller groups keep the default).
 template <class LT, int R>
 hipError_t launch_pg(int group, const PartitionArgs& a, hipStream_t s) {
-  const dim3 grid = a.xcd_group ? dim3(8 * a.HG * ((a.P * a.B + 7) / 8)) : dim3(a.P, a.HG, a.B);
+  const dim3 grid = a.BK1 ? dim3(a.HG, a.B, a.P)
+                  : a.xcd_group ? dim3(8 * a.HG * ((a.P * a.B + 7) / 8)) : dim3(a.P, a.HG, a.B);
   const dim3 block(kThreads);
   const bool keep = a.xcd_group != 0;
   if constexpr (mfma_scores(std::is_same<LT, LatBF16>::value ? LRATTN_BF16 : -1, R, 4)) {
@@ -1965,16 +2035,32 @@ hipError_t launch_rg(int group, bool rot, const PartitionArgs& a, hipStream_t s)
 template <int R>
 hipError_t launch_cg(const CombineArgs& a, hipStream_t s) {
   const dim3 grid(a.Hq, a.B), block(kThreads);
+  // two factor sets: d <= 128 and r <= 64 (modal_supported)
+  if (a.BV1 != nullptr) {
+    if constexpr (R <= 64) {
+      switch (a.d) {
+        case 64: hipLaunchKernelGGL((combine_kernel<R, 64, true>), grid, block, 0, s, a); break;
+        case 128: hipLaunchKernelGGL((combine_kernel<R, 128, true>), grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   switch (a.d) {
-    case 64: hipLaunchKernelGGL((combine_kernel<R, 64>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((combine_kernel<R, 128>), grid, block, 0, s, a); break;
-    case 256: hipLaunchKernelGGL((combine_kernel<R, 256>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((combine_kernel<R, 64, false>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((combine_kernel<R, 128, false>), grid, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((combine_kernel<R, 256, false>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 }  // namespace
+
+bool modal_supported(int head_dim, int rank) {
+  return (head_dim == 64 || head_dim == 128) && rank <= 64;
+}
 
 bool partition_supported(int latent_dtype, int rank, int group) {
   int esz;

@@ -281,3 +281,33 @@ def test_shared_decode_validates_on_host():
     assert call(one, bv=MISALIGNED) == -5
     assert call(one, ws=None, ws_bytes=need) == -6
     assert call(one, ws_bytes=need - 1) == -6
+
+
+def test_modal_decode_validates_on_host():
+    L = lr.lib()
+    def call(p, ni=576, q=ALIGNED, lk=ALIGNED, lv=ALIGNED, bk=ALIGNED, bv=ALIGNED, sc=None,
+             seq=ALIGNED, out=ALIGNED, ws=ALIGNED, ws_bytes=0):
+        return L.lrattn_modal_decode(ctypes.byref(p), ni, q, lk, lv, bk, bv, sc, seq, out, ws,
+                                     ws_bytes, None)
+    p = params()                                       # bf16, d 128, r 64, G 4, T 1000
+    assert call(params(head_dim=256)) == -4            # d in {64, 128}
+    assert call(params(rank=128)) == -4                # r <= 64
+    assert call(p, ni=-1) == -2
+    assert call(p, lk=None) == -1
+    assert call(p, bv=None) == -1
+    assert call(p, bk=MISALIGNED) == -5
+    assert call(p, ws=None) == -6
+    assert call(p, ws_bytes=lr.modal_workspace_size(p, 576) - 1) == -6
+
+
+def test_modal_plan_records():
+    """Image tokens and text are split apart, each in parts of at most the
+    decode plan's S: the workspace holds P_img + P_txt records per head."""
+    p = params(max_seq_len=1000)
+    P, S = lr.plan(p)
+    rec = lambda n: (p.batch * p.num_q_heads * n * (p.rank + 4) * 4 + 255) // 256 * 256
+    for ni in (0, 1, 576, 999, 1000, 5000):
+        nic = min(ni, 1000)
+        want = -(-nic // S) + -(-(1000 - nic) // S)
+        assert lr.modal_workspace_size(p, ni) == rec(want), ni
+
