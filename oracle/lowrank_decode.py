@@ -43,7 +43,7 @@ import numpy as np
 
 __all__ = ["as_float64", "dequantize", "rebuild", "attend", "decode",
            "decode_rows", "decode_absorbed", "rotate", "decode_rotated", "decode_shared",
-           "decode_modal"]
+           "decode_modal", "decode_adaptive"]
 
 
 def as_float64(a: np.ndarray, tag: str) -> np.ndarray:
@@ -306,3 +306,61 @@ def decode_modal(q, L_K, L_V, B_K, B_V, seq_lens, image_tokens: int, scales=None
             V = np.concatenate([rebuild(Lv[:ni], B_V[0, g]), rebuild(Lv[ni:], B_V[1, g])])
             out[b, h] = attend(q[b, h], K, V, alpha)
     return out
+
+
+def decode_adaptive(q, L_K, L_V, B_K, B_V, seq_lens, importance, threshold: float,
+                    low_rank: int, decay: float, scales=None,
+                    softmax_scale: Optional[float] = None):
+    """Decode with a per-token rank chosen by an importance score, and the
+    score's moving-average update, float64: (out [B, Hq, d], importance').
+
+    AttentionPack page, section 2.B (attention-aware decompression): a moving
+    average of each token's accumulated attention marks the important
+    tokens; those are rebuilt with the full rank, the others with a reduced
+    rank.  Readings: the latent coordinates are ordered by importance (the
+    leading singular directions first), so rank k keeps coordinates [0, k) of
+    the token's latent row and rows [0, k) of the factors, for K and V alike;
+    token t of sequence b, kv-head g uses the full rank r when
+    importance[b, g, t] >= threshold and low_rank otherwise; after the step,
+    for t < seq_len, importance'[b, g, t] = decay * importance[b, g, t] +
+    (1 - decay) * a_t with a_t the attention weight of token t averaged over
+    the query heads of kv-head g (entries t >= seq_len are unchanged).
+
+    importance [B, Hkv, T]; 1 <= low_rank <= r; 0 <= decay <= 1.
+    """
+    Bsz, Hq, d = q.shape
+    _, Hkv, T, r = L_K.shape
+    _check_shapes(q, L_K, L_V, B_K, B_V, seq_lens, scales)
+    if importance.shape != (Bsz, Hkv, T):
+        raise ValueError("importance must be [B, Hkv, T]")
+    if not 1 <= low_rank <= r:
+        raise ValueError("low_rank must be in [1, r]")
+    group = Hq // Hkv
+    alpha = float(softmax_scale) if softmax_scale is not None else 1.0 / np.sqrt(d)
+    out = np.empty((Bsz, Hq, d), dtype=np.float64)
+    imp = np.array(importance, dtype=np.float64, copy=True)
+    for b in range(Bsz):
+        n = int(seq_lens[b])
+        if n <= 0 or n > T:
+            raise ValueError(f"seq_len {n} out of range")
+        for g in range(Hkv):
+            sK = scales[0, b, g, :n] if scales is not None else None
+            sV = scales[1, b, g, :n] if scales is not None else None
+            Lk = dequantize(L_K[b, g, :n], sK)
+            Lv = dequantize(L_V[b, g, :n], sV)
+            full = importance[b, g, :n] >= threshold
+            K = np.empty((n, d))
+            V = np.empty((n, d))
+            for t in range(n):
+                k = r if full[t] else low_rank
+                K[t] = Lk[t, :k] @ B_K[g, :k]
+                V[t] = Lv[t, :k] @ B_V[g, :k]
+            a = np.zeros(n)
+            for h in range(g * group, (g + 1) * group):
+                s_ = alpha * (K @ q[b, h])
+                e = np.exp(s_ - s_.max())
+                prob = e / e.sum()
+                out[b, h] = prob @ V
+                a += prob / group
+            imp[b, g, :n] = decay * importance[b, g, :n] + (1.0 - decay) * a
+    return out, imp

@@ -373,13 +373,6 @@ __device__ __forceinline__ void compute_step(
   }
 }
 
-// The workgroup's (partition p, head group hg, sequence b).  Normally the
-// grid is (P, HG, B).  With a.xcd_group the grid is one-dimensional and the
-// HG head groups of one (p, b) tile take linear ids 8 apart: workgroups are
-// handed to the 8 XCDs in turn by linear id, so those groups run on one XCD,
-// close in time, and the tile's latents (read by every head group of a shared
-// stream) are fetched from HBM once and then served by that XCD's L2.
-// Returns false for the padding workgroups of the last round of tiles.
 // Two factor sets (image block, then text) in one launch: partitions
 // [0, P_img) cover the image tokens [0, n_img) in parts of S_img with B_K,
 // the rest cover the text from n_img in parts of S with BK1, writing record
@@ -397,6 +390,13 @@ __device__ __forceinline__ void modal_segment(PartitionArgs& a, int& p) {
   }
 }
 
+// The workgroup's (partition p, head group hg, sequence b).  Normally the
+// grid is (P, HG, B).  With a.xcd_group the grid is one-dimensional and the
+// HG head groups of one (p, b) tile take linear ids 8 apart: workgroups are
+// handed to the 8 XCDs in turn by linear id, so those groups run on one XCD,
+// close in time, and the tile's latents (read by every head group of a shared
+// stream) are fetched from HBM once and then served by that XCD's L2.
+// Returns false for the padding workgroups of the last round of tiles.
 __device__ __forceinline__ bool tile_of(const PartitionArgs& a, int& p, int& hg, int& b) {
   if (a.BK1 != nullptr) {
     // two factor sets: grid (HG, B, P), partitions slowest, so the short
