@@ -60,6 +60,8 @@ def parse():
                     help="skip the rebuilt-key (and rotated-key) mode timing")
     ap.add_argument("--no-append", action="store_true",
                     help="skip the append-step timing")
+    ap.add_argument("--no-adaptive", action="store_true",
+                    help="skip the attention-aware adaptive-rank timing")
     ap.add_argument("--no-modal", action="store_true",
                     help="skip the separate image/text factor timing")
     ap.add_argument("--no-shared", action="store_true",
@@ -289,6 +291,8 @@ def main():
         line["shared_latent"] = shared_latent(w, torch, lr, args, ms_per_step)
     if not args.no_modal:
         line["modal_factors"] = modal_factors(w, torch, lr, args, base, sets, ms_per_step)
+    if not args.no_adaptive:
+        line["adaptive_rank"] = adaptive_rank(w, torch, lr, args, base, sets, ms_per_step)
     if args.probe:
         line["probe"] = run_probe(torch, lr)
     if not args.no_cpu_baseline:
@@ -423,6 +427,43 @@ def append_step(w, torch, lr, args):
            2 * w.batch * w.num_kv_heads * w.rank * esz + (0 if sc is None else 2 * w.batch * w.num_kv_heads * 4))
     return dict(us_per_call=us, model_dim=D, bytes_per_call=alg, GBps=alg / (us / 1e6) / 1e9,
                 kernels="append_partial_kernel + append_finish_kernel")
+
+
+def adaptive_rank(w, torch, lr, args, base, sets, plain_ms):
+    """The same step with attention-aware rank (AttentionPack's adaptive
+    decompression): tokens whose importance score is below 0.5 keep r/2
+    latent coordinates; the step writes its logits and updates the scores
+    (decay 0.9).  Scores drawn U(0, 1) on the device.  None where the shape
+    has no adaptive kernel."""
+    G = w.num_q_heads // w.num_kv_heads
+    ok = {"bf16": w.rank in (32, 48, 64), "i8": w.rank == 32 and G in (1, 4),
+          "f32": w.rank == 16 and G == 1}.get(w.latent_dtype, False)
+    if not ok:
+        return None
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2026)
+    imp = torch.rand((w.batch, w.num_kv_heads, w.max_seq_len), generator=g, device="cuda")
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    decs = [lr.AdaptiveDecoder(base["q"], lk, lv, base["B_K"], base["B_V"], base["seq_lens"],
+                               imp, low_rank=w.rank // 2, threshold=0.5, decay=0.9, scales=sc,
+                               out=out, num_splits=args.num_splits)
+            for lk, lv, sc in sets]
+    n = len(decs)
+    for i in range(args.warmup):
+        decs[i % n]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        decs[i % n]()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    valid = int(w.seq_lens.sum())
+    # added traffic per valid token: importance read (partition), logits
+    # written and read, importance read and written (update)
+    extra = valid * (w.num_kv_heads * 4 + 2 * w.num_q_heads * 4 + w.num_kv_heads * 8)
+    return dict(ms_per_step=ms, tokens_per_s=w.batch / (ms / 1e3), low_rank=w.rank // 2,
+                vs_plain=ms / plain_ms, added_bytes_per_step=extra,
+                kernel="partition_kernel (adaptive) + combine + importance_kernel")
 
 
 def modal_factors(w, torch, lr, args, base, sets, one_set_ms):

@@ -270,6 +270,52 @@ int lrattn_rebuild_decode(const lrattn_params* p,
                           lrattn_stream stream);
 
 /*
+ * Attention-aware rank (AttentionPack page, section 2.B: a moving average of
+ * each token's accumulated attention marks the important tokens, which are
+ * rebuilt at the full rank; the others are rebuilt at a reduced rank).  The
+ * latent coordinates are taken as ordered by importance (leading singular
+ * directions first), so rank k keeps coordinates [0, k).  For every b, g and
+ * t < n = seq_lens[b], with k_t = r if importance[b, g, t] >= threshold and
+ * low_rank otherwise:
+ *   K[t] = Lk[t, :k_t] . B_K[g, :k_t, :]     V[t] = Lv[t, :k_t] . B_V[g, :k_t, :]
+ *   out[b,h,:] = sum_t p[b,h,t] V[t],  p = softmax_t(softmax_scale * <q[b,h,:], K[t]>)
+ * and afterwards, in place, for t < n (other entries untouched):
+ *   importance[b, g, t] = decay * importance[b, g, t]
+ *                         + (1 - decay) * mean over the query heads h of g of p[b,h,t]
+ *   importance [B, Hkv, T] fp32, 16-byte aligned, read and written
+ *   low_rank in [1, r]; decay in [0, 1]; threshold not NaN
+ * Three launches: the partitions (which also write each token's logits),
+ * the combine (which also writes each row's final max and denominator), the
+ * update.  The workspace (lrattn_adaptive_workspace_size bytes) holds the
+ * records, the logits [B, Hq, T] and the row statistics.  Supported: bf16
+ * latents with r in {32, 48, 64} and group in {1, 2, 4, 8}; int8 latents
+ * with r = 32 and group 1 or 4; fp32 latents with r = 16 and group 1; else
+ * LRATTN_ERR_UNSUPPORTED.  Other tensors, dtypes, seq_lens handling,
+ * ownership, errors and determinism as in lrattn_decode.
+ */
+typedef struct lrattn_adaptive {
+  int32_t low_rank;   /* rank of the tokens below the threshold */
+  float threshold;    /* importance at or above it: full rank */
+  float decay;        /* weight of the old score in the moving average */
+} lrattn_adaptive;
+int lrattn_adaptive_workspace_size(const lrattn_params* p, const lrattn_adaptive* ad,
+                                   size_t* bytes);
+int lrattn_adaptive_decode(const lrattn_params* p,
+                           const lrattn_adaptive* ad,
+                           const void* q,
+                           const void* L_K,
+                           const void* L_V,
+                           const void* B_K,
+                           const void* B_V,
+                           const float* scales,
+                           const int32_t* seq_lens,
+                           float* importance,
+                           void* out,
+                           void* workspace,
+                           size_t workspace_bytes,
+                           lrattn_stream stream);
+
+/*
  * Separate factors for the image block and the text (AttentionPack page,
  * section 2.A: visual and textual tokens are compressed apart, as their
  * statistics differ).  Every sequence starts with an image block of

@@ -87,6 +87,11 @@ def lib() -> ctypes.CDLL:
                                           ctypes.c_size_t, _VP]
         L.lrattn_rebuild_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                             ctypes.c_size_t, _VP]
+        L.lrattn_adaptive_decode.argtypes = [_PP, ctypes.POINTER(AdaptiveParams), _VP, _VP, _VP,
+                                             _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
+                                             _VP]
+        L.lrattn_adaptive_workspace_size.argtypes = [_PP, ctypes.POINTER(AdaptiveParams),
+                                                     ctypes.POINTER(ctypes.c_size_t)]
         L.lrattn_modal_decode.argtypes = [_PP, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                           _VP, _VP, ctypes.c_size_t, _VP]
         L.lrattn_modal_workspace_size.argtypes = [_PP, ctypes.c_int32,
@@ -115,6 +120,7 @@ def lib() -> ctypes.CDLL:
                    "lrattn_combine", "lrattn_dense_decode", "lrattn_rebuild_decode",
                    "lrattn_rebuild_plan", "lrattn_rebuild_workspace_size",
                    "lrattn_modal_decode", "lrattn_modal_workspace_size",
+                   "lrattn_adaptive_decode", "lrattn_adaptive_workspace_size",
                    "lrattn_append", "lrattn_append_workspace_size",
                    "lrattn_shared_decode", "lrattn_shared_workspace_size",
                    "lrattn_probe_read",
@@ -252,6 +258,82 @@ def decode(q, L_K, L_V, B_K, B_V, seq_lens, scales=None, *, out=None, workspace=
                              _stream(stream))
     _check(st, "lrattn_decode")
     return out
+
+
+class AdaptiveParams(ctypes.Structure):
+    """lrattn_adaptive: rank of the tokens below the importance threshold,
+    the threshold, and the moving average's decay."""
+    _fields_ = [("low_rank", ctypes.c_int32), ("threshold", ctypes.c_float),
+                ("decay", ctypes.c_float)]
+
+
+def adaptive_workspace_size(p: Params, ad: AdaptiveParams) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().lrattn_adaptive_workspace_size(ctypes.byref(p), ctypes.byref(ad),
+                                                ctypes.byref(b)),
+           "lrattn_adaptive_workspace_size")
+    return b.value
+
+
+def _check_importance(p: Params, importance):
+    import torch
+    if (tuple(importance.shape) != (p.batch, p.num_kv_heads, p.max_seq_len) or
+            importance.dtype != torch.float32 or not importance.is_contiguous()):
+        raise ValueError("importance must be contiguous float32 [B, Hkv, T]")
+
+
+def adaptive_decode(q, L_K, L_V, B_K, B_V, seq_lens, importance, *, low_rank: int,
+                    threshold: float, decay: float, scales=None, out=None, workspace=None,
+                    softmax_scale=None, num_splits: int = 0, out_dtype=None, stream=None):
+    """lrattn_adaptive_decode: tokens whose importance is below `threshold`
+    are rebuilt at `low_rank`; `importance` [B, Hkv, T] is updated in place
+    with the step's head-averaged attention (moving average, `decay`)."""
+    import torch
+    p = params_for(q, L_K, B_K, out_dtype=out_dtype, softmax_scale=softmax_scale,
+                   num_splits=num_splits)
+    _check_shapes(p, L_V, B_V, scales, seq_lens)
+    _check_importance(p, importance)
+    ad = AdaptiveParams(int(low_rank), float(threshold), float(decay))
+    if out is None:
+        out = torch.empty((p.batch, p.num_q_heads, p.head_dim),
+                          dtype=torch.float32 if p.out_dtype == F32 else torch.bfloat16,
+                          device=q.device)
+    ws, ws_bytes = _workspace(p, workspace, q.device, adaptive_workspace_size(p, ad))
+    st = lib().lrattn_adaptive_decode(ctypes.byref(p), ctypes.byref(ad), _ptr(q), _ptr(L_K),
+                                      _ptr(L_V), _ptr(B_K), _ptr(B_V), _ptr(scales),
+                                      _ptr(seq_lens), _ptr(importance), _ptr(out), _ptr(ws),
+                                      ws_bytes, _stream(stream))
+    _check(st, "lrattn_adaptive_decode")
+    return out
+
+
+class AdaptiveDecoder:
+    """lrattn_adaptive_decode on fixed buffers, marshalled once (see Decoder)."""
+
+    def __init__(self, q, L_K, L_V, B_K, B_V, seq_lens, importance, *, low_rank: int,
+                 threshold: float, decay: float, scales=None, out=None, workspace=None,
+                 softmax_scale=None, num_splits: int = 0, out_dtype=None, stream=None):
+        import torch
+        p = params_for(q, L_K, B_K, out_dtype=out_dtype, softmax_scale=softmax_scale,
+                       num_splits=num_splits)
+        _check_shapes(p, L_V, B_V, scales, seq_lens)
+        _check_importance(p, importance)
+        ad = AdaptiveParams(int(low_rank), float(threshold), float(decay))
+        if out is None:
+            out = torch.empty((p.batch, p.num_q_heads, p.head_dim),
+                              dtype=torch.float32 if p.out_dtype == F32 else torch.bfloat16,
+                              device=q.device)
+        ws, ws_bytes = _workspace(p, workspace, q.device, adaptive_workspace_size(p, ad))
+        self.params, self.adaptive, self.out, self.workspace = p, ad, out, ws
+        self._keep = (q, L_K, L_V, B_K, B_V, seq_lens, importance, scales)
+        self._fn = lib().lrattn_adaptive_decode
+        self._args = (ctypes.byref(p), ctypes.byref(ad), _ptr(q), _ptr(L_K), _ptr(L_V),
+                      _ptr(B_K), _ptr(B_V), _ptr(scales), _ptr(seq_lens), _ptr(importance),
+                      _ptr(out), _ptr(ws), ws_bytes, _stream(stream))
+
+    def __call__(self):
+        _check(self._fn(*self._args), "lrattn_adaptive_decode")
+        return self.out
 
 
 def modal_params_for(q, L_K, B_K, *, out_dtype=None, softmax_scale=None,

@@ -161,6 +161,7 @@ lrattn::PartitionArgs partition_args(const lrattn_params* p, const Plan& pl, con
   a.T = p->max_seq_len; a.P = pl.P; a.S = pl.S;
   a.t_lo = 0; a.t_hi = p->max_seq_len; a.p_off = 0; a.P_rec = pl.P;
   a.BK1 = nullptr; a.n_img = 0; a.P_img = 0; a.S_img = 1;
+  a.imp = nullptr; a.logits = nullptr; a.imp_thr = 0.f; a.low_rank = p->rank;
   a.q_dtype = p->q_dtype; a.f_dtype = p->factor_dtype;
   a.qscale = qscale_for(p);
   return a;
@@ -174,6 +175,7 @@ lrattn::CombineArgs combine_args(const lrattn_params* p, const Plan& pl, const v
   a.r = p->rank; a.T = p->max_seq_len; a.P = pl.P; a.S = pl.S;
   a.factor_per_head = 0;
   a.BV1 = nullptr; a.n_img = 0; a.P_img = 0; a.S_img = 1;
+  a.stats = nullptr;
   return a;
 }
 
@@ -290,6 +292,77 @@ int lrattn_dense_decode(const lrattn_params* p, const void* q, const void* K, co
     return LRATTN_ERR_HIP;
   const auto ca = combine_args(p, pl, nullptr, seq_lens, out, workspace);
   if (lrattn::launch_combine(group_of(p), ca, s) != hipSuccess) return LRATTN_ERR_HIP;
+  return LRATTN_OK;
+}
+
+namespace {
+// Attention-aware rank: the decode plan's records, then the step's base-2
+// logits [B, Hq, T] and each row's final (max, denominator) [B, Hq, 2], each
+// part at a 256-byte boundary.
+int adaptive_check(const lrattn_params* p, const lrattn_adaptive* ad, Plan* pl,
+                   size_t* logits_off, size_t* stats_off, size_t* total) {
+  int st = check_params(p, pl);
+  if (st != LRATTN_OK) return st;
+  if (!ad) return LRATTN_ERR_NULL;
+  if (ad->low_rank < 1 || ad->low_rank > p->rank || !(ad->decay >= 0.f && ad->decay <= 1.f) ||
+      isnan(ad->threshold))
+    return LRATTN_ERR_SHAPE;
+  if (!lrattn::adaptive_supported(p->latent_dtype, p->rank, group_of(p)))
+    return LRATTN_ERR_UNSUPPORTED;
+  if (checked_mul({p->batch, p->num_q_heads, p->max_seq_len, 4}) < 0) return LRATTN_ERR_SHAPE;
+  const size_t rec = workspace_bytes_for(p, *pl);
+  const size_t lg = ((size_t)p->batch * p->num_q_heads * p->max_seq_len * 4 + 255) & ~(size_t)255;
+  *logits_off = rec;
+  *stats_off = rec + lg;
+  *total = rec + lg + (((size_t)p->batch * p->num_q_heads * 8 + 255) & ~(size_t)255);
+  return LRATTN_OK;
+}
+}  // namespace
+
+int lrattn_adaptive_workspace_size(const lrattn_params* p, const lrattn_adaptive* ad,
+                                   size_t* bytes) {
+  if (!bytes) return LRATTN_ERR_NULL;
+  Plan pl;
+  size_t lo, so, total;
+  const int st = adaptive_check(p, ad, &pl, &lo, &so, &total);
+  if (st != LRATTN_OK) return st;
+  *bytes = total;
+  return LRATTN_OK;
+}
+
+int lrattn_adaptive_decode(const lrattn_params* p, const lrattn_adaptive* ad, const void* q,
+                           const void* L_K, const void* L_V, const void* B_K, const void* B_V,
+                           const float* scales, const int32_t* seq_lens, float* importance,
+                           void* out, void* workspace, size_t workspace_bytes,
+                           lrattn_stream stream) {
+  Plan pl;
+  size_t lo = 0, so = 0, total = 0;
+  int st = adaptive_check(p, ad, &pl, &lo, &so, &total);
+  if (st == LRATTN_OK) st = check_partition_ptrs(p, q, L_K, L_V, B_K, scales, seq_lens);
+  if (st == LRATTN_OK) st = check_combine_ptrs(B_V, seq_lens, out);
+  if (st == LRATTN_OK && !importance) st = LRATTN_ERR_NULL;
+  if (st == LRATTN_OK && !aligned16(importance)) st = LRATTN_ERR_ALIGN;
+  if (st == LRATTN_OK) st = check_workspace(p, pl, workspace, workspace_bytes);
+  if (st == LRATTN_OK && workspace_bytes < total) st = LRATTN_ERR_WORKSPACE;
+  if (st != LRATTN_OK) return st;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* logits = reinterpret_cast<float*>(static_cast<char*>(workspace) + lo);
+  float* stats = reinterpret_cast<float*>(static_cast<char*>(workspace) + so);
+  auto pa = partition_args(p, pl, q, L_K, L_V, B_K, scales, seq_lens, workspace);
+  pa.imp = importance;
+  pa.logits = logits;
+  pa.imp_thr = ad->threshold;
+  pa.low_rank = ad->low_rank;
+  if (lrattn::launch_adaptive(p->latent_dtype, p->rank, group_of(p), pa, s) != hipSuccess)
+    return LRATTN_ERR_HIP;
+  auto ca = combine_args(p, pl, B_V, seq_lens, out, workspace);
+  ca.stats = stats;
+  if (lrattn::launch_combine(group_of(p), ca, s) != hipSuccess) return LRATTN_ERR_HIP;
+  lrattn::ImportanceArgs ia;
+  ia.logits = logits; ia.stats = stats; ia.imp = importance; ia.seq_lens = seq_lens;
+  ia.B = p->batch; ia.Hq = p->num_q_heads; ia.Hkv = p->num_kv_heads; ia.T = p->max_seq_len;
+  ia.decay = ad->decay;
+  if (lrattn::launch_importance(ia, s) != hipSuccess) return LRATTN_ERR_HIP;
   return LRATTN_OK;
 }
 

@@ -51,6 +51,9 @@ struct PartitionArgs {
   int32_t HG;              // head groups (grid y): query heads hg * G .. + G - 1
   int32_t hps;             // query heads per latent stream: group hg reads stream hg * G / hps
   int32_t P, S;            // partitions, tokens per partition
+  int32_t xcd_group;       // 1: one-dimensional grid, head groups of a tile on one XCD
+  int32_t q_dtype, f_dtype;
+  float qscale;            // softmax_scale * log2(e)
   // token window and record slots of this launch: partition p covers tokens
   // [t_lo + p S, t_lo + (p + 1) S) clipped to min(seq_len, t_hi) and writes
   // record slot p_off + p of P_rec per head (defaults 0, T, 0, P)
@@ -60,9 +63,13 @@ struct PartitionArgs {
   // n_img in parts of S with BK1 (record slots unchanged)
   const void* BK1;
   int32_t n_img, P_img, S_img;
-  int32_t xcd_group;       // 1: one-dimensional grid, head groups of a tile on one XCD
-  int32_t q_dtype, f_dtype;
-  float qscale;            // softmax_scale * log2(e)
+  // attention-aware rank (adaptive kernels only): token t of (b, g) keeps
+  // latent coordinates [0, low_rank) when imp[b, g, t] < imp_thr, all r
+  // otherwise; base-2 logits go to logits [B, Hq, T]
+  const float* imp;
+  float* logits;
+  float imp_thr;
+  int32_t low_rank;
 };
 
 struct CombineArgs {
@@ -77,8 +84,26 @@ struct CombineArgs {
   // S_img, records [P_img, P) the rest in parts of S (BV1 null: one set)
   const void* BV1;
   int32_t n_img, P_img, S_img;
+  float* stats;             // [B, Hq, 2]: final (max, denominator) per row, or nullptr
 };
 
+// Attention-aware rank: the importance update after the step (one thread
+// per token; grid ceil(T / 256) x Hkv x B).
+struct ImportanceArgs {
+  const float* logits;      // [B, Hq, T] base-2 logits of the step
+  const float* stats;       // [B, Hq, 2] final (max, denominator) per row
+  float* imp;               // [B, Hkv, T] updated in place for t < seq_len
+  const int32_t* seq_lens;  // [B]
+  int32_t B, Hq, Hkv, T;
+  float decay;
+};
+hipError_t launch_importance(const ImportanceArgs& a, hipStream_t s);
+
+// Attention-aware rank: true when the adaptive partition kernel is compiled
+// for (latent dtype, rank, group); launch_adaptive launches it (grid P, HG, B).
+bool adaptive_supported(int latent_dtype, int rank, int group);
+hipError_t launch_adaptive(int latent_dtype, int rank, int group, const PartitionArgs& a,
+                           hipStream_t s);
 // True when the combine has a two-factor-set (image, text) form for (d, r).
 bool modal_supported(int head_dim, int rank);
 // True when a partition kernel is compiled for (latent dtype, rank, group).

@@ -257,12 +257,14 @@ struct Step {
   uint32_t v[Geo<LT, R, G>::kU][Geo<LT, R, G>::kWords];
   float sk[Geo<LT, R, G>::kU];
   float sv[Geo<LT, R, G>::kU];
+  float imp[Geo<LT, R, G>::kU];  // adaptive rank: the rows' importance scores
 };
 
-template <class LT, int R, int G, int kAux = LRATTN_LOAD_AUX>
+template <class LT, int R, int G, int kAux = LRATTN_LOAD_AUX, bool kAd = false>
 __device__ __forceinline__ void load_step(Step<LT, R, G>& st, int cb, int slot, uint32_t lane_off,
                                           __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                          __amdgpu_buffer_rsrc_t rsk, __amdgpu_buffer_rsrc_t rsv) {
+                                          __amdgpu_buffer_rsrc_t rsk, __amdgpu_buffer_rsrc_t rsv,
+                                          __amdgpu_buffer_rsrc_t rimp) {
   using Gm = Geo<LT, R, G>;
   constexpr int U = Gm::kU, RPW = Gm::kRPW;
 #pragma unroll
@@ -279,7 +281,23 @@ __device__ __forceinline__ void load_step(Step<LT, R, G>& st, int cb, int slot, 
       st.sv[u] = bload4f(rsv, so);
     }
   }
+  if constexpr (kAd) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) st.imp[u] = bload4f(rimp, (uint32_t)(cb + u * RPW + slot) * 4u);
+  }
 }
+
+// Attention-aware rank (AttentionPack page, section 2.B): a row whose
+// importance is below the threshold keeps latent coordinates [0, low_rank);
+// this lane's elements e >= keep are then zero (keep = low_rank - its first
+// column, clamped to [0, EPL]).
+struct AdaptiveRow {
+  float thr;
+  int keep;
+  float* lg;     // logits of the partition's tokens, head 0 (stride T per head)
+  int T;
+  bool writer;   // the row's first lane writes its logits
+};
 
 // q~ of this lane's columns: registers, or (kQtInLds) LDS rows of stride R.
 template <class LT, int R, int G>
@@ -293,10 +311,11 @@ struct QtView {
   }
 };
 
-template <class LT, int R, int G, bool kMask>
+template <class LT, int R, int G, bool kMask, bool kAd = false>
 __device__ __forceinline__ void compute_step(
     const Step<LT, R, G>& st, int cb, int ntok, int slot, const QtView<LT, R, G>& qt,
-    float (&m)[G], float (&l)[G], float (&acc)[G][Geo<LT, R, G>::kEPL]) {
+    float (&m)[G], float (&l)[G], float (&acc)[G][Geo<LT, R, G>::kEPL],
+    const AdaptiveRow& ad = {}) {
   using Gm = Geo<LT, R, G>;
   constexpr int EPL = Gm::kEPL, U = Gm::kU, RPW = Gm::kRPW;
   constexpr bool kInt8 = std::is_same<LT, LatI8>::value;
@@ -307,6 +326,11 @@ __device__ __forceinline__ void compute_step(
   for (int u = 0; u < U; ++u) {
     float x[EPL];
     Unpack<LT>::run(st.k[u], x);
+    if constexpr (kAd) {
+      const bool low = st.imp[u] < ad.thr;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x[e] = (low && e >= ad.keep) ? 0.f : x[e];
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float t = 0.f;
@@ -314,6 +338,10 @@ __device__ __forceinline__ void compute_step(
       for (int e = 0; e < EPL; ++e) t = fmaf(qt.at(h, e), x[e], t);
       t = group_sum<Gm::kLPR>(t);
       if constexpr (kInt8) t *= st.sk[u];
+      if constexpr (kAd) {
+        const int row = cb + u * RPW + slot;
+        if (ad.writer && row < ntok) ad.lg[(size_t)h * ad.T + row] = t;
+      }
       if constexpr (kMask) {
         if (cb + u * RPW + slot >= ntok) t = -INFINITY;
       }
@@ -365,6 +393,11 @@ __device__ __forceinline__ void compute_step(
   for (int u = 0; u < U; ++u) {
     float x[EPL];
     Unpack<LT>::run(st.v[u], x);
+    if constexpr (kAd) {
+      const bool low = st.imp[u] < ad.thr;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x[e] = (low && e >= ad.keep) ? 0.f : x[e];
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -378,7 +411,6 @@ __device__ __forceinline__ void compute_step(
 // the rest cover the text from n_img in parts of S with BK1, writing record
 // slots P_img + .. .  Uniform per workgroup.
 __device__ __forceinline__ void modal_segment(PartitionArgs& a, int& p) {
-  if (a.BK1 == nullptr) return;
   if (p < a.P_img) {
     a.t_hi = a.n_img;
     a.S = a.S_img;
@@ -397,8 +429,9 @@ __device__ __forceinline__ void modal_segment(PartitionArgs& a, int& p) {
 // close in time, and the tile's latents (read by every head group of a shared
 // stream) are fetched from HBM once and then served by that XCD's L2.
 // Returns false for the padding workgroups of the last round of tiles.
+template <bool kSeg = false>
 __device__ __forceinline__ bool tile_of(const PartitionArgs& a, int& p, int& hg, int& b) {
-  if (a.BK1 != nullptr) {
+  if constexpr (kSeg) {
     // two factor sets: grid (HG, B, P), partitions slowest, so the short
     // image partitions are dispatched first, one per CU, and the text
     // partitions then spread evenly over all CUs
@@ -791,12 +824,15 @@ struct PartLds {
 // Merges the kWaves per-wave partials (fixed order) and writes one record
 // per query head of the group: acc[0..R), m, l.  red_acc [wave][h][R],
 // red_m and red_l [wave][h] are in LDS; the caller has synchronized.
-template <int R, int G>
+template <int R, int G, bool kSeg = false>
 __device__ __forceinline__ void write_records(const PartitionArgs& a, int b, int hg, int p,
                                               const float* red_acc, const float* red_m,
                                               const float* red_l) {
   const int tid = threadIdx.x;
-  float* const rec0 = a.ws + ((size_t)b * a.Hq + (size_t)hg * G) * (size_t)a.P_rec * (R + kRecPad);
+  // record slots: p of P, or (two factor sets) p_off + p of P_rec
+  const int nrec = kSeg ? a.P_rec : a.P;
+  if constexpr (kSeg) p += a.p_off;
+  float* const rec0 = a.ws + ((size_t)b * a.Hq + (size_t)hg * G) * (size_t)nrec * (R + kRecPad);
   for (int it = tid; it < G * R; it += kThreads) {
     const int h = it / R, j = it - h * R;
     float M = red_m[h];
@@ -809,7 +845,7 @@ __device__ __forceinline__ void write_records(const PartitionArgs& a, int b, int
       sacc = fmaf(f, red_acc[(w * G + h) * R + j], sacc);
       L = fmaf(f, red_l[w * G + h], L);
     }
-    float* rec = rec0 + ((size_t)h * a.P_rec + a.p_off + p) * (R + kRecPad);
+    float* rec = rec0 + ((size_t)h * nrec + p) * (R + kRecPad);
     rec[j] = sacc;
     if (j == 0) {
       rec[R] = M;
@@ -818,7 +854,7 @@ __device__ __forceinline__ void write_records(const PartitionArgs& a, int b, int
   }
 }
 
-template <class LT, int R, int G, int kAux = LRATTN_LOAD_AUX>
+template <class LT, int R, int G, int kAux = LRATTN_LOAD_AUX, bool kAd = false, bool kSeg = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Geo<LT, R, G>::kWavesPerEU)))
 void partition_kernel(PartitionArgs a) {
@@ -828,15 +864,15 @@ void partition_kernel(PartitionArgs a) {
 
   // head group hg (its G query heads) reads latent stream g
   int p, hg, b;
-  if (!tile_of(a, p, hg, b)) return;
-  modal_segment(a, p);
+  if (!tile_of<kSeg>(a, p, hg, b)) return;
+  if constexpr (kSeg) modal_segment(a, p);
   const int g = hg * G / a.hps;
   // seq_lens[b] is one value for the whole workgroup; keeping it in a scalar
   // register keeps the buffer descriptors below scalar (a descriptor the
   // compiler must treat as per-lane costs a readfirstlane loop per load)
   const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
-  const int t0 = a.t_lo + p * a.S;
-  const int t1 = min(t0 + a.S, min(len, a.t_hi));
+  const int t0 = (kSeg ? a.t_lo : 0) + p * a.S;
+  const int t1 = min(t0 + a.S, kSeg ? min(len, a.t_hi) : len);
   if (t0 >= t1) return;  // partition past the sequence: nothing to write
   const int ntok = t1 - t0;
 
@@ -860,12 +896,23 @@ void partition_kernel(PartitionArgs a) {
     rsv = make_rsrc(a.scales + plane + row0, (uint32_t)ntok * 4u);
   }
   const uint32_t lane_off = colact ? (uint32_t)(slot * Gm::kRowBytes + cc * Gm::kVec) : kOffNone;
+  // attention-aware rank: the partition's importance scores and logits
+  __amdgpu_buffer_rsrc_t rimp = rk;
+  AdaptiveRow ad{};
+  if constexpr (kAd) {
+    rimp = make_rsrc(a.imp + row0, (uint32_t)ntok * 4u);
+    ad.thr = a.imp_thr;
+    ad.keep = min(max(a.low_rank - cc * EPL, 0), EPL);
+    ad.lg = a.logits + ((size_t)b * a.Hq + (size_t)hg * G) * (size_t)a.T + (size_t)t0;
+    ad.T = a.T;
+    ad.writer = cc == 0;
+  }
 
   // q and B_K are requested first, then the first step's latents; the
   // absorption then runs while the latents are in flight.
   Step<LT, R, G> cur;
   prologue<R, G, LRATTN_LATENTS_AFTER>(a, b, hg, g, q_lds, qt_lds, [&]() {
-    load_step<LT, R, G, kAux>(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv);
+    load_step<LT, R, G, kAux, kAd>(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv, rimp);
   });
 
   QtView<LT, R, G> qt;
@@ -893,16 +940,16 @@ void partition_kernel(PartitionArgs a) {
     if constexpr (LRATTN_PREFETCH) {
       // double buffering: step i+1 is in flight while step i computes; past
       // the partition the loads return zero without touching memory
-      load_step<LT, R, G, kAux>(nxt, cb + kWaves * CH, slot, lane_off, rk, rv, rsk, rsv);
+      load_step<LT, R, G, kAux, kAd>(nxt, cb + kWaves * CH, slot, lane_off, rk, rv, rsk, rsv, rimp);
     }
     if (cb + CH <= ntok)
-      compute_step<LT, R, G, false>(cur, cb, ntok, slot, qt, m, l, acc);
+      compute_step<LT, R, G, false, kAd>(cur, cb, ntok, slot, qt, m, l, acc, ad);
     else
-      compute_step<LT, R, G, true>(cur, cb, ntok, slot, qt, m, l, acc);
+      compute_step<LT, R, G, true, kAd>(cur, cb, ntok, slot, qt, m, l, acc, ad);
     if constexpr (LRATTN_PREFETCH) {
       cur = nxt;
     } else {
-      load_step<LT, R, G, kAux>(cur, cb + kWaves * CH, slot, lane_off, rk, rv, rsk, rsv);
+      load_step<LT, R, G, kAux, kAd>(cur, cb + kWaves * CH, slot, lane_off, rk, rv, rsk, rsv, rimp);
     }
   }
 
@@ -940,7 +987,7 @@ void partition_kernel(PartitionArgs a) {
   }
   __syncthreads();
 
-  write_records<R, G>(a, b, hg, p, lds.acc, lds.m, lds.l);
+  write_records<R, G, kSeg>(a, b, hg, p, lds.acc, lds.m, lds.l);
 }
 
 // ------------------------------------------------ partition, matrix-core scores
@@ -1174,7 +1221,7 @@ __device__ __forceinline__ void split3x8(const float (&x)[8], bf16x8 (&t)[3]) {
 // End of a matrix-core partition: the wave's exp-sums over its 16 token
 // lanes, its accumulators over the slots (one reference per head for the
 // whole wave: plain sums), then the fixed-order merge of the waves.
-template <int R, int G, int NT>
+template <int R, int G, int NT, bool kSeg = false>
 __device__ __forceinline__ void mfma_epilogue(const PartitionArgs& a, int b, int hg, int p,
                                               const float (&mm)[4], const float (&ll)[4],
                                               float (&acc)[G][8], PartLds<R, G>& lds) {
@@ -1215,7 +1262,7 @@ __device__ __forceinline__ void mfma_epilogue(const PartitionArgs& a, int b, int
     }
   }
   __syncthreads();
-  write_records<R, G>(a, b, hg, p, lds.acc, lds.m, lds.l);
+  write_records<R, G, kSeg>(a, b, hg, p, lds.acc, lds.m, lds.l);
 }
 
 template <int R, int G>
@@ -1224,7 +1271,7 @@ struct MPartLds {
   float w[kWaves * MGeo<R, G>::kChunk * G];
 };
 
-template <int R, int G, int kAux = LRATTN_LOAD_AUX>
+template <int R, int G, int kAux = LRATTN_LOAD_AUX, bool kSeg = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(MGeo<R, G>::kWavesPerEU)))
 void partition_mfma_kernel(PartitionArgs a) {
@@ -1233,12 +1280,12 @@ void partition_mfma_kernel(PartitionArgs a) {
 
   // head group hg (its G query heads) reads latent stream g
   int p, hg, b;
-  if (!tile_of(a, p, hg, b)) return;
-  modal_segment(a, p);
+  if (!tile_of<kSeg>(a, p, hg, b)) return;
+  if constexpr (kSeg) modal_segment(a, p);
   const int g = hg * G / a.hps;
   const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
-  const int t0 = a.t_lo + p * a.S;
-  const int t1 = min(t0 + a.S, min(len, a.t_hi));
+  const int t0 = (kSeg ? a.t_lo : 0) + p * a.S;
+  const int t1 = min(t0 + a.S, kSeg ? min(len, a.t_hi) : len);
   if (t0 >= t1) return;  // partition past the sequence: nothing to write
   const int ntok = t1 - t0;
 
@@ -1299,7 +1346,7 @@ void partition_mfma_kernel(PartitionArgs a) {
     else load_mstep<R, G, Mg::kNT, kAux>(cur, cb + kWaves * CH, koff, voff, rk, rv);
   }
 
-  mfma_epilogue<R, G, Mg::kNT>(a, b, hg, p, mm, ll, acc, lds.base);
+  mfma_epilogue<R, G, Mg::kNT, kSeg>(a, b, hg, p, mm, ll, acc, lds.base);
 }
 
 // --------------------------------------- partition, rebuilt (and rotated) keys
@@ -1870,6 +1917,12 @@ void combine_kernel(CombineArgs a) {
     }
     sm.vt[tid] = np > 0 ? acc[0] / L : 0.f;
     if constexpr (kModal) vt1[kNPG * R + tid] = np > 0 ? acc[1] / L : 0.f;
+    // the row's final reference and denominator (attention weights of the
+    // step: 2^(logit - m) / L)
+    if (a.stats != nullptr && tid == 0) {
+      a.stats[((size_t)b * a.Hq + hq) * 2] = m;
+      a.stats[((size_t)b * a.Hq + hq) * 2 + 1] = L;
+    }
   }
   __syncthreads();
 
@@ -1959,9 +2012,31 @@ constexpr bool mfma_scores(int latent_dtype, int rank, int group) {
 // 8 heads (the shared-stream groups; smaller groups keep the default).
 template <class LT, int R>
 hipError_t launch_pg(int group, const PartitionArgs& a, hipStream_t s) {
-  const dim3 grid = a.BK1 ? dim3(a.HG, a.B, a.P)
-                  : a.xcd_group ? dim3(8 * a.HG * ((a.P * a.B + 7) / 8)) : dim3(a.P, a.HG, a.B);
   const dim3 block(kThreads);
+  if (a.BK1 != nullptr) {
+    // two factor sets: grid (HG, B, P), see tile_of
+    const dim3 grid(a.HG, a.B, a.P);
+    constexpr int X = LRATTN_LOAD_AUX;
+    if constexpr (mfma_scores(std::is_same<LT, LatBF16>::value ? LRATTN_BF16 : -1, R, 4)) {
+      if (group == 4) {
+        hipLaunchKernelGGL((partition_mfma_kernel<R, 4, X, true>), grid, block, 0, s, a);
+        return hipGetLastError();
+      }
+      if (group == 8) {
+        hipLaunchKernelGGL((partition_mfma_kernel<R, 8, X, true>), grid, block, 0, s, a);
+        return hipGetLastError();
+      }
+    }
+    switch (group) {
+      case 1: hipLaunchKernelGGL((partition_kernel<LT, R, 1, X, false, true>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((partition_kernel<LT, R, 2, X, false, true>), grid, block, 0, s, a); break;
+      case 4: hipLaunchKernelGGL((partition_kernel<LT, R, 4, X, false, true>), grid, block, 0, s, a); break;
+      case 8: hipLaunchKernelGGL((partition_kernel<LT, R, 8, X, false, true>), grid, block, 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  const dim3 grid = a.xcd_group ? dim3(8 * a.HG * ((a.P * a.B + 7) / 8)) : dim3(a.P, a.HG, a.B);
   const bool keep = a.xcd_group != 0;
   if constexpr (mfma_scores(std::is_same<LT, LatBF16>::value ? LRATTN_BF16 : -1, R, 4)) {
     if (group == 4) {
@@ -2003,6 +2078,21 @@ hipError_t launch_pr(int rank, int group, const PartitionArgs& a, hipStream_t s)
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
+}
+
+// Attention-aware rank: the VALU partition kernel with per-row rank masks
+// and logits output, for the shapes of adaptive_supported.
+template <class LT, int R>
+hipError_t launch_ag(int group, const PartitionArgs& a, hipStream_t s) {
+  const dim3 grid(a.P, a.HG, a.B), block(kThreads);
+  switch (group) {
+    case 1: hipLaunchKernelGGL((partition_kernel<LT, R, 1, LRATTN_LOAD_AUX, true>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((partition_kernel<LT, R, 2, LRATTN_LOAD_AUX, true>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((partition_kernel<LT, R, 4, LRATTN_LOAD_AUX, true>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((partition_kernel<LT, R, 8, LRATTN_LOAD_AUX, true>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <int R, int D>
@@ -2088,6 +2178,28 @@ hipError_t launch_partition(int latent_dtype, int rank, int group, const Partiti
     case LRATTN_F16: return launch_pr<LatF16>(rank, group, a, s);
     case LRATTN_I8: return launch_pr<LatI8>(rank, group, a, s);
     default: return hipErrorInvalidValue;
+  }
+}
+
+bool adaptive_supported(int latent_dtype, int rank, int group) {
+  const bool g = group == 1 || group == 2 || group == 4 || group == 8;
+  switch (latent_dtype) {
+    case LRATTN_F32: return rank == 16 && group == 1;
+    case LRATTN_BF16: return (rank == 32 || rank == 48 || rank == 64) && g;
+    case LRATTN_I8: return rank == 32 && (group == 1 || group == 4);
+    default: return false;
+  }
+}
+
+hipError_t launch_adaptive(int latent_dtype, int rank, int group, const PartitionArgs& a,
+                           hipStream_t s) {
+  if (!adaptive_supported(latent_dtype, rank, group)) return hipErrorInvalidValue;
+  if (latent_dtype == LRATTN_F32) return launch_ag<LatF32, 16>(1, a, s);
+  if (latent_dtype == LRATTN_I8) return launch_ag<LatI8, 32>(group, a, s);
+  switch (rank) {
+    case 32: return launch_ag<LatBF16, 32>(group, a, s);
+    case 48: return launch_ag<LatBF16, 48>(group, a, s);
+    default: return launch_ag<LatBF16, 64>(group, a, s);
   }
 }
 

@@ -311,3 +311,28 @@ def test_modal_plan_records():
         want = -(-nic // S) + -(-(1000 - nic) // S)
         assert lr.modal_workspace_size(p, ni) == rec(want), ni
 
+
+def test_adaptive_decode_validates_on_host():
+    L = lr.lib()
+    def call(p, ad=None, q=ALIGNED, lk=ALIGNED, lv=ALIGNED, bk=ALIGNED, bv=ALIGNED, sc=None,
+             seq=ALIGNED, imp=ALIGNED, out=ALIGNED, ws=ALIGNED, ws_bytes=0):
+        ad = ad or lr.AdaptiveParams(16, 0.5, 0.9)
+        return L.lrattn_adaptive_decode(ctypes.byref(p), ctypes.byref(ad), q, lk, lv, bk, bv,
+                                        sc, seq, imp, out, ws, ws_bytes, None)
+    p = params()                                       # bf16, d 128, r 64, G 4
+    assert call(params(latent_dtype=lr.F16)) == -4     # bf16, int8 (r 32), fp32 (r 16)
+    assert call(params(rank=128)) == -4
+    assert call(p, ad=lr.AdaptiveParams(0, 0.5, 0.9)) == -2       # low_rank in [1, r]
+    assert call(p, ad=lr.AdaptiveParams(65, 0.5, 0.9)) == -2
+    assert call(p, ad=lr.AdaptiveParams(8, 0.5, 1.5)) == -2       # decay in [0, 1]
+    assert call(p, ad=lr.AdaptiveParams(8, float("nan"), 0.5)) == -2
+    assert call(p, imp=None) == -1
+    assert call(p, imp=MISALIGNED) == -5
+    assert call(p, ws=None) == -6
+    ad = lr.AdaptiveParams(16, 0.5, 0.9)
+    need = lr.adaptive_workspace_size(p, ad)
+    assert call(p, ad=ad, ws_bytes=need - 1) == -6
+    rec = lr.workspace_size(p)
+    lg = (p.batch * p.num_q_heads * p.max_seq_len * 4 + 255) // 256 * 256
+    assert need == rec + lg + 256          # records, logits [B, Hq, T], row statistics
+
