@@ -95,7 +95,7 @@ def device_tensors(w, torch, copies):
 
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for name in ("lrattn_kernels.hip", "lrattn_internal.hpp"):
+    for name in ("lrattn_kernels.hip", "lrattn_internal.hpp", "lrattn_device.hpp"):
         with open(os.path.join(ROOT, "rank_kv_cache_head_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -535,7 +535,7 @@ def shared_latent(w, torch, lr, args, grouped_ms):
     lat = valid * 2 * R * 2
     res = dict(ms_per_step=ms, tokens_per_s=w.batch / (ms / 1e3), rank=R, streams=1,
                latent_bytes_per_step=lat, latent_GBps=lat / (ms / 1e3) / 1e9,
-               head_groups=Hq // 8, vs_grouped=ms / grouped_ms)
+               heads_per_pass=32 if Hq % 32 == 0 else 8, vs_grouped=ms / grouped_ms)
     del LK, LV
     torch.cuda.empty_cache()
     return res

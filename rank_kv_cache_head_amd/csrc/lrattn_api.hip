@@ -9,6 +9,7 @@
 #include "lrattn.h"
 #include "lrattn_append.hpp"
 #include "lrattn_internal.hpp"
+#include "lrattn_shared.hpp"
 #include "lrattn_probe.h"
 
 namespace {
@@ -521,13 +522,38 @@ int shared_group(const lrattn_params* p) {
   return 1;
 }
 
-int check_shared(const lrattn_params* p, lrattn_params* grouped, Plan* pl) {
+// One pass per stream (bf16 latents, r in {32, 64, 128}, heads per stream a
+// multiple of 32): each workgroup reads a tile once for 32 heads, so the
+// default plan splits T into enough partitions for the grid (partitions x
+// streams x 32-head groups x sequences) to give every CU about one
+// workgroups, in whole 64-token steps.  An explicit num_splits is used as
+// given.  *once tells whether that kernel runs.
+constexpr int64_t kOnceBlocks = 256;
+
+int check_shared(const lrattn_params* p, lrattn_params* grouped, Plan* pl, bool* once = nullptr) {
   if (!p) return LRATTN_ERR_NULL;
   if (p->num_kv_heads <= 0 || p->num_q_heads <= 0 || p->num_q_heads % p->num_kv_heads)
     return LRATTN_ERR_SHAPE;
   *grouped = *p;
   grouped->num_kv_heads = p->num_q_heads / shared_group(p);  // one "kv-head" per group
-  return check_params(grouped, pl);
+  const int st = check_params(grouped, pl);
+  if (st != LRATTN_OK) return st;
+  const int nh = p->num_q_heads / p->num_kv_heads;
+  const bool one = lrattn::shared_once_supported(p->latent_dtype, p->rank, nh);
+  if (once) *once = one;
+  if (one && p->num_splits == 0) {
+    const int64_t T = p->max_seq_len;
+    const int64_t cells = (int64_t)p->batch * p->num_kv_heads * (nh / 32);
+    const int64_t want = (kOnceBlocks + cells - 1) / cells;
+    int64_t S = (T + want - 1) / want;
+    S = (S + 63) / 64 * 64;
+    if (S > T) S = T;
+    pl->S = (int32_t)S;
+    pl->P = (int32_t)((T + S - 1) / S);
+    if (checked_mul({p->batch, p->num_q_heads, pl->P, p->rank + kRecPad, 4}) < 0)
+      return LRATTN_ERR_SHAPE;
+  }
+  return LRATTN_OK;
 }
 
 size_t shared_ws_bytes(const lrattn_params* p, const Plan& pl) {
@@ -605,7 +631,8 @@ int lrattn_shared_decode(const lrattn_params* p, const void* q, const void* L_K,
                          size_t workspace_bytes, lrattn_stream stream) {
   lrattn_params gp;
   Plan pl;
-  int st = check_shared(p, &gp, &pl);
+  bool once = false;
+  int st = check_shared(p, &gp, &pl, &once);
   if (st == LRATTN_OK) st = check_partition_ptrs(p, q, L_K, L_V, B_K, scales, seq_lens);
   if (st == LRATTN_OK) st = check_combine_ptrs(B_V, seq_lens, out);
   if (st == LRATTN_OK && !workspace) st = LRATTN_ERR_WORKSPACE;
@@ -622,6 +649,18 @@ int lrattn_shared_decode(const lrattn_params* p, const void* q, const void* L_K,
   ab.B = p->batch; ab.Hq = p->num_q_heads; ab.d = p->head_dim; ab.r = p->rank;
   ab.q_dtype = p->q_dtype; ab.f_dtype = p->factor_dtype; ab.qscale = qscale_for(p);
   if (lrattn::launch_absorb_heads(ab, s) != hipSuccess) return LRATTN_ERR_HIP;
+  if (once) {
+    lrattn::SharedOnceArgs oa;
+    oa.qt = qt; oa.LK = L_K; oa.LV = L_V; oa.seq_lens = seq_lens;
+    oa.ws = static_cast<float*>(workspace);
+    oa.B = p->batch; oa.Hq = p->num_q_heads; oa.S = p->num_kv_heads; oa.T = p->max_seq_len;
+    oa.P = pl.P; oa.Stok = pl.S;
+    if (lrattn::launch_shared_once(p->rank, oa, s) != hipSuccess) return LRATTN_ERR_HIP;
+    auto ca = combine_args(p, pl, B_V, seq_lens, out, workspace);
+    ca.factor_per_head = 1;
+    if (lrattn::launch_combine(G, ca, s) != hipSuccess) return LRATTN_ERR_HIP;
+    return LRATTN_OK;
+  }
   auto pa = partition_args(p, pl, q, L_K, L_V, B_K, scales, seq_lens, workspace);
   pa.qt_pre = qt;
   pa.HG = p->num_q_heads / G;                    // head groups

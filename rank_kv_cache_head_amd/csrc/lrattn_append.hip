@@ -25,22 +25,12 @@
 
 #include "lrattn.h"
 #include "lrattn_append.hpp"
+#include "lrattn_device.hpp"
 
 namespace lrattn {
 namespace {
 
 constexpr int kThreads = 256, kWaves = 4;
-constexpr uint32_t kOffNone = 0x80000000u;  // past any resource: loads zero
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
 
 template <int R, int RB, bool kF16>
 __global__ __launch_bounds__(kThreads) void append_partial_kernel(AppendArgs a) {

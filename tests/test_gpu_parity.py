@@ -387,11 +387,15 @@ def test_rebuild_full_size_rotated():
 
 @pytest.mark.parametrize("lt,S,Hq,r,d", [("bf16", 1, 32, 64, 128), ("bf16", 1, 12, 48, 128),
                                          ("f16", 2, 16, 32, 64), ("i8", 1, 40, 32, 128),
-                                         ("f32", 1, 8, 16, 64), ("bf16", 3, 3, 32, 128)])
+                                         ("f32", 1, 8, 16, 64), ("bf16", 3, 3, 32, 128),
+                                         # one pass for 32 heads (bf16, r 32/64/128)
+                                         ("bf16", 1, 32, 128, 128), ("bf16", 2, 64, 32, 64),
+                                         ("bf16", 1, 64, 64, 128)])
 def test_shared_decode_matches_oracle(lt, S, Hq, r, d):
     """Shared latent streams (AttentionPack's multi-head compression) with a
-    factor block per query head: q~ per head, partitions over head groups of
-    up to 8 reading the same stream, combine with each head's B_V."""
+    factor block per query head: q~ per head, then partitions over head
+    groups of up to 8 reading the same stream, or (bf16, 32 heads per
+    stream) one pass per tile for 32 heads; combine with each head's B_V."""
     import torch
     import rank_kv_cache_head_amd as lr
     base = "int8" if lt == "i8" else "gqa_vlm"
