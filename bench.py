@@ -380,8 +380,15 @@ def rebuilt_keys(w, torch, lr, args, base, sets, absorbed_ms):
             decs[i % n]()
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) / args.steps * 1e3
+        # per step: the latent rows read (HBM) and the rebuild's matrix-core
+        # work, 2 r d flops per valid (token, kv-head)
+        lat = w.algorithmic_bytes()["latents"]
+        units = int(w.seq_lens.sum()) * w.num_kv_heads
         res[name] = dict(ms_per_step=ms, tokens_per_s=w.batch / (ms / 1e3),
-                         vs_absorbed=ms / absorbed_ms)
+                         vs_absorbed=ms / absorbed_ms,
+                         latent_GBps=lat / (ms / 1e3) / 1e9,
+                         frac_of_8TBps=lat / (ms / 1e3) / 8e12,
+                         rebuild_TFLOPs=2.0 * w.rank * w.head_dim * units / (ms / 1e3) / 1e12)
     res["kernel"] = "partition_rebuild_kernel"
     res["num_splits"], res["split_tokens"] = lr.rebuild_plan(decs[0].params)
     return res
@@ -461,8 +468,10 @@ def adaptive_rank(w, torch, lr, args, base, sets, plain_ms):
     # added traffic per valid token: importance read (partition), logits
     # written and read, importance read and written (update)
     extra = valid * (w.num_kv_heads * 4 + 2 * w.num_q_heads * 4 + w.num_kv_heads * 8)
+    moved = w.algorithmic_bytes()["total"] + extra
     return dict(ms_per_step=ms, tokens_per_s=w.batch / (ms / 1e3), low_rank=w.rank // 2,
                 vs_plain=ms / plain_ms, added_bytes_per_step=extra,
+                step_GBps=moved / (ms / 1e3) / 1e9, frac_of_8TBps=moved / (ms / 1e3) / 8e12,
                 kernel="partition_kernel (adaptive) + combine + importance_kernel")
 
 
@@ -495,8 +504,10 @@ def modal_factors(w, torch, lr, args, base, sets, one_set_ms):
         decs[i % n]()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / args.steps * 1e3
+    moved = w.algorithmic_bytes()["total"] + BK.nbytes // 2 + BV.nbytes // 2
     return dict(ms_per_step=ms, tokens_per_s=w.batch / (ms / 1e3), image_tokens=ni,
                 vs_one_set=ms / one_set_ms,
+                step_GBps=moved / (ms / 1e3) / 1e9, frac_of_8TBps=moved / (ms / 1e3) / 8e12,
                 records=lr.modal_workspace_size(decs[0].params, ni))
 
 
@@ -535,6 +546,7 @@ def shared_latent(w, torch, lr, args, grouped_ms):
     lat = valid * 2 * R * 2
     res = dict(ms_per_step=ms, tokens_per_s=w.batch / (ms / 1e3), rank=R, streams=1,
                latent_bytes_per_step=lat, latent_GBps=lat / (ms / 1e3) / 1e9,
+               frac_of_8TBps=lat / (ms / 1e3) / 8e12,
                heads_per_pass=32 if Hq % 32 == 0 else 8, vs_grouped=ms / grouped_ms)
     del LK, LV
     torch.cuda.empty_cache()

@@ -427,6 +427,36 @@ def test_shared_decode_matches_oracle(lt, S, Hq, r, d):
         assert err <= 2e-5, err
 
 
+def test_shared_one_pass_edges():
+    """The one-pass shared kernel (32 heads per stream): an empty sequence
+    gives a zero row, NaN padding past each length is never read, and the
+    result repeats bit for bit."""
+    import torch
+    import rank_kv_cache_head_amd as lr
+    kw = dict(B=3, Hq=32, Hkv=32, d=128, r=64, T=600, seq_lens=[600, 0, 77],
+              factor_std=0.125)
+    wz = workloads.make("gqa_vlm", seed=1300, pad="zero", **kw)
+    wn = workloads.make("gqa_vlm", seed=1300, pad="nan", **kw)
+    outs = []
+    for w in (wz, wn, wz):
+        dev = to_device(w)
+        say("shared one pass edges")
+        o = lr.shared_decode(dev["q"], dev["L_K"][:, :1].contiguous(),
+                             dev["L_V"][:, :1].contiguous(), dev["B_K"], dev["B_V"],
+                             dev["seq_lens"])
+        torch.cuda.synchronize()
+        outs.append(o.cpu().numpy())
+    assert np.isfinite(outs[1]).all()
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    assert (outs[0][1] == 0).all()
+    f = oracle.as_float64
+    sel = [0, 2]
+    ref = oracle.decode_shared(f(wz.q[sel], wz.q_dtype), f(wz.L_K[sel], wz.latent_dtype)[:, :1],
+                               f(wz.L_V[sel], wz.latent_dtype)[:, :1], f(wz.B_K, wz.factor_dtype),
+                               f(wz.B_V, wz.factor_dtype), wz.seq_lens[sel])
+    assert rel_rowmax(outs[0][sel], ref) <= 2e-5
+
+
 def test_shared_equals_per_head_cache():
     """A stream shared by G heads gives the result of a per-head cache that
     repeats the stream's latents for each head (same factors)."""
