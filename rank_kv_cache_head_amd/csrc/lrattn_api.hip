@@ -522,8 +522,8 @@ int shared_group(const lrattn_params* p) {
   return 1;
 }
 
-// One pass per stream (bf16 latents, r in {32, 64, 128}, heads per stream a
-// multiple of 32): each workgroup reads a tile once for 32 heads, so the
+// One pass per stream (bf16 latents, r in {32, 64, 128}, at least 32 heads
+// per stream): each workgroup reads a tile once for up to 32 heads, so the
 // default plan splits T into enough partitions for the grid (partitions x
 // streams x 32-head groups x sequences) to give every CU about one
 // workgroups, in whole 64-token steps.  An explicit num_splits is used as
@@ -543,7 +543,7 @@ int check_shared(const lrattn_params* p, lrattn_params* grouped, Plan* pl, bool*
   if (once) *once = one;
   if (one && p->num_splits == 0) {
     const int64_t T = p->max_seq_len;
-    const int64_t cells = (int64_t)p->batch * p->num_kv_heads * (nh / 32);
+    const int64_t cells = (int64_t)p->batch * p->num_kv_heads * ((nh + 31) / 32);
     const int64_t want = (kOnceBlocks + cells - 1) / cells;
     int64_t S = (T + want - 1) / want;
     S = (S + 63) / 64 * 64;

@@ -1642,8 +1642,8 @@ void partition_rebuild_kernel(PartitionArgs a) {
 // The kernel is latency-bound, so its loads are issued together, before
 // anything waits, as raw buffer loads bounded by their slices with no branch
 // around any of them (a load past a slice returns zero):
-//   1. each thread loads its slice of B_V[g] (column i = tid % d, row block
-//      jb = tid / d of NB = kThreads / d blocks) and its share of the first
+//   1. each thread loads its pieces of B_V[g] (16 bytes each: a column
+//      chunk of every NG-th row, ProjTile below) and its share of the first
 //      chunk of the head's records (16 bytes per load) -- speculatively, as
 //      the records past seq_len's last partition are never folded;
 //   2. the chunk is staged in LDS (further chunks: one round trip each);
@@ -1651,8 +1651,8 @@ void partition_rebuild_kernel(PartitionArgs a) {
 //      in ascending order (online log-sum-exp rule; NPG = kThreads / r
 //      groups shorten the chain), then the NPG groups are folded in
 //      ascending order: v~ = acc / l;
-//   4. thread (jb, i) forms the row-block partial of v~ . B_V[g][:, i] and
-//      the NB partials are added in ascending order.
+//   4. thread (rg, c) forms the partial of its column chunk over its rows
+//      and the NG partials of each column are added in ascending order.
 // Every order is fixed, so results are bitwise reproducible.
 
 template <int R>
@@ -1665,7 +1665,55 @@ struct CombineLds {
   float l[kNPG * R];
   float v[kNPG * R];
   float vt[R];
-  float part[kThreads];  // [jb][i], NB * d == kThreads
+};
+
+// The projection out[i] = sum_j v~[j] B_V[g][j][i] in 16-byte pieces of B_V
+// (ES bytes per element: EPP = 16 / ES columns a piece): thread (rg, c)
+// takes column chunk c of rows rg, rg + NG, ... (each set), so a wave's
+// loads cover whole consecutive rows; the NG partials of a column are added
+// in ascending rg.  Rows past r load zeros (buffer bounds) and are skipped.
+template <int R, int D, int ES, int NSET>
+struct ProjTile {
+  static constexpr int kEPP = 16 / ES;              // columns per piece
+  static constexpr int kCPR = D / kEPP;             // pieces per row
+  static constexpr int kNG = kThreads / kCPR;       // row groups
+  static constexpr int kRPT = (R + kNG - 1) / kNG;  // rows per thread (a set)
+  static constexpr int kTP = kRPT * NSET;           // pieces per thread
+  static constexpr int kPB = kTP < 16 ? kTP : 16;   // pieces per batch in flight
+  static_assert(kCPR * kNG == kThreads && kTP % kPB == 0, "projection tiling");
+
+  __device__ static void load(const __amdgpu_buffer_rsrc_t (&rbv)[NSET], int tid, int bt,
+                              u32x4 (&bw)[kPB]) {
+    const int c = tid % kCPR, rg = tid / kCPR;
+#pragma unroll
+    for (int q = 0; q < kPB; ++q) {
+      const int qq = bt * kPB + q, st = qq / kRPT, row = rg + kNG * (qq % kRPT);
+      bw[q] = __builtin_amdgcn_raw_buffer_load_b128(rbv[st], row * D * ES + c * 16, 0, 0);
+    }
+  }
+
+  __device__ static void fma(const float* const (&vts)[2], int tid, int bt,
+                             const u32x4 (&bw)[kPB], int fdt, float (&o)[kEPP]) {
+    const int rg = tid / kCPR;
+#pragma unroll
+    for (int q = 0; q < kPB; ++q) {
+      const int qq = bt * kPB + q, st = qq / kRPT, row = rg + kNG * (qq % kRPT);
+      if (row < R) {
+        const float v = vts[st][row];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t w = bw[q][k];
+          if constexpr (ES == 4) {
+            o[k] = fmaf(v, __uint_as_float(w), o[k]);
+          } else {
+            const bool bf = fdt == LRATTN_BF16;
+            o[2 * k] = fmaf(v, bf ? bf16_lo(w) : f16_lo(w), o[2 * k]);
+            o[2 * k + 1] = fmaf(v, bf ? bf16_hi(w) : f16_hi(w), o[2 * k + 1]);
+          }
+        }
+      }
+    }
+  }
 };
 
 // 16-byte loads of records [p0, p0 + n) of one head into this thread's
@@ -1688,27 +1736,25 @@ __device__ __forceinline__ void load_chunk(const float* rec0, int p0, int n,
 // section 2.A compresses the modalities apart): the records of each set fold
 // into their own latent-space sum under the common running max and
 // denominator, and out = (acc_img . B_V_img[g] + acc_txt . B_V_txt[g]) / L.
-template <int R, int D, bool kModal>
+template <int R, int D, bool kModal, int ES>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void combine_kernel(CombineArgs a) {
   using CL = CombineLds<R>;
   constexpr int RS = R + kRecPad;
   constexpr int kNPG = CL::kNPG, kChunk = CL::kChunk;
   constexpr int kPer = CL::kStage / 4 / kThreads;
-  constexpr int NB = kThreads / D, RB = R / NB;
   constexpr int NSET = kModal ? 2 : 1;
-  static_assert(NB * D == kThreads && RB * NB == R, "combine tiling");
+  using PT = ProjTile<R, D, ES, NSET>;
+  static_assert(PT::kNG * D <= CL::kStage, "projection partials fit the stage");
   const int hq = blockIdx.x, b = blockIdx.y;
   // B_V block: per kv-head, or per query head (shared latent streams)
   const int g = a.factor_per_head ? hq : hq / (a.Hq / a.Hkv);
   const int tid = threadIdx.x;
   const MergeArgs& mg = a.merge;
 
-  // 1. B_V[g] rows [jb * RB, (jb + 1) * RB) of column i: the 32-bit word
-  //    holding each element (2-byte formats: the element's half of it)
-  const int i_col = tid % D, jb = tid / D;
+  // 1. B_V[g] pieces of this thread (PT::load): 16-byte pieces, column
+  //    chunk c of rows rg, rg + NG, ...
   const int fdt = mg.f_dtype;
-  const uint32_t fes = fdt == LRATTN_F32 ? 4u : 2u;
   // dense cache (no B_V, r == d): an empty resource, every load returns zero
   const bool dense = mg.BV == nullptr;
   __amdgpu_buffer_rsrc_t rbv[NSET];
@@ -1716,26 +1762,11 @@ void combine_kernel(CombineArgs a) {
   for (int st = 0; st < NSET; ++st) {
     const void* bv = st == 0 ? mg.BV : a.BV1;
     rbv[st] = dense ? make_rsrc(nullptr, 0u)
-                    : make_rsrc(static_cast<const char*>(bv) + (size_t)g * R * D * fes,
-                                (uint32_t)(R * D) * fes);
+                    : make_rsrc(static_cast<const char*>(bv) + (size_t)g * R * D * ES,
+                                (uint32_t)(R * D * ES));
   }
-  // at most 64 words in flight per thread (r = 128 with d = 256 takes four
-  // batches of 32, the later ones loaded at the projection; two sets take
-  // one batch of up to 32 each, else batches of 16)
-  constexpr int kB = !kModal ? (RB <= 64 ? RB : 32) : (RB <= 32 ? RB : 16);
-  static_assert(RB % kB == 0, "projection batches");
-  uint32_t bw[NSET][kB];
-  auto load_bv = [&](int k0) {
-#pragma unroll
-    for (int st = 0; st < NSET; ++st) {
-#pragma unroll
-      for (int k = 0; k < kB; ++k) {
-        const uint32_t off = (uint32_t)((jb * RB + k0 + k) * D + i_col) * fes;
-        bw[st][k] = __builtin_amdgcn_raw_buffer_load_b32(rbv[st], (int)(off & ~3u), 0, 0);
-      }
-    }
-  };
-  load_bv(0);
+  u32x4 bw[PT::kPB];
+  PT::load(rbv, tid, 0, bw);
   const float* rec0 = a.ws + ((size_t)b * a.Hq + hq) * (size_t)a.P * RS;
   float4 v4[kPer];
   load_chunk<R>(rec0, 0, min(kChunk, a.P), v4);
@@ -1825,33 +1856,33 @@ void combine_kernel(CombineArgs a) {
   }
   __syncthreads();
 
-  // 4. row-block partial of out[i] = sum_j v~[j] * B_V[g][j][i] (each set)
-  const bool odd = i_col & 1;
-  float o = 0.f;
+  // 4. partial of out[c EPP .. + EPP) over the thread's rows (each set), in
+  //    the stage (free after the fold): part[rg][column]
+  float* part = reinterpret_cast<float*>(sm.stage);
+  {
+    const float* vts[2] = {sm.vt, kModal ? vt1 + kNPG * R : sm.vt};
+    float o[PT::kEPP];
 #pragma unroll
-  for (int k0 = 0; k0 < RB; k0 += kB) {
-    if (k0 > 0) {
-      __syncthreads();  // a scheduling boundary: the batches never overlap in registers
-      load_bv(k0);
-    }
+    for (int e = 0; e < PT::kEPP; ++e) o[e] = 0.f;
 #pragma unroll
-    for (int st = 0; st < NSET; ++st) {
-      const float* vt = st == 0 ? sm.vt : vt1 + kNPG * R;
-#pragma unroll
-      for (int k = 0; k < kB; ++k) {
-        const uint32_t w = bw[st][k];
-        const float two = fdt == LRATTN_BF16 ? (odd ? bf16_hi(w) : bf16_lo(w))
-                                             : (odd ? f16_hi(w) : f16_lo(w));
-        o = fmaf(vt[jb * RB + k0 + k], fdt == LRATTN_F32 ? __uint_as_float(w) : two, o);
+    for (int bt = 0; bt < PT::kTP / PT::kPB; ++bt) {
+      if (bt > 0) {
+        __syncthreads();  // a scheduling boundary: the batches never overlap in registers
+        PT::load(rbv, tid, bt, bw);
       }
+      PT::fma(vts, tid, bt, bw, fdt, o);
     }
+    const int c = tid % PT::kCPR, rg = tid / PT::kCPR;
+#pragma unroll
+    for (int e = 0; e < PT::kEPP; e += 4)
+      *reinterpret_cast<float4*>(part + rg * D + c * PT::kEPP + e) =
+          make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
   }
-  sm.part[jb * D + i_col] = o;
   __syncthreads();
   if (tid < D) {
-    float r = sm.part[tid];
+    float r = part[tid];
 #pragma unroll
-    for (int q = 1; q < NB; ++q) r += sm.part[q * D + tid];
+    for (int q = 1; q < PT::kNG; ++q) r += part[q * D + tid];
     if (dense) r = tid < R ? sm.vt[tid] : 0.f;  // r == d: v~ is the output row
     if (np == 0) r = 0.f;       // attention over no tokens: zero output
     const size_t oi = out_row0 + tid;
@@ -2021,15 +2052,15 @@ hipError_t launch_rg(int group, bool rot, const PartitionArgs& a, hipStream_t s)
   return hipGetLastError();
 }
 
-template <int R>
-hipError_t launch_cg(const CombineArgs& a, hipStream_t s) {
+template <int R, int ES>
+hipError_t launch_cge(const CombineArgs& a, hipStream_t s) {
   const dim3 grid(a.Hq, a.B), block(kThreads);
   // two factor sets: d <= 128 and r <= 64 (modal_supported)
   if (a.BV1 != nullptr) {
     if constexpr (R <= 64) {
       switch (a.d) {
-        case 64: hipLaunchKernelGGL((combine_kernel<R, 64, true>), grid, block, 0, s, a); break;
-        case 128: hipLaunchKernelGGL((combine_kernel<R, 128, true>), grid, block, 0, s, a); break;
+        case 64: hipLaunchKernelGGL((combine_kernel<R, 64, true, ES>), grid, block, 0, s, a); break;
+        case 128: hipLaunchKernelGGL((combine_kernel<R, 128, true, ES>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
       }
       return hipGetLastError();
@@ -2037,12 +2068,18 @@ hipError_t launch_cg(const CombineArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   }
   switch (a.d) {
-    case 64: hipLaunchKernelGGL((combine_kernel<R, 64, false>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((combine_kernel<R, 128, false>), grid, block, 0, s, a); break;
-    case 256: hipLaunchKernelGGL((combine_kernel<R, 256, false>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((combine_kernel<R, 64, false, ES>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((combine_kernel<R, 128, false, ES>), grid, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((combine_kernel<R, 256, false, ES>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// factor element size: 4 bytes (fp32) or 2 (bf16, fp16)
+template <int R>
+hipError_t launch_cg(const CombineArgs& a, hipStream_t s) {
+  return a.merge.f_dtype == LRATTN_F32 ? launch_cge<R, 4>(a, s) : launch_cge<R, 2>(a, s);
 }
 
 }  // namespace

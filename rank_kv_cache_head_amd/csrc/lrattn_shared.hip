@@ -10,7 +10,7 @@
 //
 // Grid (Hq, sequence blocks of 8); thread (coordinate j, block row s) forms
 // q~ for sequences s, s + 256 / r, ... of the block: the factor row B_K[h][j]
-// is streamed once per thread in 8-element pieces and reused across those
+// is streamed once per thread, 256 bytes per round, and reused across those
 // sequences; the query rows sit in LDS.  Every product is exact in fp32 and
 // the sums run over i in increasing order.
 #include <float.h>
@@ -23,67 +23,126 @@
 namespace lrattn {
 namespace {
 
-__device__ __forceinline__ float elem(const void* p, size_t i, int dt) {
-  if (dt == LRATTN_F32) return static_cast<const float*>(p)[i];
-  const uint32_t h = static_cast<const uint16_t*>(p)[i];
-  if (dt == LRATTN_BF16) return __uint_as_float(h << 16);
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+constexpr int kAbsorbPieces = 16;  // 16-byte pieces of a factor row per round
+
+// The elements of one 16-byte piece as fp32 (4 for fp32, 8 for 16-bit types).
+template <int DT>
+__device__ __forceinline__ void unpack_piece(const u32x4& w, float (&f)[DT == LRATTN_F32 ? 4 : 8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if constexpr (DT == LRATTN_F32) {
+      f[k] = __uint_as_float(w[k]);
+    } else if constexpr (DT == LRATTN_BF16) {
+      f[2 * k] = __uint_as_float(w[k] << 16);
+      f[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    } else {
+      f[2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] & 0xffffu));
+      f[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] >> 16));
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void stage_q_piece(const u32x4& w, float* dst) {
+  float f[DT == LRATTN_F32 ? 4 : 8];
+  unpack_piece<DT>(w, f);
+#pragma unroll
+  for (int e = 0; e < (DT == LRATTN_F32 ? 4 : 8); ++e) dst[e] = f[e];
+}
+
+// Every load is issued before anything waits: the first round of the
+// factor row, then the block's query rows (16-byte pieces, at most two per
+// thread), so the kernel costs about one memory round trip.  Query rows
+// past the batch load zeros (buffer bounds); pieces past a factor row are
+// loaded (the next row, or zeros past the block) and never used.
+template <int R, int FT>
+__device__ __forceinline__ void absorb_body(const AbsorbHeadsArgs& a) {
+  constexpr int SB = 8;                      // sequences per workgroup
+  constexpr int TPJ = kThreads / R;          // threads per latent coordinate
+  constexpr int KPT = (SB + TPJ - 1) / TPJ;  // sequences per thread
+  constexpr int ES = FT == LRATTN_F32 ? 4 : 2;
+  constexpr int EPP = 16 / ES;  // factor elements per piece
+  const int h = blockIdx.x, b0 = blockIdx.y * SB;
+  const int tid = threadIdx.x, j = tid % R, s0 = tid / R;
+  const int d = a.d, npieces = d / EPP;
+  // the head's factor block (a wave-uniform resource); row j at j d ES bytes
+  const auto rb = make_rsrc(static_cast<const char*>(a.BK) + (size_t)h * R * d * ES,
+                            (uint32_t)(R * d * ES));
+  u32x4 w[kAbsorbPieces];
+  auto load_round = [&](int r0) {
+#pragma unroll
+    for (int k = 0; k < kAbsorbPieces; ++k)
+      w[k] = __builtin_amdgcn_raw_buffer_load_b128(
+          rb, j * d * ES + (r0 * kAbsorbPieces + k) * 16, 0, 0);
+  };
+  load_round(0);
+
+  __shared__ float qs[SB][kMaxHeadDim];
+  {
+    const int qes = a.q_dtype == LRATTN_F32 ? 4 : 2;
+    const int qpr = d * qes / 16;  // pieces per query row
+    const int nb = min(SB, a.B - b0);
+    const uint32_t qrow = (uint32_t)a.Hq * d * qes;  // bytes between sequences
+    const auto rq = make_rsrc(static_cast<const char*>(a.q) + ((size_t)b0 * a.Hq + h) * d * qes,
+                              (uint32_t)(nb - 1) * qrow + (uint32_t)(d * qes));
+    u32x4 qw[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = tid + k * kThreads, sq = e / qpr, c = e - sq * qpr;
+      const uint32_t off = sq < nb ? (uint32_t)sq * qrow + (uint32_t)c * 16u : kOffNone;
+      qw[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)off, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = tid + k * kThreads, sq = e / qpr, c = e - sq * qpr;
+      if (sq < SB) {
+        if (a.q_dtype == LRATTN_F32) stage_q_piece<LRATTN_F32>(qw[k], &qs[sq][4 * c]);
+        else if (a.q_dtype == LRATTN_BF16) stage_q_piece<LRATTN_BF16>(qw[k], &qs[sq][8 * c]);
+        else stage_q_piece<LRATTN_F16>(qw[k], &qs[sq][8 * c]);
+      }
+    }
+  }
+  __syncthreads();
+  if (s0 >= TPJ) return;  // r = 48: 16 threads without a coordinate
+
+  // acc[m] = sum_i qs[s0 + m TPJ][i] * B_K[h][j][i], i in increasing order
+  float acc[KPT];
+#pragma unroll
+  for (int m = 0; m < KPT; ++m) acc[m] = 0.f;
+  for (int r0 = 0; r0 * kAbsorbPieces < npieces; ++r0) {
+    if (r0 > 0) {
+      load_round(r0);
+      __builtin_amdgcn_sched_barrier(0);  // the round's loads ahead of its arithmetic
+    }
+#pragma unroll
+    for (int k = 0; k < kAbsorbPieces; ++k) {
+      const int pc = r0 * kAbsorbPieces + k;
+      if (pc < npieces) {
+        float f[EPP];
+        unpack_piece<FT>(w[k], f);
+#pragma unroll
+        for (int m = 0; m < KPT; ++m) {
+          const int sq = s0 + m * TPJ;
+          if (sq < SB) {
+#pragma unroll
+            for (int e = 0; e < EPP; ++e) acc[m] = fmaf(qs[sq][pc * EPP + e], f[e], acc[m]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < KPT; ++m) {
+    const int sq = s0 + m * TPJ, b = b0 + sq;
+    if (sq < SB && b < a.B) a.qt[((size_t)b * a.Hq + h) * R + j] = acc[m] * a.qscale;
+  }
 }
 
 template <int R>
 __global__ __launch_bounds__(kThreads) void absorb_heads_kernel(AbsorbHeadsArgs a) {
-  constexpr int SB = 8;          // sequences per workgroup
-  constexpr int TPJ = kThreads / R;  // threads per latent coordinate
-  constexpr int KPT = (SB + TPJ - 1) / TPJ;  // sequences per thread
-  const int h = blockIdx.x, b0 = blockIdx.y * SB;
-  const int tid = threadIdx.x, j = tid % R, s0 = tid / R;
-  const int d = a.d;
-  __shared__ float qs[SB][kMaxHeadDim];
-  for (int e = tid; e < SB * d; e += kThreads) {
-    const int s = e / d, i = e - s * d, b = b0 + s;
-    qs[s][i] = b < a.B ? elem(a.q, ((size_t)b * a.Hq + h) * d + i, a.q_dtype) : 0.f;
-  }
-  __syncthreads();
-  if (s0 >= TPJ) return;  // r = 48: 16 threads without a coordinate
-  float acc[KPT];
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) acc[k] = 0.f;
-  const size_t row = ((size_t)h * R + j) * d;
-  for (int i0 = 0; i0 < d; i0 += 8) {
-    float f[8];
-    if (a.f_dtype == LRATTN_F32) {
-      const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(a.BK) + row + i0);
-      const float4 y =
-          *reinterpret_cast<const float4*>(static_cast<const float*>(a.BK) + row + i0 + 4);
-      f[0] = x.x; f[1] = x.y; f[2] = x.z; f[3] = x.w;
-      f[4] = y.x; f[5] = y.y; f[6] = y.z; f[7] = y.w;
-    } else {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.BK) + row + i0);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (a.f_dtype == LRATTN_BF16) {
-          f[2 * k] = __uint_as_float(w[k] << 16);
-          f[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-        } else {
-          f[2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] & 0xffffu));
-          f[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] >> 16));
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < KPT; ++k) {
-      const int s = s0 + k * TPJ;
-      if (s < SB) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[k] = fmaf(qs[s][i0 + e], f[e], acc[k]);
-      }
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const int s = s0 + k * TPJ, b = b0 + s;
-    if (s < SB && b < a.B) a.qt[((size_t)b * a.Hq + h) * R + j] = acc[k] * a.qscale;
-  }
+  if (a.f_dtype == LRATTN_F32) absorb_body<R, LRATTN_F32>(a);
+  else if (a.f_dtype == LRATTN_BF16) absorb_body<R, LRATTN_BF16>(a);
+  else absorb_body<R, LRATTN_F16>(a);
 }
 
 template <int R>
@@ -113,7 +172,7 @@ hipError_t launch_r(const AbsorbHeadsArgs& a, hipStream_t s) {
 //           ([coordinate][token], two buffers, one barrier per tile), and P
 //           goes through a small LDS tile per wave to the operand layout.
 //
-// Workgroup: one (sequence, stream, group of 32 heads, partition); wave w
+// Workgroup: one (sequence, stream, group of up to 32 heads, partition); wave w
 // takes head block w % 2 (16 heads) and token half w / 2 of every 64-token
 // step; the two halves are merged at the end (fixed order).  Scores and
 // value accumulators share one layout (lane l, register i: head
@@ -140,8 +199,11 @@ struct OnceLds {
   alignas(16) float pw[4][16 * kPStride];                 // per wave: P [head][token]
 };
 
+// Two waves per SIMD: at R = 128 the registers fit 256 without spills and
+// two workgroups' LDS (2 x 79 KB) fit a CU, so a CU can run a second
+// workgroup while the first waits on memory.
 template <int R>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void shared_once_kernel(SharedOnceArgs a) {
   constexpr int KC = R / 32;          // 32-wide steps of r (scores)
   constexpr int NBV = R / 16;         // 16-wide blocks of r (values)
@@ -149,7 +211,7 @@ void shared_once_kernel(SharedOnceArgs a) {
   constexpr int KS = OnceLds<R>::kKStride;
   constexpr int KV = kOnceStep * RowB / 16 / 256;  // 16-byte pieces per thread, tile and K|V
   const int p = blockIdx.x, b = blockIdx.z;
-  const int nh = a.Hq / a.S, hgs = nh / 32;
+  const int nh = a.Hq / a.S, hgs = (nh + 31) / 32;  // the last group may be partial
   const int s = blockIdx.y / hgs, hg = blockIdx.y % hgs;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hb = wave & 1, th = wave >> 1;
@@ -159,6 +221,9 @@ void shared_once_kernel(SharedOnceArgs a) {
   if (t0 >= t1) return;  // partition past the sequence: nothing to write
   const int ntok = t1 - t0;
   const int head0 = s * nh + hg * 32 + 16 * hb;  // first head of this wave's block
+  // heads of the block that exist (a partial last group: q~ rows past them
+  // load zeros, their records are not written)
+  const int nvalid = min(max(nh - hg * 32 - 16 * hb, 0), 16);
 
   __shared__ OnceLds<R> lds;
   const size_t row0 = ((size_t)b * a.S + s) * (size_t)a.T + (size_t)t0;
@@ -201,7 +266,7 @@ void shared_once_kernel(SharedOnceArgs a) {
   Tile ta, tb;
   bf16x8 qa[3][KC];
   {
-    const auto rq = make_rsrc(a.qt + ((size_t)b * a.Hq + head0) * R, 16u * R * 4u);
+    const auto rq = make_rsrc(a.qt + ((size_t)b * a.Hq + head0) * R, (uint32_t)nvalid * R * 4u);
     u32x4 qw[KC][2];
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
@@ -362,6 +427,7 @@ void shared_once_kernel(SharedOnceArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hr = 4 * (lane >> 4) + i;  // head row in the block
+      if (hr >= nvalid) continue;
       const float m1 = mrg_m[hb * 16 + hr], l1 = mrg_l[hb * 16 + hr];
       const float M = fmaxf(mm[i], m1);
       const float f0 = fast_exp2(mm[i] - M), f1 = fast_exp2(m1 - M);
@@ -383,11 +449,11 @@ void shared_once_kernel(SharedOnceArgs a) {
 
 bool shared_once_supported(int latent_dtype, int rank, int heads_per_stream) {
   return latent_dtype == LRATTN_BF16 && (rank == 32 || rank == 64 || rank == 128) &&
-         heads_per_stream % 32 == 0;
+         heads_per_stream >= 32;
 }
 
 hipError_t launch_shared_once(int rank, const SharedOnceArgs& a, hipStream_t s) {
-  const dim3 grid(a.P, a.S * (a.Hq / a.S / 32), a.B), block(256);
+  const dim3 grid(a.P, a.S * ((a.Hq / a.S + 31) / 32), a.B), block(256);
   switch (rank) {
     case 32: hipLaunchKernelGGL(shared_once_kernel<32>, grid, block, 0, s, a); break;
     case 64: hipLaunchKernelGGL(shared_once_kernel<64>, grid, block, 0, s, a); break;

@@ -19,7 +19,7 @@ struct SharedOnceArgs {
 
 // True when the one-pass kernel serves (latent dtype, rank, heads per stream).
 bool shared_once_supported(int latent_dtype, int rank, int heads_per_stream);
-// Grid (P, S * heads per stream / 32, B), 256 threads.
+// Grid (P, S * ceil(heads per stream / 32), B), 256 threads.
 hipError_t launch_shared_once(int rank, const SharedOnceArgs& a, hipStream_t s);
 
 }  // namespace lrattn

@@ -390,12 +390,15 @@ def test_rebuild_full_size_rotated():
                                          ("f32", 1, 8, 16, 64), ("bf16", 3, 3, 32, 128),
                                          # one pass for 32 heads (bf16, r 32/64/128)
                                          ("bf16", 1, 32, 128, 128), ("bf16", 2, 64, 32, 64),
-                                         ("bf16", 1, 64, 64, 128)])
+                                         ("bf16", 1, 64, 64, 128),
+                                         # a partial last group of heads (8, then 18)
+                                         ("bf16", 1, 40, 64, 128), ("bf16", 2, 100, 32, 64)])
 def test_shared_decode_matches_oracle(lt, S, Hq, r, d):
     """Shared latent streams (AttentionPack's multi-head compression) with a
     factor block per query head: q~ per head, then partitions over head
-    groups of up to 8 reading the same stream, or (bf16, 32 heads per
-    stream) one pass per tile for 32 heads; combine with each head's B_V."""
+    groups of up to 8 reading the same stream, or (bf16, at least 32 heads
+    per stream) one pass per tile for up to 32 heads; combine with each
+    head's B_V."""
     import torch
     import rank_kv_cache_head_amd as lr
     base = "int8" if lt == "i8" else "gqa_vlm"
