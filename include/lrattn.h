@@ -287,10 +287,11 @@ int lrattn_rebuild_decode(const lrattn_params* p,
  * Three launches: the partitions (which also write each token's logits),
  * the combine (which also writes each row's final max and denominator), the
  * update.  The workspace (lrattn_adaptive_workspace_size bytes) holds the
- * records, the logits [B, Hq, T] and the row statistics.  Supported: bf16
+ * records, the logits and the row statistics.  Supported: bf16
  * latents with r in {32, 48, 64} and group in {1, 2, 4, 8}; int8 latents
- * with r = 32 and group 1 or 4; fp32 latents with r = 16 and group 1; else
- * LRATTN_ERR_UNSUPPORTED.  Other tensors, dtypes, seq_lens handling,
+ * with r = 32 and group 1 or 4; fp32 latents with r = 16 and group 1; and
+ * group * T * 4 < 2^31 bytes; else LRATTN_ERR_UNSUPPORTED.  Other tensors,
+ * dtypes, seq_lens handling,
  * ownership, errors and determinism as in lrattn_decode.
  */
 typedef struct lrattn_adaptive {

@@ -298,7 +298,7 @@ int lrattn_dense_decode(const lrattn_params* p, const void* q, const void* K, co
 
 namespace {
 // Attention-aware rank: the decode plan's records, then the step's base-2
-// logits [B, Hq, T] and each row's final (max, denominator) [B, Hq, 2], each
+// logits [B, Hkv, T, Hq / Hkv] and each row's final (max, denominator) [B, Hq, 2], each
 // part at a 256-byte boundary.
 int adaptive_check(const lrattn_params* p, const lrattn_adaptive* ad, Plan* pl,
                    size_t* logits_off, size_t* stats_off, size_t* total) {
@@ -311,6 +311,8 @@ int adaptive_check(const lrattn_params* p, const lrattn_adaptive* ad, Plan* pl,
   if (!lrattn::adaptive_supported(p->latent_dtype, p->rank, group_of(p)))
     return LRATTN_ERR_UNSUPPORTED;
   if (checked_mul({p->batch, p->num_q_heads, p->max_seq_len, 4}) < 0) return LRATTN_ERR_SHAPE;
+  // a partition's logits are addressed with 32-bit offsets
+  if ((int64_t)group_of(p) * p->max_seq_len * 4 >= (int64_t(1) << 31)) return LRATTN_ERR_UNSUPPORTED;
   const size_t rec = workspace_bytes_for(p, *pl);
   const size_t lg = ((size_t)p->batch * p->num_q_heads * p->max_seq_len * 4 + 255) & ~(size_t)255;
   *logits_off = rec;

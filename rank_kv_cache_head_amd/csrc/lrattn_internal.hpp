@@ -90,7 +90,7 @@ struct CombineArgs {
 // Attention-aware rank: the importance update after the step (one thread
 // per token; grid ceil(T / 256) x Hkv x B).
 struct ImportanceArgs {
-  const float* logits;      // [B, Hq, T] base-2 logits of the step
+  const float* logits;      // [B, Hkv, T, G] base-2 logits of the step (G = Hq / Hkv)
   const float* stats;       // [B, Hq, 2] final (max, denominator) per row
   float* imp;               // [B, Hkv, T] updated in place for t < seq_len
   const int32_t* seq_lens;  // [B]

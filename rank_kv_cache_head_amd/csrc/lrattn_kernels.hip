@@ -220,9 +220,9 @@ __device__ __forceinline__ void load_step(Step<LT, R, G>& st, int cb, int slot, 
 struct AdaptiveRow {
   float thr;
   int keep;
-  float* lg;     // logits of the partition's tokens, head 0 (stride T per head)
-  int T;
-  bool writer;   // the row's first lane writes its logits
+  int col;       // this lane's place in its row (it stages heads col, col + LPR, ...)
+  float* lds;    // the wave's staging tile [rows per wave per step][G]
+  __amdgpu_buffer_rsrc_t rlg;  // the group's logits [token][G] from the partition start
 };
 
 // q~ of this lane's columns: registers, or (kQtInLds) LDS rows of stride R.
@@ -265,14 +265,33 @@ __device__ __forceinline__ void compute_step(
       t = group_sum<Gm::kLPR>(t);
       if constexpr (kInt8) t *= st.sk[u];
       if constexpr (kAd) {
-        const int row = cb + u * RPW + slot;
-        if (ad.writer && row < ntok) ad.lg[(size_t)h * ad.T + row] = t;
+        if (h % Gm::kLPR == ad.col) ad.lds[(u * RPW + slot) * G + h] = t;
       }
       if constexpr (kMask) {
         if (cb + u * RPW + slot >= ntok) t = -INFINITY;
       }
       s[u][h] = t;
     }
+  }
+  if constexpr (kAd) {
+    // the step's logits leave through the wave's LDS tile in the logits'
+    // token-major layout ([token][head] per head group), so each store
+    // instruction writes 256 contiguous bytes (one 4-byte store per row and
+    // head into [head][token] rows cost ~40 us of the step at gqa_vlm).
+    // Rows past the partition get an offset past the buffer and are
+    // dropped.  LDS accesses of one wave complete in order; the asm keeps
+    // the compiler from moving them across.
+    constexpr int NV = G * Gm::kChunk;
+    const int lane = threadIdx.x & 63;
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < (NV + 63) / 64; ++k) {
+      const int i = min(64 * k + lane, NV - 1), r = i / G;
+      const bool ok = (NV % 64 == 0 || 64 * k + lane < NV) && cb + r < ntok;
+      const uint32_t off = ok ? (uint32_t)(cb * G + i) * 4u : kOffNone;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ad.lds[i]), ad.rlg, (int)off, 0, 0);
+    }
+    __asm__ volatile("" ::: "memory");
   }
 
   // online softmax per slot and head, with a lazily moved reference max: the
@@ -803,6 +822,7 @@ void partition_kernel(PartitionArgs a) {
   const int ntok = t1 - t0;
 
   __shared__ PartLds<R, G> lds;
+  __shared__ float lg_lds[kAd ? kWaves * G * CH : 1];  // adaptive rank: logits staging
   float* q_lds = lds.q;
   float* qt_lds = lds.qt;
 
@@ -829,9 +849,10 @@ void partition_kernel(PartitionArgs a) {
     rimp = make_rsrc(a.imp + row0, (uint32_t)ntok * 4u);
     ad.thr = a.imp_thr;
     ad.keep = min(max(a.low_rank - cc * EPL, 0), EPL);
-    ad.lg = a.logits + ((size_t)b * a.Hq + (size_t)hg * G) * (size_t)a.T + (size_t)t0;
-    ad.T = a.T;
-    ad.writer = cc == 0;
+    ad.col = cc;
+    ad.lds = lg_lds + wave * G * CH;
+    ad.rlg = make_rsrc(a.logits + (((size_t)b * a.HG + hg) * (size_t)a.T + (size_t)t0) * G,
+                       (uint32_t)ntok * G * 4u);
   }
 
   // q and B_K are requested first, then the first step's latents; the
