@@ -547,7 +547,7 @@ def shared_latent(w, torch, lr, args, grouped_ms):
     res = dict(ms_per_step=ms, tokens_per_s=w.batch / (ms / 1e3), rank=R, streams=1,
                latent_bytes_per_step=lat, latent_GBps=lat / (ms / 1e3) / 1e9,
                frac_of_8TBps=lat / (ms / 1e3) / 8e12,
-               heads_per_pass=32 if Hq >= 32 else 8, vs_grouped=ms / grouped_ms)
+               heads_per_pass=min(64, 16 * -(-Hq // 16)) if Hq >= 32 else 8, vs_grouped=ms / grouped_ms)
     del LK, LV
     torch.cuda.empty_cache()
     return res

@@ -525,10 +525,10 @@ int shared_group(const lrattn_params* p) {
 }
 
 // One pass per stream (bf16 latents, r in {32, 64, 128}, at least 32 heads
-// per stream): each workgroup reads a tile once for up to 32 heads, so the
+// per stream): each workgroup reads a tile once for up to 64 heads, so the
 // default plan splits T into enough partitions for the grid (partitions x
-// streams x 32-head groups x sequences) to give every CU about one
-// workgroups, in whole 64-token steps.  An explicit num_splits is used as
+// streams x head groups x sequences) to give every CU about one
+// workgroup, in whole 64-token steps.  An explicit num_splits is used as
 // given.  *once tells whether that kernel runs.
 constexpr int64_t kOnceBlocks = 256;
 
@@ -545,7 +545,8 @@ int check_shared(const lrattn_params* p, lrattn_params* grouped, Plan* pl, bool*
   if (once) *once = one;
   if (one && p->num_splits == 0) {
     const int64_t T = p->max_seq_len;
-    const int64_t cells = (int64_t)p->batch * p->num_kv_heads * ((nh + 31) / 32);
+    const int gh = 16 * lrattn::shared_once_blocks(nh);  // heads per workgroup
+    const int64_t cells = (int64_t)p->batch * p->num_kv_heads * ((nh + gh - 1) / gh);
     const int64_t want = (kOnceBlocks + cells - 1) / cells;
     int64_t S = (T + want - 1) / want;
     S = (S + 63) / 64 * 64;

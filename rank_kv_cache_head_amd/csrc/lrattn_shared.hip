@@ -158,8 +158,8 @@ hipError_t launch_r(const AbsorbHeadsArgs& a, hipStream_t s) {
 // AttentionPack page, section 2.A: all heads read the same compressed rows.
 // Reading them once per head group multiplies the stream's traffic, and the
 // value sums of many heads (heads x r accumulators) are more than the VALU
-// can keep up with.  This kernel reads each tile once for 32 heads and runs
-// both products on the matrix cores:
+// can keep up with.  This kernel reads each tile once for up to 64 heads
+// (NHB blocks of 16) and runs both products on the matrix cores:
 //
 //   scores  S (16 heads x 16 tokens) = q~ . L_K^T with v_mfma_f32_16x16x32_bf16,
 //           q~ split exactly into three bf16 terms (the latents are bf16, so
@@ -172,12 +172,12 @@ hipError_t launch_r(const AbsorbHeadsArgs& a, hipStream_t s) {
 //           ([coordinate][token], two buffers, one barrier per tile), and P
 //           goes through a small LDS tile per wave to the operand layout.
 //
-// Workgroup: one (sequence, stream, group of up to 32 heads, partition); wave w
-// takes head block w % 2 (16 heads) and token half w / 2 of every 64-token
-// step; the two halves are merged at the end (fixed order).  Scores and
-// value accumulators share one layout (lane l, register i: head
-// 4 (l / 16) + i), so the lazily moved softmax reference and its rescale stay
-// within a lane.
+// Workgroup: one (sequence, stream, group of up to 16 NHB heads, partition),
+// 2 NHB waves; wave w takes head block w % NHB (16 heads) and token half
+// w / NHB of every 64-token step; the two halves are merged at the end
+// (fixed order).  Waves 0-3 stage the tiles.  Scores and value accumulators
+// share one layout (lane l, register i: head 4 (l / 16) + i), so the lazily
+// moved softmax reference and its rescale stay within a lane.
 
 namespace {
 
@@ -191,41 +191,45 @@ constexpr int kPStride = 36;             // floats per P row: 32 tokens + pad
 // consecutive rows of one parity of 16) stays one contiguous 16-byte piece.
 __device__ __forceinline__ int vt_swizzle(int row) { return (row & 16); }
 
-template <int R>
+template <int R, int NHB>
 struct OnceLds {
   static constexpr int kKStride = 2 * R + 16;  // bytes per K row: r bf16 + pad
   alignas(16) unsigned char kt[2][kOnceStep * kKStride];  // L_K tiles [token][coordinate]
   alignas(16) unsigned char vt[2][R * kVtStride];         // L_V tiles [coordinate][token]
-  alignas(16) float pw[4][16 * kPStride];                 // per wave: P [head][token]
+  alignas(16) float pw[2 * NHB][16 * kPStride];           // per wave: P [head][token]
+  // the final merge reuses both K buffers: [head block][16 heads][R], m, l
+  static_assert(NHB * 16 * (R + 2) * 4 <= 2 * kOnceStep * kKStride, "merge area");
 };
 
-// Two waves per SIMD: at R = 128 the registers fit 256 without spills and
-// two workgroups' LDS (2 x 79 KB) fit a CU, so a CU can run a second
-// workgroup while the first waits on memory.
-template <int R>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// Two waves per SIMD: at R = 128 the registers fit 256 without spills, and
+// with NHB = 2 two workgroups' LDS (2 x 79 KB) fit a CU, so a CU can run a
+// second workgroup while the first waits on memory.
+template <int R, int NHB>
+__global__ __launch_bounds__(128 * NHB) __attribute__((amdgpu_waves_per_eu(2)))
 void shared_once_kernel(SharedOnceArgs a) {
   constexpr int KC = R / 32;          // 32-wide steps of r (scores)
   constexpr int NBV = R / 16;         // 16-wide blocks of r (values)
   constexpr int RowB = 2 * R;         // bytes per latent row
-  constexpr int KS = OnceLds<R>::kKStride;
+  constexpr int KS = OnceLds<R, NHB>::kKStride;
   constexpr int KV = kOnceStep * RowB / 16 / 256;  // 16-byte pieces per thread, tile and K|V
   const int p = blockIdx.x, b = blockIdx.z;
-  const int nh = a.Hq / a.S, hgs = (nh + 31) / 32;  // the last group may be partial
+  constexpr int GH = 16 * NHB;        // heads per group
+  const int nh = a.Hq / a.S, hgs = (nh + GH - 1) / GH;  // the last group may be partial
   const int s = blockIdx.y / hgs, hg = blockIdx.y % hgs;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hb = wave & 1, th = wave >> 1;
+  const int hb = wave % NHB, th = wave / NHB;
+  const bool stager = NHB == 2 || wave < 4;  // waves 0-3 stage the tiles
   const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
   const int t0 = p * a.Stok;
   const int t1 = min(t0 + a.Stok, len);
   if (t0 >= t1) return;  // partition past the sequence: nothing to write
   const int ntok = t1 - t0;
-  const int head0 = s * nh + hg * 32 + 16 * hb;  // first head of this wave's block
+  const int head0 = s * nh + hg * GH + 16 * hb;  // first head of this wave's block
   // heads of the block that exist (a partial last group: q~ rows past them
   // load zeros, their records are not written)
-  const int nvalid = min(max(nh - hg * 32 - 16 * hb, 0), 16);
+  const int nvalid = min(max(nh - hg * GH - 16 * hb, 0), 16);
 
-  __shared__ OnceLds<R> lds;
+  __shared__ OnceLds<R, NHB> lds;
   const size_t row0 = ((size_t)b * a.S + s) * (size_t)a.T + (size_t)t0;
   const uint32_t nbytes = (uint32_t)ntok * RowB;
   const auto rk = make_rsrc(static_cast<const char*>(a.LK) + row0 * RowB, nbytes);
@@ -235,20 +239,23 @@ void shared_once_kernel(SharedOnceArgs a) {
   // contiguous bytes of 16 rows.  K goes to LDS as it is (rows padded by 16
   // bytes: the score operand reads of 16 rows at one column are
   // conflict-free); V goes transposed (each write puts 16 consecutive tokens
-  // of 4 rows).
-  const int stok = 16 * wave + (lane & 15);
+  // of 4 rows).  Waves past the fourth load nothing (an offset past the
+  // buffer: zeros, no memory access) and write nothing.
+  const int stok = 16 * (wave & 3) + (lane & 15);
+  const uint32_t soff = stager ? (uint32_t)stok * RowB + (lane >> 4) * 16u : kOffNone;
   struct Tile {
     u32x4 k[KV], v[KV];
   };
   auto load_tile = [&](Tile& tl, int cb) {
 #pragma unroll
     for (int k = 0; k < KV; ++k) {
-      const uint32_t off = (uint32_t)(cb + stok) * RowB + ((lane >> 4) + 4 * k) * 16u;
+      const uint32_t off = stager ? soff + (uint32_t)cb * RowB + 64u * k : kOffNone;
       tl.k[k] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)off, 0, 2);
       tl.v[k] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off, 0, 2);
     }
   };
   auto stage_tile = [&](const Tile& tl, int buf) {
+    if (!stager) return;
     uint16_t* vt = reinterpret_cast<uint16_t*>(lds.vt[buf]);
 #pragma unroll
     for (int k = 0; k < KV; ++k) {
@@ -405,8 +412,8 @@ void shared_once_kernel(SharedOnceArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) l[i] = group_sum<16>(ll[i]);
   float* mrg = reinterpret_cast<float*>(lds.kt[0]);  // [hb][16 heads][R], then m, l
-  float* mrg_m = mrg + 2 * 16 * R;
-  float* mrg_l = mrg_m + 2 * 16;
+  float* mrg_m = mrg + NHB * 16 * R;
+  float* mrg_l = mrg_m + NHB * 16;
   if (th == 1) {
 #pragma unroll
     for (int n = 0; n < NBV; ++n) {
@@ -452,15 +459,31 @@ bool shared_once_supported(int latent_dtype, int rank, int heads_per_stream) {
          heads_per_stream >= 32;
 }
 
-hipError_t launch_shared_once(int rank, const SharedOnceArgs& a, hipStream_t s) {
-  const dim3 grid(a.P, a.S * ((a.Hq / a.S + 31) / 32), a.B), block(256);
+int shared_once_blocks(int heads_per_stream) {
+  const int nhb = (heads_per_stream + 15) / 16;
+  return nhb < 2 ? 2 : nhb > 4 ? 4 : nhb;
+}
+
+template <int NHB>
+hipError_t launch_once_nhb(int rank, const SharedOnceArgs& a, hipStream_t s) {
+  const int groups = (a.Hq / a.S + 16 * NHB - 1) / (16 * NHB);
+  const dim3 grid(a.P, a.S * groups, a.B), block(128 * NHB);
   switch (rank) {
-    case 32: hipLaunchKernelGGL(shared_once_kernel<32>, grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL(shared_once_kernel<64>, grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL(shared_once_kernel<128>, grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((shared_once_kernel<32, NHB>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((shared_once_kernel<64, NHB>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((shared_once_kernel<128, NHB>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_shared_once(int rank, const SharedOnceArgs& a, hipStream_t s) {
+  switch (shared_once_blocks(a.Hq / a.S)) {
+    case 2: return launch_once_nhb<2>(rank, a, s);
+    case 3: return launch_once_nhb<3>(rank, a, s);
+    case 4: return launch_once_nhb<4>(rank, a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_absorb_heads(const AbsorbHeadsArgs& a, hipStream_t s) {

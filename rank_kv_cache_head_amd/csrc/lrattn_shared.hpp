@@ -19,7 +19,10 @@ struct SharedOnceArgs {
 
 // True when the one-pass kernel serves (latent dtype, rank, heads per stream).
 bool shared_once_supported(int latent_dtype, int rank, int heads_per_stream);
-// Grid (P, S * ceil(heads per stream / 32), B), 256 threads.
+// Head blocks of 16 per workgroup (2, 3 or 4): each workgroup serves up to
+// 16 * that many heads of its stream.
+int shared_once_blocks(int heads_per_stream);
+// Grid (P, S * ceil(heads per stream / (16 blocks)), B), 128 * blocks threads.
 hipError_t launch_shared_once(int rank, const SharedOnceArgs& a, hipStream_t s);
 
 }  // namespace lrattn

@@ -391,14 +391,16 @@ def test_rebuild_full_size_rotated():
                                          # one pass for 32 heads (bf16, r 32/64/128)
                                          ("bf16", 1, 32, 128, 128), ("bf16", 2, 64, 32, 64),
                                          ("bf16", 1, 64, 64, 128),
-                                         # a partial last group of heads (8, then 18)
-                                         ("bf16", 1, 40, 64, 128), ("bf16", 2, 100, 32, 64)])
+                                         # 3 and 4 blocks of 16 heads per workgroup, full
+                                         # or with a partial last block or group
+                                         ("bf16", 1, 40, 64, 128), ("bf16", 2, 100, 32, 64),
+                                         ("bf16", 1, 48, 128, 128), ("bf16", 1, 80, 128, 64)])
 def test_shared_decode_matches_oracle(lt, S, Hq, r, d):
     """Shared latent streams (AttentionPack's multi-head compression) with a
     factor block per query head: q~ per head, then partitions over head
     groups of up to 8 reading the same stream, or (bf16, at least 32 heads
-    per stream) one pass per tile for up to 32 heads; combine with each
-    head's B_V."""
+    per stream) one pass per tile for up to 64 heads (2, 3 or 4 blocks of
+    16); combine with each head's B_V."""
     import torch
     import rank_kv_cache_head_amd as lr
     base = "int8" if lt == "i8" else "gqa_vlm"
@@ -430,13 +432,14 @@ def test_shared_decode_matches_oracle(lt, S, Hq, r, d):
         assert err <= 2e-5, err
 
 
-def test_shared_one_pass_edges():
-    """The one-pass shared kernel (32 heads per stream): an empty sequence
-    gives a zero row, NaN padding past each length is never read, and the
-    result repeats bit for bit."""
+@pytest.mark.parametrize("Hq", [32, 48])
+def test_shared_one_pass_edges(Hq):
+    """The one-pass shared kernel (32 or 48 heads per stream: 2 or 3 blocks
+    of 16 per workgroup): an empty sequence gives a zero row, NaN padding
+    past each length is never read, and the result repeats bit for bit."""
     import torch
     import rank_kv_cache_head_amd as lr
-    kw = dict(B=3, Hq=32, Hkv=32, d=128, r=64, T=600, seq_lens=[600, 0, 77],
+    kw = dict(B=3, Hq=Hq, Hkv=Hq, d=128, r=64, T=600, seq_lens=[600, 0, 77],
               factor_std=0.125)
     wz = workloads.make("gqa_vlm", seed=1300, pad="zero", **kw)
     wn = workloads.make("gqa_vlm", seed=1300, pad="nan", **kw)
