@@ -367,7 +367,7 @@ int lrattn_modal_decode(const lrattn_params* p,
  * Hq / S any multiple of 1, 2, 4 or 8.  Three launches: q~ for every head,
  * the partitions, the combine.  With bf16 latents, rank 32, 64 or 128 and
  * Hq / S >= 32, each partition workgroup reads its tile of the stream once
- * for up to 32 heads (scores and value sums on the matrix cores, the
+ * for up to 64 heads (scores and value sums on the matrix cores, the
  * weights split into two bf16 terms); otherwise heads run in groups of up to
  * 8 that read the same stream.  The plan (and so the workspace size) depends
  * on which applies; the workspace holds the partial records and q~.
