@@ -185,11 +185,12 @@ constexpr int kOnceStep = 64;            // tokens per step (32 per wave)
 constexpr int kVtStride = 144;           // bytes per transposed V row: 64 tokens + pad
 constexpr int kPStride = 36;             // floats per P row: 32 tokens + pad
 
-// Transposed L_V rows whose index has bit 4 set keep their tokens 16
-// places further (an XOR on whole 8-token chunks): the staging writes of
-// rows 16 apart then fall in different banks, and an operand read (16
-// consecutive rows of one parity of 16) stays one contiguous 16-byte piece.
-__device__ __forceinline__ int vt_swizzle(int row) { return (row & 16); }
+// Transposed L_V row `row` keeps its tokens XOR 8 ((row / 8) % 8) (whole
+// 8-token chunks move): a staging write (16 rows 8 apart, 4 consecutive
+// tokens each) then spreads over the banks instead of hitting one group,
+// and an operand read (8 consecutive tokens of one row) stays one
+// contiguous 16-byte piece.
+__device__ __forceinline__ int vt_swizzle(int row) { return 8 * ((row >> 3) & 7); }
 
 template <int R, int NHB>
 struct OnceLds {
@@ -234,22 +235,23 @@ void shared_once_kernel(SharedOnceArgs a) {
   const uint32_t nbytes = (uint32_t)ntok * RowB;
   const auto rk = make_rsrc(static_cast<const char*>(a.LK) + row0 * RowB, nbytes);
   const auto rv = make_rsrc(static_cast<const char*>(a.LV) + row0 * RowB, nbytes);
-  // Staging: piece k of a thread is token 16 wave + l % 16 of the step,
-  // columns 8 (l / 16 + 4 k) .. + 7: each load instruction reads 64
-  // contiguous bytes of 16 rows.  K goes to LDS as it is (rows padded by 16
-  // bytes: the score operand reads of 16 rows at one column are
-  // conflict-free); V goes transposed (each write puts 16 consecutive tokens
-  // of 4 rows).  Waves past the fourth load nothing (an offset past the
-  // buffer: zeros, no memory access) and write nothing.
-  const int stok = 16 * (wave & 3) + (lane & 15);
-  const uint32_t soff = stager ? (uint32_t)stok * RowB + (lane >> 4) * 16u : kOffNone;
+  // Staging: piece k of thread t (t < 256) is piece 256 k + t of the tile's
+  // 16-byte pieces in memory order (CPR = r / 8 pieces a row), so every load
+  // instruction reads 1 KB of consecutive rows (16 rows x 64 bytes per
+  // instruction streamed 14% slower).  K goes to LDS as it is (rows padded
+  // by 16 bytes: the score operand reads of 16 rows at one column are
+  // conflict-free); V goes transposed (vt_swizzle).  Waves past the fourth
+  // load nothing (an offset past the buffer: zeros, no memory access) and
+  // write nothing.
+  constexpr int CPR = RowB / 16;
+  const uint32_t soff = stager ? (uint32_t)(tid & 255) * 16u : kOffNone;
   struct Tile {
     u32x4 k[KV], v[KV];
   };
   auto load_tile = [&](Tile& tl, int cb) {
 #pragma unroll
     for (int k = 0; k < KV; ++k) {
-      const uint32_t off = stager ? soff + (uint32_t)cb * RowB + 64u * k : kOffNone;
+      const uint32_t off = stager ? soff + (uint32_t)cb * RowB + 4096u * k : kOffNone;
       tl.k[k] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)off, 0, 2);
       tl.v[k] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off, 0, 2);
     }
@@ -259,12 +261,12 @@ void shared_once_kernel(SharedOnceArgs a) {
     uint16_t* vt = reinterpret_cast<uint16_t*>(lds.vt[buf]);
 #pragma unroll
     for (int k = 0; k < KV; ++k) {
-      const int cg = (lane >> 4) + 4 * k, col = 8 * cg;
-      *reinterpret_cast<u32x4*>(lds.kt[buf] + stok * KS + cg * 16) = tl.k[k];
+      const int pc = 256 * k + (tid & 255), tk = pc / CPR, cg = pc % CPR, col = 8 * cg;
+      *reinterpret_cast<u32x4*>(lds.kt[buf] + tk * KS + cg * 16) = tl.k[k];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int row = col + j;
-        vt[row * (kVtStride / 2) + (stok ^ vt_swizzle(row))] = (uint16_t)(tl.v[k][j / 2] >> (16 * (j & 1)));
+        vt[row * (kVtStride / 2) + (tk ^ vt_swizzle(row))] = (uint16_t)(tl.v[k][j / 2] >> (16 * (j & 1)));
       }
     }
   };
