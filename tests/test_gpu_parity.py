@@ -189,6 +189,22 @@ def test_instantiation_matrix(lt, r, G, d):
     assert err <= TOL[lt], err
 
 
+@pytest.mark.parametrize("r,d,fdt", [(128, 256, "f32"), (128, 64, "f32"), (48, 64, "bf16"),
+                                     (16, 64, "f32"), (128, 128, "f16"), (48, 256, "f32")])
+def test_combine_projection_tiles(r, d, fdt):
+    """The combine's projection reads B_V in 16-byte pieces, a column chunk of
+    every NG-th row per thread: bf16 latents with fp32 / fp16 / bf16 factors
+    cover two batches of pieces (r 128, d 256, fp32), a row count that does
+    not fill the last row group (r 48 or 16 with 16 or 32 row groups), and
+    one batch of 16 pieces."""
+    kw = dict(B=2, Hq=2, Hkv=2, d=d, r=r, T=500, seq_lens=[500, 131], latent_dtype="bf16",
+              q_dtype=fdt, factor_dtype=fdt, factor_std=1.0 / np.sqrt(r))
+    w = workloads.make("tiny", seed=700 + r + d, **kw)
+    say(f"combine projection r={r} d={d} factors={fdt}")
+    got = run_decode(w, num_splits=3).cpu().numpy()
+    assert rel_rowmax(got, _full_oracle(w)) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("r,G", [(32, 4), (32, 8), (64, 4), (64, 8), (128, 4), (128, 8)])
 def test_matrix_core_scores_exact_inputs(r, G):
     """bf16 latents with 4 or 8 heads per kv-head are scored on the matrix
