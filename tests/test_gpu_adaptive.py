@@ -60,6 +60,9 @@ CASES = {
     "int8_g4": ("int8", dict(B=2, Hq=8, Hkv=2, T=1100, seq_lens=[1100, 99])),
     "int8_g1": ("int8", dict(B=2, Hq=4, Hkv=4, T=900, seq_lens=[900, 1])),
     "fp32_r16": ("tiny", dict(B=2, T=256, seq_lens=[256, 31])),
+    # two heads per kv-head; T not a multiple of 4 (one token per thread in
+    # the score update)
+    "g2_bf16_odd_T": ("gqa_vlm", dict(B=2, Hq=4, Hkv=2, T=1001, seq_lens=[1001, 250])),
 }
 
 
