@@ -404,6 +404,8 @@ def test_rebuild_full_size_rotated():
 @pytest.mark.parametrize("lt,S,Hq,r,d", [("bf16", 1, 32, 64, 128), ("bf16", 1, 12, 48, 128),
                                          ("f16", 2, 16, 32, 64), ("i8", 1, 40, 32, 128),
                                          ("f32", 1, 8, 16, 64), ("bf16", 3, 3, 32, 128),
+                                         # q~ from factor rows read in two rounds
+                                         ("bf16", 1, 8, 64, 256), ("f32", 1, 4, 32, 128),
                                          # one pass per tile (bf16, r 32/64/128, >= 32 heads)
                                          ("bf16", 1, 32, 128, 128), ("bf16", 2, 64, 32, 64),
                                          ("bf16", 1, 64, 64, 128),
