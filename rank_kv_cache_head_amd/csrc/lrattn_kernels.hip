@@ -979,6 +979,43 @@ struct MStep {
   uint32_t v[NT][MGeo<R, G, NT>::kVU][4];
 };
 
+// Attention-aware rank on the matrix-core kernel (AttentionPack page, section
+// 2.B): the importance scores of the step's rows in both layouts, and this
+// lane's masks.  A row below the threshold keeps latent columns
+// [0, low_rank); keepk[c] and keepv count the kept columns among the 8 this
+// lane holds (score layout, 32-column step c; value layout).
+template <int NT, int VU>
+struct MImp {
+  float k[NT];      // row 16 t + lane % 16 (score layout)
+  float v[NT][VU];  // rows 16 t + slot + RPW u (value layout)
+};
+
+struct MAdaptive {
+  float thr;
+  int keepk[4];
+  int keepv;
+  __amdgpu_buffer_rsrc_t rlg;  // the group's logits [token][G] from the partition start
+};
+
+template <int R, int G, int NT>
+__device__ __forceinline__ void load_mimp(MImp<NT, MGeo<R, G, NT>::kVU>& im, int cb, int lane,
+                                          int slot, __amdgpu_buffer_rsrc_t rimp) {
+  using Mg = MGeo<R, G, NT>;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    im.k[t] = bload4f(rimp, (uint32_t)(cb + 16 * t + (lane & 15)) * 4u);
+#pragma unroll
+    for (int u = 0; u < Mg::kVU; ++u)
+      im.v[t][u] = bload4f(rimp, (uint32_t)(cb + 16 * t + slot + Mg::kRPW * u) * 4u);
+  }
+}
+
+// Latent word holding elements e0 (low half) and e0 + 1 (high half): the
+// elements at or past `keep` become zero.
+__device__ __forceinline__ uint32_t keep_word(uint32_t w, int keep, int e0) {
+  return w & (keep > e0 + 1 ? 0xffffffffu : keep > e0 ? 0x0000ffffu : 0u);
+}
+
 template <int R, int G, int NT, int kAux = LRATTN_LOAD_AUX>
 __device__ __forceinline__ void load_mstep(MStep<R, G, NT>& st, int cb, uint32_t koff,
                                            uint32_t voff, __amdgpu_buffer_rsrc_t rk,
@@ -1001,23 +1038,45 @@ __device__ __forceinline__ void load_mstep(MStep<R, G, NT>& st, int cb, uint32_t
 
 // Scores of the step's tiles: s[t][i] = base-2 logit of token 16 t + l % 16
 // for this lane's head i (rows 4 * (l / 16) + i of the product).
-template <int R, int G, int NT, bool kMask>
+template <int R, int G, int NT, bool kMask, bool kAd = false>
 __device__ __forceinline__ void mfma_scores(const MStep<R, G, NT>& st, int cb, int ntok, int lane,
                                             const bf16x8 (&qa)[3][MGeo<R, G, NT>::kKC],
-                                            float (&s)[NT][4]) {
+                                            float (&s)[NT][4],
+                                            const MImp<NT, MGeo<R, G, NT>::kVU>* im = nullptr,
+                                            const MAdaptive* ad = nullptr) {
   constexpr int KC = MGeo<R, G, NT>::kKC;
   const int tok = lane & 15;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
+    u32x4 kw[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      kw[c] = u32x4{st.k[t][c][0], st.k[t][c][1], st.k[t][c][2], st.k[t][c][3]};
+      if constexpr (kAd) {
+        const bool low = im->k[t] < ad->thr;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kw[c][j] = low ? keep_word(kw[c][j], ad->keepk[c], 2 * j) : kw[c][j];
+      }
+    }
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int term = 2; term >= 0; --term) {  // smallest term first
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const u32x4 kw = {st.k[t][c][0], st.k[t][c][1], st.k[t][c][2], st.k[t][c][3]};
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[term][c], __builtin_bit_cast(bf16x8, kw), d,
-                                                    0, 0, 0);
-      }
+      for (int c = 0; c < KC; ++c)
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[term][c], __builtin_bit_cast(bf16x8, kw[c]),
+                                                    d, 0, 0, 0);
+    }
+    if constexpr (kAd) {
+      // the logits, token-major per head group: lanes 0-15 hold heads 0-3 of
+      // their token, lanes 16-31 heads 4-7 (G = 8); 16 bytes a lane, one
+      // store per tile; rows past the partition are dropped (offset past
+      // the buffer)
+      const int row = cb + 16 * t + tok;
+      const bool writer = lane < (G == 8 ? 32 : 16) && row < ntok;
+      const uint32_t off = writer ? (uint32_t)(row * G + 4 * ((lane >> 4) & 1)) * 4u : kOffNone;
+      const u32x4 v = {__float_as_uint(d[0]), __float_as_uint(d[1]), __float_as_uint(d[2]),
+                       __float_as_uint(d[3])};
+      __builtin_amdgcn_raw_buffer_store_b128(v, ad->rlg, (int)off, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1033,10 +1092,12 @@ __device__ __forceinline__ void mfma_scores(const MStep<R, G, NT>& st, int cb, i
 // latent-space value accumulation in the slot layout.  Lane l's result i is
 // head (4 * (l / 16) + i) % G: with G < 4 results i >= G repeat heads and are
 // not used.
-template <int R, int G, int NT>
+template <int R, int G, int NT, bool kAd = false>
 __device__ __forceinline__ void softmax_values(const float (&s)[NT][4], const MStep<R, G, NT>& st,
                                                int lane, float (&mm)[4], float (&ll)[4],
-                                               float (&acc)[G][8], float* wl) {
+                                               float (&acc)[G][8], float* wl,
+                                               const MImp<NT, MGeo<R, G, NT>::kVU>* im = nullptr,
+                                               const MAdaptive* ad = nullptr) {
   using Mg = MGeo<R, G, NT>;
   constexpr int VU = Mg::kVU, RPW = Mg::kRPW, HL = Mg::kHL;
   const int tok = lane & 15;
@@ -1119,6 +1180,11 @@ __device__ __forceinline__ void softmax_values(const float (&s)[NT][4], const MS
       }
       float x[8];
       Unpack<LatBF16>::run(st.v[t][u], x);
+      if constexpr (kAd) {
+        const bool low = im->v[t][u] < ad->thr;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = (low && j >= ad->keepv) ? 0.f : x[j];
+      }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -1129,13 +1195,14 @@ __device__ __forceinline__ void softmax_values(const float (&s)[NT][4], const MS
   __asm__ volatile("" ::: "memory");
 }
 
-template <int R, int G, bool kMask>
+template <int R, int G, bool kMask, bool kAd = false>
 __device__ __forceinline__ void compute_mstep(
     const MStep<R, G>& st, int cb, int ntok, int lane, const bf16x8 (&qa)[3][MGeo<R, G>::kKC],
-    float (&mm)[4], float (&ll)[4], float (&acc)[G][8], float* wl) {
+    float (&mm)[4], float (&ll)[4], float (&acc)[G][8], float* wl,
+    const MImp<MGeo<R, G>::kNT, MGeo<R, G>::kVU>* im = nullptr, const MAdaptive* ad = nullptr) {
   float s[MGeo<R, G>::kNT][4];
-  mfma_scores<R, G, MGeo<R, G>::kNT, kMask>(st, cb, ntok, lane, qa, s);
-  softmax_values<R, G, MGeo<R, G>::kNT>(s, st, lane, mm, ll, acc, wl);
+  mfma_scores<R, G, MGeo<R, G>::kNT, kMask, kAd>(st, cb, ntok, lane, qa, s, im, ad);
+  softmax_values<R, G, MGeo<R, G>::kNT, kAd>(s, st, lane, mm, ll, acc, wl, im, ad);
 }
 
 // End of a matrix-core partition: the wave's exp-sums over its 16 token
@@ -1191,7 +1258,7 @@ struct MPartLds {
   float w[kWaves * MGeo<R, G>::kChunk * G];
 };
 
-template <int R, int G, int kAux = LRATTN_LOAD_AUX, bool kSeg = false>
+template <int R, int G, int kAux = LRATTN_LOAD_AUX, bool kSeg = false, bool kAd = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(MGeo<R, G>::kWavesPerEU)))
 void partition_mfma_kernel(PartitionArgs a) {
@@ -1221,10 +1288,24 @@ void partition_mfma_kernel(PartitionArgs a) {
   // 64-byte (32-column) step; value layout: slot rows, 16 bytes per lane
   const uint32_t koff = (uint32_t)((lane & 15) * Mg::kRowBytes + (lane >> 4) * 16);
   const uint32_t voff = (uint32_t)(slot * Mg::kRowBytes + cc * 16);
+  // attention-aware rank: the partition's importance scores and logits
+  __amdgpu_buffer_rsrc_t rimp = rk;
+  MAdaptive ad{};
+  if constexpr (kAd) {
+    rimp = make_rsrc(a.imp + row0, (uint32_t)ntok * 4u);
+    ad.thr = a.imp_thr;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) ad.keepk[c] = min(max(a.low_rank - (32 * c + 8 * (lane >> 4)), 0), 8);
+    ad.keepv = min(max(a.low_rank - cc * 8, 0), 8);
+    ad.rlg = make_rsrc(a.logits + (((size_t)b * a.HG + hg) * (size_t)a.T + (size_t)t0) * G,
+                       (uint32_t)ntok * G * 4u);
+  }
 
   MStep<R, G> cur;
+  MImp<Mg::kNT, Mg::kVU> icur;
   prologue<R, G, LRATTN_MFMA_LATENTS_AFTER>(a, b, hg, g, lds.base.q, lds.base.qt, [&]() {
     load_mstep<R, G, Mg::kNT, kAux>(cur, wave * CH, koff, voff, rk, rv);
+    if constexpr (kAd) load_mimp<R, G, Mg::kNT>(icur, wave * CH, lane, slot, rimp);
   });
 
   // A operands: row lane % 16 is head (lane % 16) % G; k-group lane / 16
@@ -1257,13 +1338,22 @@ void partition_mfma_kernel(PartitionArgs a) {
   float* wl = lds.w + wave * CH * G;
   for (int cb = wave * CH; cb < ntok; cb += kWaves * CH) {
     MStep<R, G> nxt;
-    if constexpr (LRATTN_PREFETCH) load_mstep<R, G, Mg::kNT, kAux>(nxt, cb + kWaves * CH, koff, voff, rk, rv);
+    MImp<Mg::kNT, Mg::kVU> inxt;
+    if constexpr (LRATTN_PREFETCH) {
+      load_mstep<R, G, Mg::kNT, kAux>(nxt, cb + kWaves * CH, koff, voff, rk, rv);
+      if constexpr (kAd) load_mimp<R, G, Mg::kNT>(inxt, cb + kWaves * CH, lane, slot, rimp);
+    }
     if (cb + CH <= ntok)
-      compute_mstep<R, G, false>(cur, cb, ntok, lane, qa, mm, ll, acc, wl);
+      compute_mstep<R, G, false, kAd>(cur, cb, ntok, lane, qa, mm, ll, acc, wl, &icur, &ad);
     else
-      compute_mstep<R, G, true>(cur, cb, ntok, lane, qa, mm, ll, acc, wl);
-    if constexpr (LRATTN_PREFETCH) cur = nxt;
-    else load_mstep<R, G, Mg::kNT, kAux>(cur, cb + kWaves * CH, koff, voff, rk, rv);
+      compute_mstep<R, G, true, kAd>(cur, cb, ntok, lane, qa, mm, ll, acc, wl, &icur, &ad);
+    if constexpr (LRATTN_PREFETCH) {
+      cur = nxt;
+      if constexpr (kAd) icur = inxt;
+    } else {
+      load_mstep<R, G, Mg::kNT, kAux>(cur, cb + kWaves * CH, koff, voff, rk, rv);
+      if constexpr (kAd) load_mimp<R, G, Mg::kNT>(icur, cb + kWaves * CH, lane, slot, rimp);
+    }
   }
 
   mfma_epilogue<R, G, Mg::kNT, kSeg>(a, b, hg, p, mm, ll, acc, lds.base);
@@ -2036,6 +2126,19 @@ hipError_t launch_pr(int rank, int group, const PartitionArgs& a, hipStream_t s)
 template <class LT, int R>
 hipError_t launch_ag(int group, const PartitionArgs& a, hipStream_t s) {
   const dim3 grid(a.P, a.HG, a.B), block(kThreads);
+  // bf16 latents with 4 or 8 heads per kv-head and r a multiple of 32: the
+  // matrix-core kernel, as for the plain decode
+  if constexpr (mfma_scores(std::is_same<LT, LatBF16>::value ? LRATTN_BF16 : -1, R, 4)) {
+    constexpr int X = LRATTN_LOAD_AUX;
+    if (group == 4) {
+      hipLaunchKernelGGL((partition_mfma_kernel<R, 4, X, false, true>), grid, block, 0, s, a);
+      return hipGetLastError();
+    }
+    if (group == 8) {
+      hipLaunchKernelGGL((partition_mfma_kernel<R, 8, X, false, true>), grid, block, 0, s, a);
+      return hipGetLastError();
+    }
+  }
   switch (group) {
     case 1: hipLaunchKernelGGL((partition_kernel<LT, R, 1, LRATTN_LOAD_AUX, true>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((partition_kernel<LT, R, 2, LRATTN_LOAD_AUX, true>), grid, block, 0, s, a); break;
