@@ -186,10 +186,10 @@ constexpr int kVtStride = 144;           // bytes per transposed V row: 64 token
 constexpr int kPStride = 36;             // floats per P row: 32 tokens + pad
 
 // Transposed L_V row `row` keeps its tokens XOR 8 ((row / 8) % 8) (whole
-// 8-token chunks move): a staging write (16 rows 8 apart, 4 consecutive
-// tokens each) then spreads over the banks instead of hitting one group,
-// and an operand read (8 consecutive tokens of one row) stays one
-// contiguous 16-byte piece.
+// 8-token chunks move): a staging write (at r = 128, 16 rows 8 apart with 4
+// consecutive tokens each) then spreads over the banks instead of hitting
+// one group, and an operand read (8 consecutive tokens of one row) stays
+// one contiguous 16-byte piece.
 __device__ __forceinline__ int vt_swizzle(int row) { return 8 * ((row >> 3) & 7); }
 
 template <int R, int NHB>
