@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 
 import workloads
-from gpu_helpers import (TOL, f64_args, oracle_rows, rel_rowmax, run_decode, say, to_device)
+from gpu_helpers import (TOL, f64_args, oracle_rows, rel_rowmax, run_decode, say, tensor,
+                         to_device)
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -479,6 +480,36 @@ def test_shared_one_pass_edges(Hq):
                                f(wz.L_V[sel], wz.latent_dtype)[:, :1], f(wz.B_K, wz.factor_dtype),
                                f(wz.B_V, wz.factor_dtype), wz.seq_lens[sel])
     assert rel_rowmax(outs[0][sel], ref) <= 2e-5
+
+
+def test_shared_full_size_gqa_vlm():
+    """The benchmark's shared-stream shape at full size: gqa_vlm's batch,
+    heads and lengths over one stream of R = 128 bf16 latents shared by all
+    32 heads (one pass per tile), each head with its own factor blocks;
+    sequences 0 and 15 against the oracle."""
+    import torch
+    import rank_kv_cache_head_amd as lr
+    w = workloads.make("gqa_vlm", Hkv=1, r=128, factor_std=1.0 / np.sqrt(128))
+    wf = workloads.make("gqa_vlm", seed=1400, B=1, Hkv=w.num_q_heads, r=128, T=16,
+                        seq_lens=[16], factor_std=1.0 / np.sqrt(128))
+    say("shared full gqa_vlm: inputs")
+    dev = to_device(w)
+    BK, BV = tensor(wf.B_K, wf.factor_dtype), tensor(wf.B_V, wf.factor_dtype)
+    say("shared full gqa_vlm: decode")
+    got = lr.shared_decode(dev["q"], dev["L_K"], dev["L_V"], BK, BV, dev["seq_lens"],
+                           softmax_scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    assert np.isfinite(got).all()
+    sel = [0, w.batch - 1]
+    f = oracle.as_float64
+    ref = oracle.decode_shared(f(w.q[sel], w.q_dtype), f(w.L_K[sel], w.latent_dtype),
+                               f(w.L_V[sel], w.latent_dtype), f(wf.B_K, wf.factor_dtype),
+                               f(wf.B_V, wf.factor_dtype), w.seq_lens[sel],
+                               softmax_scale=w.softmax_scale)
+    err = rel_rowmax(got[sel], ref)
+    say(f"  err {err:.3e}")
+    assert err <= 2e-5, err
 
 
 def test_shared_equals_per_head_cache():
