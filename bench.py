@@ -419,13 +419,14 @@ def append_step(w, torch, lr, args):
     p = lr.AppendParams(w.batch, w.num_kv_heads, D, w.rank, T, lr.BF16, lr.BF16,
                         {"f32": lr.F32, "bf16": lr.BF16, "f16": lr.F16, "i8": lr.I8}[w.latent_dtype])
     ws = torch.empty(lr.append_workspace_size(p), dtype=torch.uint8, device="cuda")
+    run = lr.Appender(x, AK, AV, pos, LK, LV, sc, workspace=ws)
     for _ in range(args.warmup):
-        lr.append(x, AK, AV, pos, LK, LV, sc, workspace=ws)
+        run()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
-        lr.append(x, AK, AV, pos, LK, LV, sc, workspace=ws)
+        run()
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / args.steps * 1e3
@@ -433,7 +434,10 @@ def append_step(w, torch, lr, args):
     alg = (AK.nbytes + AV.nbytes + x.nbytes +
            2 * w.batch * w.num_kv_heads * w.rank * esz + (0 if sc is None else 2 * w.batch * w.num_kv_heads * 4))
     return dict(us_per_call=us, model_dim=D, bytes_per_call=alg, GBps=alg / (us / 1e6) / 1e9,
-                kernels="append_partial_kernel + append_finish_kernel")
+                frac_of_8TBps=alg / (us / 1e6) / 8e12,
+                kernels=("append_direct_kernel" if w.latent_dtype != "i8" and
+                         w.num_kv_heads * 2 * (w.rank // 16) >= 192
+                         else "append_partial_kernel + append_finish_kernel"))
 
 
 def adaptive_rank(w, torch, lr, args, base, sets, plain_ms):

@@ -406,10 +406,12 @@ int lrattn_shared_decode(const lrattn_params* p,
  * reproducible); the int8 decision is taken in fp32 on those sums.
  * Supported: r in {16, 32, 48, 64, 128}, 1 <= B <= 64, D a multiple of 128;
  * else LRATTN_ERR_UNSUPPORTED.  All pointers 16-byte aligned.  Only the
- * addressed rows (and scales) are written.  Two launches on `stream` (partial
- * sums over chunks of D into the caller's workspace, then the rows): no
- * allocation, no host synchronization; workspace contents on entry do not
- * matter.
+ * addressed rows (and scales) are written.  On `stream`: float latents with
+ * Hkv * 2 * r / 16 >= 192 take one launch (each workgroup sums all of D for
+ * 16 latent coordinates; the workspace is not touched); otherwise, and for
+ * I8 latents, two launches (partial sums over chunks of D into the caller's
+ * workspace, then the rows and scales).  No allocation, no host
+ * synchronization; workspace contents on entry do not matter.
  */
 typedef struct lrattn_append_params {
   int32_t batch;        /* B: sequences, one new token each */

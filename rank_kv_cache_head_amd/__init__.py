@@ -23,8 +23,15 @@ from typing import Optional, Tuple
 
 __all__ = [
     "LrattnError", "Params", "lib", "library_path", "version", "status_string",
-    "params_for", "plan", "workspace_size", "decode", "partition", "combine",
-    "probe_read", "probe_copy", "probe_sink_floats", "declared_symbols", "Decoder",
+    "params_for", "plan", "workspace_size", "partition_kernel", "decode", "partition",
+    "combine", "Decoder",
+    "dense_params_for", "dense_decode", "DenseDecoder",
+    "rebuild_plan", "rebuild_workspace_size", "rebuild_decode", "RebuildDecoder",
+    "AppendParams", "append_workspace_size", "append", "Appender",
+    "shared_params_for", "shared_workspace_size", "shared_decode",
+    "modal_params_for", "modal_workspace_size", "modal_decode", "ModalDecoder",
+    "AdaptiveParams", "adaptive_workspace_size", "adaptive_decode", "AdaptiveDecoder",
+    "probe_read", "probe_copy", "probe_sink_floats", "declared_symbols",
     "F32", "BF16", "F16", "I8",
 ]
 
@@ -564,6 +571,29 @@ def append(x, A_K, A_V, positions, L_K, L_V, scales=None, *, workspace=None, str
                              _stream(stream))
     _check(st, "lrattn_append")
     return L_K, L_V
+
+
+class Appender:
+    """lrattn_append on fixed buffers: arguments validated and marshalled
+    once, each call passes the same pointers and stream to the library.  The
+    tensors must stay alive and keep their storage while the object is used."""
+
+    def __init__(self, x, A_K, A_V, positions, L_K, L_V, scales=None, *, workspace=None,
+                 stream=None):
+        import torch
+        append(x, A_K, A_V, positions, L_K, L_V, scales, workspace=workspace, stream=stream)
+        p = AppendParams(x.shape[0], A_K.shape[0], x.shape[1], A_K.shape[1], L_K.shape[2],
+                         _dtype_code(x), _dtype_code(A_K), _dtype_code(L_K))
+        if workspace is None:
+            workspace = torch.empty(append_workspace_size(p), dtype=torch.uint8, device=x.device)
+        self.params, self.workspace = p, workspace
+        self._keep = (x, A_K, A_V, positions, L_K, L_V, scales)
+        self._args = (ctypes.byref(p), _ptr(x), _ptr(A_K), _ptr(A_V), _ptr(positions),
+                      _ptr(L_K), _ptr(L_V), _ptr(scales), _ptr(workspace),
+                      workspace.numel() * workspace.element_size(), _stream(stream))
+
+    def __call__(self):
+        _check(lib().lrattn_append(*self._args), "lrattn_append")
 
 
 def partition(q, L_K, L_V, B_K, seq_lens, scales=None, *, workspace=None, softmax_scale=None,

@@ -24,6 +24,8 @@ struct AppendArgs {
 constexpr int kAppendMaxBatch = 64;
 
 bool append_supported(int rank, int batch, int model_dim);
+// True when the one-launch path serves (latent dtype, Hkv, r).
+bool append_direct(int latent_dtype, int hkv, int r);
 // Chunks of D for (Hkv, D): enough workgroups to cover the chip, chunks of at
 // least 128 elements that divide D.
 int append_chunks(int num_kv_heads, int model_dim);

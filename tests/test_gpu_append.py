@@ -124,7 +124,9 @@ def _untouched(got, positions, T, ldt):
 @pytest.mark.parametrize("xdt", ["bf16", "f16"])
 @pytest.mark.parametrize("ldt", ["bf16", "f32", "f16", "i8"])
 @pytest.mark.parametrize("B,Hkv,D,r", [(5, 3, 256, 32), (17, 2, 1024, 64), (1, 4, 128, 16),
-                                       (64, 1, 512, 128), (33, 2, 384, 48)])
+                                       (64, 1, 512, 128), (33, 2, 384, 48),
+                                       # Hkv * 2 * r / 16 >= 192: float latents in one launch
+                                       (9, 48, 512, 64), (64, 24, 256, 128), (3, 40, 640, 48)])
 def test_append_matches_oracle(B, Hkv, D, r, ldt, xdt):
     T = 40
     rng = np.random.default_rng(B + D + r)
