@@ -63,6 +63,9 @@ CASES = {
     # two heads per kv-head; T not a multiple of 4 (one token per thread in
     # the score update)
     "g2_bf16_odd_T": ("gqa_vlm", dict(B=2, Hq=4, Hkv=2, T=1001, seq_lens=[1001, 250])),
+    # the matrix-core kernel's other shapes (8 heads at r = 64, 4 at r = 32)
+    "g8_bf16_r64": ("gqa_vlm", dict(B=2, Hq=16, Hkv=2, T=700, seq_lens=[700, 129])),
+    "g4_bf16_r32": ("gqa_vlm", dict(B=2, Hq=8, Hkv=2, r=32, T=600, seq_lens=[600, 77])),
 }
 
 
