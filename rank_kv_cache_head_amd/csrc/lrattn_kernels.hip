@@ -1258,9 +1258,16 @@ struct MPartLds {
   float w[kWaves * MGeo<R, G>::kChunk * G];
 };
 
+// The adaptive form holds the rows' importance scores and masks besides:
+// with 8 heads that no longer fits three waves per SIMD without spills.
+template <int R, int G, bool kAd>
+constexpr int mfma_waves() {
+  return kAd && G == 8 && MGeo<R, G>::kWavesPerEU > 2 ? 2 : MGeo<R, G>::kWavesPerEU;
+}
+
 template <int R, int G, int kAux = LRATTN_LOAD_AUX, bool kSeg = false, bool kAd = false>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(MGeo<R, G>::kWavesPerEU)))
+__attribute__((amdgpu_waves_per_eu(mfma_waves<R, G, kAd>())))
 void partition_mfma_kernel(PartitionArgs a) {
   using Mg = MGeo<R, G>;
   constexpr int KC = Mg::kKC, LPR = Mg::kLPR, CH = Mg::kChunk;
