@@ -49,24 +49,27 @@ def f64_args(w: workloads.Workload):
     return q, LK, LV, BK, BV, w.seq_lens, sc
 
 
-def oracle_rows(w: workloads.Workload, rows):
-    """Oracle output rows for (b, h) pairs, reading only the needed slices."""
-    out = np.empty((len(rows), w.head_dim))
+def oracle_all_rows(w: workloads.Workload) -> np.ndarray:
+    """The oracle's whole output [B, Hq, d], one (sequence, kv-head) at a time:
+    each step converts only that pair's valid latent rows to float64 and
+    rebuilds K and V once for the group's query heads, so a full-size
+    workload (2 GB of ragged latents) stays within a few hundred MB."""
     q = oracle.as_float64(w.q, w.q_dtype)
     BK = oracle.as_float64(w.B_K, w.factor_dtype)
     BV = oracle.as_float64(w.B_V, w.factor_dtype)
     G = w.group
-    for i, (b, h) in enumerate(rows):
-        g = h // G
+    out = np.empty((w.batch, w.num_q_heads, w.head_dim))
+    for b in range(w.batch):
         n = int(w.seq_lens[b])
-        LK = oracle.as_float64(w.L_K[b:b + 1, g:g + 1, :n], w.latent_dtype)
-        LV = oracle.as_float64(w.L_V[b:b + 1, g:g + 1, :n], w.latent_dtype)
-        sc = None
-        if w.scales is not None:
-            sc = w.scales[:, b:b + 1, g:g + 1, :n].astype(np.float64)
-        out[i] = oracle.decode_rows(q[b:b + 1, h:h + 1], LK, LV, BK[g:g + 1], BV[g:g + 1],
-                                    np.array([n]), [(0, 0)], scales=sc,
-                                    softmax_scale=w.softmax_scale)[0]
+        for g in range(w.num_kv_heads):
+            LK = oracle.as_float64(w.L_K[b:b + 1, g:g + 1, :n], w.latent_dtype)
+            LV = oracle.as_float64(w.L_V[b:b + 1, g:g + 1, :n], w.latent_dtype)
+            sc = None
+            if w.scales is not None:
+                sc = w.scales[:, b:b + 1, g:g + 1, :n].astype(np.float64)
+            out[b, g * G:(g + 1) * G] = oracle.decode_rows(
+                q[b:b + 1, g * G:(g + 1) * G], LK, LV, BK[g:g + 1], BV[g:g + 1], np.array([n]),
+                [(0, h) for h in range(G)], scales=sc, softmax_scale=w.softmax_scale)
     return out
 
 
