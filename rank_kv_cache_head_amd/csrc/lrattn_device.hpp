@@ -47,6 +47,18 @@ __device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 constexpr uint32_t kOffNone = 0x80000000u;  // beyond any buffer: loads zero
 
+// Hand-off of LDS data between the lanes of one wave: after the call, every
+// lane sees the LDS stores the wave's lanes issued before it.  A wave's LDS
+// instructions are performed in issue order, so no wait is needed; the
+// wavefront-scope release/acquire fences and the wave barrier keep the
+// compiler from moving LDS accesses across the point.  (HIP's __syncwarp
+// has the same body.)
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // -------------------------------------------------------------- reductions
 
 template <int CTRL>

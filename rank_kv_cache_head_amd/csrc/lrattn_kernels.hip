@@ -83,52 +83,27 @@ template <> struct Unpack<LatI8> {
 };
 
 // ------------------------------------------------------------ partition
-// Compile-time tuning knobs (ordinary parameters; every setting computes the
-// same result):
-//   LRATTN_UNROLL_SMALL_G  rows per slot per step, 1-2 heads, 2- and 4-byte latents
-//   LRATTN_UNROLL_LARGE_G  rows per slot per step, 4-8 heads
-//   LRATTN_UNROLL_I8       rows per slot per step, 1-2 heads, int8 latents
-//   LRATTN_PREFETCH        1: load step i+1 while step i computes
-//   LRATTN_LOAD_AUX        cache-policy bits of the streaming latent loads;
-//                          2 = non-temporal: each latent byte is used once, so
-//                          it should not displace reusable lines in L2
-#ifndef LRATTN_UNROLL_SMALL_G
-#define LRATTN_UNROLL_SMALL_G 4
-#endif
-#ifndef LRATTN_UNROLL_LARGE_G
-#define LRATTN_UNROLL_LARGE_G 2
-#endif
-#ifndef LRATTN_UNROLL_I8
-#define LRATTN_UNROLL_I8 2
-#endif
-#ifndef LRATTN_PREFETCH
-#define LRATTN_PREFETCH 0
-#endif
-#ifndef LRATTN_LOAD_AUX
-#define LRATTN_LOAD_AUX 2
-#endif
-//   LRATTN_MFMA_SCORES     1: bf16 latents with 4 or 8 heads per kv-head and
-//                          r a multiple of 32 score on the matrix cores
-//   LRATTN_MFMA_TILES      16-token score tiles per wave per step there
-//   LRATTN_LATENTS_AFTER   where the VALU kernel issues its first latent
-//                          loads in the prologue: 0 first, 1 after q is
-//                          staged (the matrix-core absorption: first), 2
-//                          after the absorption (every load the prologue
-//                          waits for is then served ahead of the grid's
-//                          latent stream)
-//   LRATTN_MFMA_LATENTS_AFTER  the same for the matrix-core score kernel
-#ifndef LRATTN_LATENTS_AFTER
-#define LRATTN_LATENTS_AFTER 1
-#endif
-#ifndef LRATTN_MFMA_LATENTS_AFTER
-#define LRATTN_MFMA_LATENTS_AFTER 2
-#endif
-#ifndef LRATTN_MFMA_SCORES
-#define LRATTN_MFMA_SCORES 1
-#endif
-#ifndef LRATTN_MFMA_TILES
-#define LRATTN_MFMA_TILES 2
-#endif
+// Fixed launch-shape choices, each measured on MI355X:
+//   kUnrollSmallG  rows per slot per step, 1-2 heads, 2- and 4-byte latents
+//   kUnrollLargeG  rows per slot per step, 4-8 heads
+//   kUnrollI8      rows per slot per step, 1-2 heads, int8 latents
+//   kNonTemporal   cache-policy bits of the streaming latent loads: each
+//                  latent byte is used once, so it should not displace
+//                  reusable lines in L2
+//   kMfmaTiles     16-token score tiles per wave per step in the
+//                  matrix-core kernel
+//   kValuAfter, kMfmaAfter  where a kernel issues its first latent loads in
+//                  the prologue (prologue's kAfter): the VALU kernel once q
+//                  is staged, the matrix-core kernel after the absorption,
+//                  so every load the prologue waits for is served ahead of
+//                  the grid's latent stream
+constexpr int kUnrollSmallG = 4;
+constexpr int kUnrollLargeG = 2;
+constexpr int kUnrollI8 = 2;
+constexpr int kNonTemporal = 2;
+constexpr int kMfmaTiles = 2;
+constexpr int kValuAfter = 1;
+constexpr int kMfmaAfter = 2;
 
 
 template <class LT, int R, int G>
@@ -148,8 +123,8 @@ struct Geo {
   // per step.
   static constexpr bool kQtInLds = kEPL * G >= 128;
   static constexpr int kU = kQtInLds ? 1
-                           : G >= 4 ? LRATTN_UNROLL_LARGE_G
-                           : (LT::kBytes == 1 ? LRATTN_UNROLL_I8 : LRATTN_UNROLL_SMALL_G);
+                           : G >= 4 ? kUnrollLargeG
+                           : (LT::kBytes == 1 ? kUnrollI8 : kUnrollSmallG);
   static constexpr int kChunk = kU * kRPW;                // rows per wave per step
   // Occupancy target (waves per SIMD) the register allocation must meet:
   // 4 (<= 128 VGPRs) unless q~ plus accumulators alone need more than 64.
@@ -160,9 +135,9 @@ struct Geo {
 };
 
 // One lane load of kWords 32-bit words (16 or 8 bytes) with cache policy kAux:
-// LRATTN_LOAD_AUX (non-temporal) for latents read once, 0 where other
+// kNonTemporal for latents read once, 0 where other
 // workgroups of the same XCD read the same latents (shared streams).
-template <int kWords, int kAux = LRATTN_LOAD_AUX>
+template <int kWords, int kAux = kNonTemporal>
 __device__ __forceinline__ void load_words(uint32_t (&w)[kWords], __amdgpu_buffer_rsrc_t r,
                                            uint32_t off) {
   if constexpr (kWords == 4) {
@@ -186,7 +161,7 @@ struct Step {
   float imp[Geo<LT, R, G>::kU];  // adaptive rank: the rows' importance scores
 };
 
-template <class LT, int R, int G, int kAux = LRATTN_LOAD_AUX, bool kAd = false>
+template <class LT, int R, int G, int kAux = kNonTemporal, bool kAd = false>
 __device__ __forceinline__ void load_step(Step<LT, R, G>& st, int cb, int slot, uint32_t lane_off,
                                           __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                           __amdgpu_buffer_rsrc_t rsk, __amdgpu_buffer_rsrc_t rsv,
@@ -279,11 +254,12 @@ __device__ __forceinline__ void compute_step(
     // instruction writes 256 contiguous bytes (one 4-byte store per row and
     // head into [head][token] rows cost ~40 us of the step at gqa_vlm).
     // Rows past the partition get an offset past the buffer and are
-    // dropped.  LDS accesses of one wave complete in order; the asm keeps
-    // the compiler from moving them across.
+    // dropped.  wave_sync: the other lanes' tile stores are visible to the
+    // reads below, and (after the loop) those reads are done before the next
+    // step's stores.
     constexpr int NV = G * Gm::kChunk;
     const int lane = threadIdx.x & 63;
-    __asm__ volatile("" ::: "memory");
+    wave_sync();
 #pragma unroll
     for (int k = 0; k < (NV + 63) / 64; ++k) {
       const int i = min(64 * k + lane, NV - 1), r = i / G;
@@ -291,7 +267,7 @@ __device__ __forceinline__ void compute_step(
       const uint32_t off = ok ? (uint32_t)(cb * G + i) * 4u : kOffNone;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ad.lds[i]), ad.rlg, (int)off, 0, 0);
     }
-    __asm__ volatile("" ::: "memory");
+    wave_sync();
   }
 
   // online softmax per slot and head, with a lazily moved reference max: the
@@ -799,7 +775,7 @@ __device__ __forceinline__ void write_records(const PartitionArgs& a, int b, int
   }
 }
 
-template <class LT, int R, int G, int kAux = LRATTN_LOAD_AUX, bool kAd = false, bool kSeg = false>
+template <class LT, int R, int G, int kAux = kNonTemporal, bool kAd = false, bool kSeg = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Geo<LT, R, G>::kWavesPerEU)))
 void partition_kernel(PartitionArgs a) {
@@ -858,7 +834,7 @@ void partition_kernel(PartitionArgs a) {
   // q and B_K are requested first, then the first step's latents; the
   // absorption then runs while the latents are in flight.
   Step<LT, R, G> cur;
-  prologue<R, G, LRATTN_LATENTS_AFTER>(a, b, hg, g, q_lds, qt_lds, [&]() {
+  prologue<R, G, kValuAfter>(a, b, hg, g, q_lds, qt_lds, [&]() {
     load_step<LT, R, G, kAux, kAd>(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv, rimp);
   });
 
@@ -882,22 +858,15 @@ void partition_kernel(PartitionArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
+  // one step in flight per wave: the next step's loads are issued once this
+  // step's registers are free (past the partition they return zero without
+  // touching memory)
   for (int cb = wave * CH; cb < ntok; cb += kWaves * CH) {
-    Step<LT, R, G> nxt;
-    if constexpr (LRATTN_PREFETCH) {
-      // double buffering: step i+1 is in flight while step i computes; past
-      // the partition the loads return zero without touching memory
-      load_step<LT, R, G, kAux, kAd>(nxt, cb + kWaves * CH, slot, lane_off, rk, rv, rsk, rsv, rimp);
-    }
     if (cb + CH <= ntok)
       compute_step<LT, R, G, false, kAd>(cur, cb, ntok, slot, qt, m, l, acc, ad);
     else
       compute_step<LT, R, G, true, kAd>(cur, cb, ntok, slot, qt, m, l, acc, ad);
-    if constexpr (LRATTN_PREFETCH) {
-      cur = nxt;
-    } else {
-      load_step<LT, R, G, kAux, kAd>(cur, cb + kWaves * CH, slot, lane_off, rk, rv, rsk, rsv, rimp);
-    }
+    load_step<LT, R, G, kAux, kAd>(cur, cb + kWaves * CH, slot, lane_off, rk, rv, rsk, rsv, rimp);
   }
 
   // ---- merge the slots of this wave (lanes with equal cc)
@@ -955,7 +924,7 @@ void partition_kernel(PartitionArgs a) {
 // VALU path), so the exponentials computed in the score layout can be handed
 // to the value side through a per-wave LDS tile [token][head]; the value side
 // keeps the VALU path's slot layout: kLPR lanes per row, 8 columns per lane.
-template <int R, int G, int NT = LRATTN_MFMA_TILES>
+template <int R, int G, int NT = kMfmaTiles>
 struct MGeo {
   static constexpr int kRowBytes = 2 * R;
   static constexpr int kKC = R / 32;           // 32-column MFMA steps per tile
@@ -973,7 +942,7 @@ struct MGeo {
   static_assert(R % 32 == 0 && (G == 1 || G == 2 || G == 4 || G == 8), "matrix-core path shape");
 };
 
-template <int R, int G, int NT = LRATTN_MFMA_TILES>
+template <int R, int G, int NT = kMfmaTiles>
 struct MStep {
   uint32_t k[NT][MGeo<R, G, NT>::kKC][4];
   uint32_t v[NT][MGeo<R, G, NT>::kVU][4];
@@ -1016,7 +985,7 @@ __device__ __forceinline__ uint32_t keep_word(uint32_t w, int keep, int e0) {
   return w & (keep > e0 + 1 ? 0xffffffffu : keep > e0 ? 0x0000ffffu : 0u);
 }
 
-template <int R, int G, int NT, int kAux = LRATTN_LOAD_AUX>
+template <int R, int G, int NT, int kAux = kNonTemporal>
 __device__ __forceinline__ void load_mstep(MStep<R, G, NT>& st, int cb, uint32_t koff,
                                            uint32_t voff, __amdgpu_buffer_rsrc_t rk,
                                            __amdgpu_buffer_rsrc_t rv) {
@@ -1154,9 +1123,8 @@ __device__ __forceinline__ void softmax_values(const float (&s)[NT][4], const MS
       else dst[0] = e[t][0];
     }
   }
-  // LDS accesses of one wave complete in order; this keeps the compiler
-  // from moving the reads below above the writes of other lanes
-  __asm__ volatile("" ::: "memory");
+  // the other lanes' weights are read below
+  wave_sync();
 
   // latent-space value accumulation, slot layout
   const int slot = lane / Mg::kLPR;
@@ -1192,7 +1160,8 @@ __device__ __forceinline__ void softmax_values(const float (&s)[NT][4], const MS
       }
     }
   }
-  __asm__ volatile("" ::: "memory");
+  // the tile's reads are done before the next step writes it
+  wave_sync();
 }
 
 template <int R, int G, bool kMask, bool kAd = false>
@@ -1265,7 +1234,7 @@ constexpr int mfma_waves() {
   return kAd && G == 8 && MGeo<R, G>::kWavesPerEU > 2 ? 2 : MGeo<R, G>::kWavesPerEU;
 }
 
-template <int R, int G, int kAux = LRATTN_LOAD_AUX, bool kSeg = false, bool kAd = false>
+template <int R, int G, int kAux = kNonTemporal, bool kSeg = false, bool kAd = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(mfma_waves<R, G, kAd>())))
 void partition_mfma_kernel(PartitionArgs a) {
@@ -1310,7 +1279,7 @@ void partition_mfma_kernel(PartitionArgs a) {
 
   MStep<R, G> cur;
   MImp<Mg::kNT, Mg::kVU> icur;
-  prologue<R, G, LRATTN_MFMA_LATENTS_AFTER>(a, b, hg, g, lds.base.q, lds.base.qt, [&]() {
+  prologue<R, G, kMfmaAfter>(a, b, hg, g, lds.base.q, lds.base.qt, [&]() {
     load_mstep<R, G, Mg::kNT, kAux>(cur, wave * CH, koff, voff, rk, rv);
     if constexpr (kAd) load_mimp<R, G, Mg::kNT>(icur, wave * CH, lane, slot, rimp);
   });
@@ -1344,23 +1313,12 @@ void partition_mfma_kernel(PartitionArgs a) {
   }
   float* wl = lds.w + wave * CH * G;
   for (int cb = wave * CH; cb < ntok; cb += kWaves * CH) {
-    MStep<R, G> nxt;
-    MImp<Mg::kNT, Mg::kVU> inxt;
-    if constexpr (LRATTN_PREFETCH) {
-      load_mstep<R, G, Mg::kNT, kAux>(nxt, cb + kWaves * CH, koff, voff, rk, rv);
-      if constexpr (kAd) load_mimp<R, G, Mg::kNT>(inxt, cb + kWaves * CH, lane, slot, rimp);
-    }
     if (cb + CH <= ntok)
       compute_mstep<R, G, false, kAd>(cur, cb, ntok, lane, qa, mm, ll, acc, wl, &icur, &ad);
     else
       compute_mstep<R, G, true, kAd>(cur, cb, ntok, lane, qa, mm, ll, acc, wl, &icur, &ad);
-    if constexpr (LRATTN_PREFETCH) {
-      cur = nxt;
-      if constexpr (kAd) icur = inxt;
-    } else {
-      load_mstep<R, G, Mg::kNT, kAux>(cur, cb + kWaves * CH, koff, voff, rk, rv);
-      if constexpr (kAd) load_mimp<R, G, Mg::kNT>(icur, cb + kWaves * CH, lane, slot, rimp);
-    }
+    load_mstep<R, G, Mg::kNT, kAux>(cur, cb + kWaves * CH, koff, voff, rk, rv);
+    if constexpr (kAd) load_mimp<R, G, Mg::kNT>(icur, cb + kWaves * CH, lane, slot, rimp);
   }
 
   mfma_epilogue<R, G, Mg::kNT, kSeg>(a, b, hg, p, mm, ll, acc, lds.base);
@@ -2051,7 +2009,7 @@ __global__ __launch_bounds__(kThreads) void probe_copy_kernel(u32x4* __restrict_
 // The matrix-core score kernel serves bf16 latents, r a multiple of 32 and
 // 4 or 8 heads per kv-head.
 constexpr bool mfma_scores(int latent_dtype, int rank, int group) {
-  return LRATTN_MFMA_SCORES && latent_dtype == LRATTN_BF16 && rank % 32 == 0 &&
+  return latent_dtype == LRATTN_BF16 && rank % 32 == 0 &&
          (group == 4 || group == 8);
 }
 
@@ -2064,7 +2022,7 @@ hipError_t launch_pg(int group, const PartitionArgs& a, hipStream_t s) {
   if (a.BK1 != nullptr) {
     // two factor sets: grid (HG, B, P), see tile_of
     const dim3 grid(a.HG, a.B, a.P);
-    constexpr int X = LRATTN_LOAD_AUX;
+    constexpr int X = kNonTemporal;
     if constexpr (mfma_scores(std::is_same<LT, LatBF16>::value ? LRATTN_BF16 : -1, R, 4)) {
       if (group == 4) {
         hipLaunchKernelGGL((partition_mfma_kernel<R, 4, X, true>), grid, block, 0, s, a);
@@ -2136,7 +2094,7 @@ hipError_t launch_ag(int group, const PartitionArgs& a, hipStream_t s) {
   // bf16 latents with 4 or 8 heads per kv-head and r a multiple of 32: the
   // matrix-core kernel, as for the plain decode
   if constexpr (mfma_scores(std::is_same<LT, LatBF16>::value ? LRATTN_BF16 : -1, R, 4)) {
-    constexpr int X = LRATTN_LOAD_AUX;
+    constexpr int X = kNonTemporal;
     if (group == 4) {
       hipLaunchKernelGGL((partition_mfma_kernel<R, 4, X, false, true>), grid, block, 0, s, a);
       return hipGetLastError();
@@ -2147,10 +2105,10 @@ hipError_t launch_ag(int group, const PartitionArgs& a, hipStream_t s) {
     }
   }
   switch (group) {
-    case 1: hipLaunchKernelGGL((partition_kernel<LT, R, 1, LRATTN_LOAD_AUX, true>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((partition_kernel<LT, R, 2, LRATTN_LOAD_AUX, true>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((partition_kernel<LT, R, 4, LRATTN_LOAD_AUX, true>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((partition_kernel<LT, R, 8, LRATTN_LOAD_AUX, true>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((partition_kernel<LT, R, 1, kNonTemporal, true>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((partition_kernel<LT, R, 2, kNonTemporal, true>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((partition_kernel<LT, R, 4, kNonTemporal, true>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((partition_kernel<LT, R, 8, kNonTemporal, true>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -2256,6 +2214,11 @@ bool adaptive_supported(int latent_dtype, int rank, int group) {
     case LRATTN_I8: return rank == 32 && (group == 1 || group == 4);
     default: return false;
   }
+}
+
+const char* adaptive_kernel_name(int latent_dtype, int rank, int group) {
+  if (!adaptive_supported(latent_dtype, rank, group)) return "";
+  return mfma_scores(latent_dtype, rank, group) ? "partition_mfma_kernel" : "partition_kernel";
 }
 
 hipError_t launch_adaptive(int latent_dtype, int rank, int group, const PartitionArgs& a,

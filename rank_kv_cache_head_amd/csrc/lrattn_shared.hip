@@ -369,9 +369,8 @@ void shared_once_kernel(SharedOnceArgs a) {
         pw[(4 * (lane >> 4) + i) * kPStride + 16 * t + (lane & 15)] = e;
       }
     }
-    // LDS accesses of one wave complete in order; the asm keeps the compiler
-    // from moving the reads below above the writes of other lanes
-    __asm__ volatile("" ::: "memory");
+    // the other lanes' weights are read below
+    wave_sync();
     // A operand: head l % 16, tokens 8 (l / 16) .. + 7, as hi + lo bf16
     bf16x8 pa[2];
     {
