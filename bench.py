@@ -1,19 +1,25 @@
 #!/usr/bin/env python3
 """Decode-attention benchmark over a per-head low-rank KV cache on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config gqa_vlm]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config ragged]
 
 One step = one lrattn_decode call (partition kernel + combine kernel) over
 one batch: every query head of every sequence attends to its whole cached
 context once, i.e. one decode token per sequence for one attention layer.
 Inputs are seeded synthetic tensors with the workload's shapes and value
-distributions, resident in HBM before timing starts.
+distributions, resident in HBM before timing starts.  The headline workload
+is the largest, ragged long context (4 sequences x 40 heads, lengths up to
+131072, 256 partitions per head); the other workloads are timed the same way
+and reported under `other_workloads`.
 
 Printed: one JSON line.  `value` = decode tokens/s = B * K / (wall time of K
 steps), bracketed by device synchronization.  `roofline` describes the
 dominant (partition) kernel: algorithmic bytes per launch / mean launch time
-measured with HIP events on the launch stream.  `cpu_baseline` times the fp64
-CPU oracle on a bounded sample of the same workload.
+measured with HIP events on the launch stream, the counted HBM traffic of a
+launch from the committed rocprofv3 counter record (and its GB/s at the
+launch time measured here), and the read probe's attainable GB/s.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -45,15 +51,20 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="gqa_vlm",
-                    choices=["tiny", "llm7b", "gqa_vlm", "int8", "ragged"])
+    ap.add_argument("--config", default="ragged",
+                    choices=["tiny", "llm7b", "gqa_vlm", "int8", "ragged"],
+                    help="headline workload (default: ragged, the largest: 4 x 40 heads over "
+                         "up to 131072 tokens, 256 partitions per head)")
+    ap.add_argument("--also", default="gqa_vlm,int8,llm7b,tiny",
+                    help="comma-separated workloads also timed (plain decode step and "
+                         "partition kernel), reported under other_workloads; '' for none")
     ap.add_argument("--num-splits", type=int, default=0,
                     help="0 = the workload's own (ragged: 256), else the library heuristic")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--probe", action="store_true",
-                    help="also run the HBM read/copy probe kernels (calibration)")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the HBM read/copy probe kernels (attainable bandwidth)")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-cache baseline (same workload, K and V of d columns)")
     ap.add_argument("--no-rebuild", action="store_true",
@@ -101,20 +112,21 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(config: str, per_launch_alg: float):
-    """HBM bytes per partition launch from committed rocprofv3 counter runs.
-
-    Null when no counter file exists for this workload or the kernel source has
-    changed since the counters were taken.
-    """
-    path = os.path.join(ROOT, "profiles", f"partition_{config}_traffic.json")
+def load_traffic(config: str):
+    """The partition launch's HBM traffic record from the committed rocprofv3
+    counter runs (FETCH_SIZE, then WRITE_SIZE, each calibrated against a
+    probe copy of known size): (bytes per launch, record file), or None when
+    no record exists for this workload or the kernel source has changed since
+    the counters were taken."""
+    rel = os.path.join("profiles", f"partition_{config}_traffic.json")
+    path = os.path.join(ROOT, rel)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_sha") != kernel_source_sha():
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("bytes_per_launch"), rel, rec.get("kernel_sha")
 
 
 def cpu_baseline(w, gpu_out, seconds: float):
@@ -161,6 +173,108 @@ def cpu_baseline(w, gpu_out, seconds: float):
                 seconds=dt, max_rel_err_vs_gpu=err, checked_sequences=min(done, w.batch))
 
 
+class Measured:
+    """One workload's decode step, timed: K steps back to back (wall clock and
+    HIP events), then the partition kernel alone (K launches between two HIP
+    events on the stream they are launched on, and K isolated launches)."""
+
+    def __init__(self, name, torch, lr, args, splits, steps, warmup):
+        import numpy as np
+        import workloads
+        t_gen = time.perf_counter()
+        w = workloads.make(name)
+        self.w = w
+        self.ab = ab = w.algorithmic_bytes()
+        self.gen_s = time.perf_counter() - t_gen
+        lat_bytes = ab["latents"] + ab["scales"]
+        # rotate input copies so the 256 MB MALL cannot serve a step from cache
+        self.copies = copies = max(1, min(8, math.ceil(ROTATE_BYTES / max(1, lat_bytes))))
+        self.base, self.sets = base, sets = device_tensors(w, torch, copies)
+        self.p = p = lr.params_for(base["q"], sets[0][0], base["B_K"], num_splits=splits)
+        self.P, self.S = lr.plan(p)
+        ws = torch.empty(lr.workspace_size(p), dtype=torch.uint8, device="cuda")
+        self.out = out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32,
+                                     device="cuda")
+        decs = [lr.Decoder(base["q"], lk, lv, base["B_K"], base["B_V"], base["seq_lens"], sc,
+                           out=out, workspace=ws, num_splits=splits)
+                for lk, lv, sc in sets]
+
+        for i in range(warmup):
+            decs[i % copies]()
+        torch.cuda.synchronize()
+        e_beg, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e_beg.record()
+        for i in range(steps):
+            decs[i % copies]()
+        e_end.record()
+        torch.cuda.synchronize()
+        self.wall = time.perf_counter() - t0
+        self.region_ms = e_beg.elapsed_time(e_end)
+        self.gpu_out = out.cpu().numpy().astype(np.float64)
+
+        for i in range(min(warmup, 5)):
+            decs[i % copies].partition()
+        torch.cuda.synchronize()
+        r_beg, r_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r_beg.record()
+        for i in range(steps):
+            decs[i % copies].partition()
+        r_end.record()
+        torch.cuda.synchronize()
+        self.launch_mean_s = r_beg.elapsed_time(r_end) / steps / 1e3
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record()
+            decs[i % copies].partition()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        self.launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+        self.ms_per_step = self.wall / steps * 1e3
+        # algorithmic bytes of one partition launch: valid latent rows (K and
+        # V), their int8 scales, q and B_K
+        self.part_bytes = ab["latents"] + ab["scales"] + ab["q"] + w.B_K.nbytes
+        self.kernel = lr.partition_kernel(p)
+        del decs
+
+    def roofline(self):
+        achieved = self.part_bytes / self.launch_mean_s / 1e9
+        tr = load_traffic(self.w.name)
+        res = {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None if tr is None else tr[0],
+            "kernel": self.kernel,
+            "mean_launch_us": self.launch_mean_s * 1e6,
+            "isolated_launch_us": float(self.launch_ms.mean()) * 1e3,
+            "min_isolated_launch_us": float(self.launch_ms.min()) * 1e3,
+            "algorithmic_bytes_per_launch": self.part_bytes,
+        }
+        if tr is not None:
+            # counter bandwidth: the counted HBM bytes of one launch over the
+            # mean launch time measured here
+            res["counter_GBps"] = tr[0] / self.launch_mean_s / 1e9
+            res["traffic_over_algorithmic"] = tr[0] / self.part_bytes
+            res["traffic_source"] = f"{tr[1]} (kernel source {tr[2]})"
+        return res
+
+    def summary(self):
+        w = self.w
+        return dict(workload=WORKLOAD_TEXT[w.name], ms_per_step=self.ms_per_step,
+                    tokens_per_s=w.batch / (self.ms_per_step / 1e3),
+                    step_algorithmic_GBps=self.ab["total"] / (self.ms_per_step / 1e3) / 1e9,
+                    num_splits=self.P, split_tokens=self.S, roofline=self.roofline())
+
+    def release(self, torch):
+        self.base = self.sets = self.out = None
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -168,89 +282,23 @@ def main():
               "single-GPU, sharding across GPUs is described in the design notes.",
               file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
     import workloads
     import rank_kv_cache_head_amd as lr
 
     lr.lib()  # fail loudly if the library is missing
-    if args.num_splits == 0:
-        args.num_splits = workloads.SPLITS.get(args.config, 0)
-    t_gen = time.perf_counter()
-    w = workloads.make(args.config)
-    ab = w.algorithmic_bytes()
-    gen_s = time.perf_counter() - t_gen
-    lat_bytes = ab["latents"] + ab["scales"]
-    copies = max(1, min(8, math.ceil(ROTATE_BYTES / max(1, lat_bytes))))
-    base, sets = device_tensors(w, torch, copies)
-    p = lr.params_for(base["q"], sets[0][0], base["B_K"], num_splits=args.num_splits)
-    P, S = lr.plan(p)
-    ws = torch.empty(lr.workspace_size(p), dtype=torch.uint8, device="cuda")
-    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
-
-    decs = [lr.Decoder(base["q"], lk, lv, base["B_K"], base["B_V"], base["seq_lens"], sc,
-                       out=out, workspace=ws, num_splits=args.num_splits)
-            for lk, lv, sc in sets]
-
-    def step(i):
-        decs[i % copies]()
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # ---- timed region: K whole decode steps, back to back
+    splits = args.num_splits or workloads.SPLITS.get(args.config, 0)
     K = args.steps
-    e_beg, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e_beg.record()
-    for i in range(K):
-        step(i)
-    e_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    region_ms = e_beg.elapsed_time(e_end)
-    gpu_out = out.cpu().numpy().astype(np.float64)
-
-    # ---- the dominant kernel (partition) alone: K launches back to back
-    # between two HIP events on the stream they are launched on (the average
-    # launch duration), then K launches each between its own pair of events
-    # (an isolated launch, which adds the launch latency)
-    for i in range(min(args.warmup, 5)):
-        decs[i % copies].partition()
-    torch.cuda.synchronize()
-    r_beg, r_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    r_beg.record()
-    for i in range(K):
-        decs[i % copies].partition()
-    r_end.record()
-    torch.cuda.synchronize()
-    launch_mean_s = r_beg.elapsed_time(r_end) / K / 1e3
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-    for i in range(K):
-        ev[i][0].record()
-        decs[i % copies].partition()
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
-
-    # algorithmic bytes of one partition launch: valid latent rows (K and V),
-    # their int8 scales, q and B_K
-    part_bytes = ab["latents"] + ab["scales"] + ab["q"] + w.B_K.nbytes
-    achieved = part_bytes / launch_mean_s / 1e9
-    traffic = load_traffic(args.config, part_bytes)
-
-    ms_per_step = wall / K * 1e3
+    m = Measured(args.config, torch, lr, args, splits, K, args.warmup)
+    w, ab = m.w, m.ab
     line = {
         "metric": "decode attention tokens/s per GPU + achieved HBM GB/s vs ~8 TB/s peak",
-        "value": w.batch * K / wall,
+        "value": w.batch * K / m.wall,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": m.ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -261,40 +309,41 @@ def main():
             "name": args.config,
             "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "rank": w.rank, "max_seq_len": w.max_seq_len,
+            "seq_lens": [int(x) for x in w.seq_lens],
             "valid_tokens": ab["valid_tokens"], "storage": w.latent_dtype,
-            "num_splits": P, "split_tokens": S, "input_copies_rotated": copies,
+            "num_splits": m.P, "split_tokens": m.S, "input_copies_rotated": m.copies,
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": traffic,
-            "kernel": lr.partition_kernel(p),
-            "mean_launch_us": launch_mean_s * 1e6,
-            "isolated_launch_us": float(launch_ms.mean()) * 1e3,
-            "min_isolated_launch_us": float(launch_ms.min()) * 1e3,
-            "algorithmic_bytes_per_launch": part_bytes,
-        },
-        "step_algorithmic_GBps": ab["total"] / (ms_per_step / 1e3) / 1e9,
-        "timed_region_event_ms": region_ms,
-        "input_generation_s": gen_s,
+        "roofline": m.roofline(),
+        "step_algorithmic_GBps": ab["total"] / (m.ms_per_step / 1e3) / 1e9,
+        "timed_region_event_ms": m.region_ms,
+        "input_generation_s": m.gen_s,
     }
+    base, sets, ms_per_step = m.base, m.sets, m.ms_per_step
+    if not args.no_probe:
+        line["probe"] = run_probe(torch, lr)
+        line["roofline"]["attainable_read_GBps"] = line["probe"]["read_GBps"]
     if not args.no_dense:
-        line["dense_baseline"] = dense_baseline(w, torch, lr, args, ms_per_step)
+        line["dense_baseline"] = dense_baseline(w, torch, lr, args, splits, ms_per_step)
     if not args.no_rebuild:
-        line["rebuilt_keys"] = rebuilt_keys(w, torch, lr, args, base, sets, ms_per_step)
+        line["rebuilt_keys"] = rebuilt_keys(w, torch, lr, args, splits, base, sets, ms_per_step)
     if not args.no_append:
         line["append_step"] = append_step(w, torch, lr, args)
     if not args.no_shared:
-        line["shared_latent"] = shared_latent(w, torch, lr, args, ms_per_step)
+        line["shared_latent"] = shared_latent(w, torch, lr, args, splits, ms_per_step)
     if not args.no_modal:
-        line["modal_factors"] = modal_factors(w, torch, lr, args, base, sets, ms_per_step)
+        line["modal_factors"] = modal_factors(w, torch, lr, args, splits, base, sets, ms_per_step)
     if not args.no_adaptive:
-        line["adaptive_rank"] = adaptive_rank(w, torch, lr, args, base, sets, ms_per_step)
-    if args.probe:
-        line["probe"] = run_probe(torch, lr)
+        line["adaptive_rank"] = adaptive_rank(w, torch, lr, args, splits, base, sets, ms_per_step)
+    gpu_out = m.gpu_out
+    m.release(torch)
+    base = sets = None
+    others = [x for x in args.also.split(",") if x and x != args.config]
+    if others:
+        line["other_workloads"] = {}
+        for name in others:
+            o = Measured(name, torch, lr, args, workloads.SPLITS.get(name, 0), K, args.warmup)
+            line["other_workloads"][name] = o.summary()
+            o.release(torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, gpu_out, args.cpu_seconds)
     else:
@@ -302,7 +351,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def dense_baseline(w, torch, lr, args, compressed_ms):
+def dense_baseline(w, torch, lr, args, splits, compressed_ms):
     """The same workload over an uncompressed cache: K, V [B, Hkv, T, d] in
     the latent storage type (random values drawn on the device; the content
     does not change the work), timed like the main loop.  None when such rows
@@ -334,7 +383,7 @@ def dense_baseline(w, torch, lr, args, compressed_ms):
     for _ in range(copies):
         K, V = draw(), draw()
         keep.append((K, V))
-        decs.append(lr.DenseDecoder(q, K, V, seq, sc, out=out, num_splits=args.num_splits))
+        decs.append(lr.DenseDecoder(q, K, V, seq, sc, out=out, num_splits=splits))
     for i in range(args.warmup):
         decs[i % copies]()
     torch.cuda.synchronize()
@@ -355,7 +404,7 @@ def dense_baseline(w, torch, lr, args, compressed_ms):
     return res
 
 
-def rebuilt_keys(w, torch, lr, args, base, sets, absorbed_ms):
+def rebuilt_keys(w, torch, lr, args, splits, base, sets, absorbed_ms):
     """The same step with keys rebuilt on chip (lrattn_rebuild_decode), without
     and with a rotary table, on the same inputs.  None where the mode does not
     apply (it takes bf16 inputs, d in {64, 128}, r in {32, 64})."""
@@ -369,7 +418,7 @@ def rebuilt_keys(w, torch, lr, args, base, sets, absorbed_ms):
     res = {}
     for name, tab in (("unrotated", None), ("rotated", rope)):
         decs = [lr.RebuildDecoder(base["q"], lk, lv, base["B_K"], base["B_V"], base["seq_lens"],
-                                  tab, out=out, num_splits=args.num_splits)
+                                  tab, out=out, num_splits=splits)
                 for lk, lv, _ in sets]
         n = len(decs)
         for i in range(args.warmup):
@@ -440,7 +489,7 @@ def append_step(w, torch, lr, args):
                          else "append_partial_kernel + append_finish_kernel"))
 
 
-def adaptive_rank(w, torch, lr, args, base, sets, plain_ms):
+def adaptive_rank(w, torch, lr, args, splits, base, sets, plain_ms):
     """The same step with attention-aware rank (AttentionPack's adaptive
     decompression): tokens whose importance score is below 0.5 keep r/2
     latent coordinates; the step writes its logits and updates the scores
@@ -457,7 +506,7 @@ def adaptive_rank(w, torch, lr, args, base, sets, plain_ms):
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     decs = [lr.AdaptiveDecoder(base["q"], lk, lv, base["B_K"], base["B_V"], base["seq_lens"],
                                imp, low_rank=w.rank // 2, threshold=0.5, decay=0.9, scales=sc,
-                               out=out, num_splits=args.num_splits)
+                               out=out, num_splits=splits)
             for lk, lv, sc in sets]
     n = len(decs)
     for i in range(args.warmup):
@@ -473,13 +522,14 @@ def adaptive_rank(w, torch, lr, args, base, sets, plain_ms):
     # written and read, importance read and written (update)
     extra = valid * (w.num_kv_heads * 4 + 2 * w.num_q_heads * 4 + w.num_kv_heads * 8)
     moved = w.algorithmic_bytes()["total"] + extra
+    kern = lr.adaptive_kernel(decs[0].params, decs[0].adaptive)
     return dict(ms_per_step=ms, tokens_per_s=w.batch / (ms / 1e3), low_rank=w.rank // 2,
                 vs_plain=ms / plain_ms, added_bytes_per_step=extra,
                 step_GBps=moved / (ms / 1e3) / 1e9, frac_of_8TBps=moved / (ms / 1e3) / 8e12,
-                kernel="partition_kernel (adaptive) + combine + importance_kernel")
+                kernel=f"{kern} (adaptive) + combine_kernel + importance_kernel")
 
 
-def modal_factors(w, torch, lr, args, base, sets, one_set_ms):
+def modal_factors(w, torch, lr, args, splits, base, sets, one_set_ms):
     """The same step with separate factors for the workload's image block and
     its text (AttentionPack's modal separation): the image tokens and the
     text in partitions of their own, one latent-space sum per set in the
@@ -497,7 +547,7 @@ def modal_factors(w, torch, lr, args, base, sets, one_set_ms):
                                     base["B_V"].float().std()).to(base["B_V"].dtype)])
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     decs = [lr.ModalDecoder(base["q"], lk, lv, BK, BV, base["seq_lens"], ni, sc, out=out,
-                            num_splits=args.num_splits)
+                            num_splits=splits)
             for lk, lv, sc in sets]
     n = len(decs)
     for i in range(args.warmup):
@@ -515,7 +565,7 @@ def modal_factors(w, torch, lr, args, base, sets, one_set_ms):
                 records=lr.modal_workspace_size(decs[0].params, ni))
 
 
-def shared_latent(w, torch, lr, args, grouped_ms):
+def shared_latent(w, torch, lr, args, splits, grouped_ms):
     """The workload's batch, query heads and lengths over one latent stream of
     R = 128 bf16 values per token shared by all heads, each head with its own
     factor blocks (AttentionPack's multi-head compression), timed like the
@@ -533,11 +583,11 @@ def shared_latent(w, torch, lr, args, grouped_ms):
     q = torch.randn((w.batch, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
     import numpy as np
     sl = torch.from_numpy(w.seq_lens.astype(np.int32)).cuda()
-    p = lr.shared_params_for(q, LK, BK, num_splits=args.num_splits)
+    p = lr.shared_params_for(q, LK, BK, num_splits=splits)
     ws = torch.empty(lr.shared_workspace_size(p), dtype=torch.uint8, device="cuda")
     out = torch.empty((w.batch, Hq, d), device="cuda")
     run = lambda: lr.shared_decode(q, LK, LV, BK, BV, sl, out=out, workspace=ws,
-                                   num_splits=args.num_splits)
+                                   num_splits=splits)
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()

@@ -301,6 +301,11 @@ typedef struct lrattn_adaptive {
 } lrattn_adaptive;
 int lrattn_adaptive_workspace_size(const lrattn_params* p, const lrattn_adaptive* ad,
                                    size_t* bytes);
+/* Host-only.  Name of the partition kernel lrattn_adaptive_decode launches
+ * for `p` and `ad`, as profilers list it: "partition_mfma_kernel" (bf16
+ * latents, r a multiple of 32, 4 or 8 query heads per kv-head) or
+ * "partition_kernel"; static text.  NULL when the call would be rejected. */
+const char* lrattn_adaptive_kernel(const lrattn_params* p, const lrattn_adaptive* ad);
 int lrattn_adaptive_decode(const lrattn_params* p,
                            const lrattn_adaptive* ad,
                            const void* q,

@@ -30,7 +30,8 @@ __all__ = [
     "AppendParams", "append_workspace_size", "append", "Appender",
     "shared_params_for", "shared_workspace_size", "shared_decode",
     "modal_params_for", "modal_workspace_size", "modal_decode", "ModalDecoder",
-    "AdaptiveParams", "adaptive_workspace_size", "adaptive_decode", "AdaptiveDecoder",
+    "AdaptiveParams", "adaptive_workspace_size", "adaptive_kernel", "adaptive_decode",
+    "AdaptiveDecoder",
     "probe_read", "probe_copy", "probe_sink_floats", "declared_symbols",
     "F32", "BF16", "F16", "I8",
 ]
@@ -115,6 +116,8 @@ def lib() -> ctypes.CDLL:
         L.lrattn_shared_workspace_size.argtypes = [_PP, ctypes.POINTER(ctypes.c_size_t)]
         L.lrattn_partition_kernel.argtypes = [_PP]
         L.lrattn_partition_kernel.restype = ctypes.c_char_p
+        L.lrattn_adaptive_kernel.argtypes = [_PP, ctypes.POINTER(AdaptiveParams)]
+        L.lrattn_adaptive_kernel.restype = ctypes.c_char_p
         L.lrattn_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                     ctypes.c_size_t, _VP]
         L.lrattn_partition.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -280,6 +283,12 @@ def adaptive_workspace_size(p: Params, ad: AdaptiveParams) -> int:
                                                 ctypes.byref(b)),
            "lrattn_adaptive_workspace_size")
     return b.value
+
+
+def adaptive_kernel(p: Params, ad: AdaptiveParams) -> str:
+    """lrattn_adaptive_kernel: the adaptive-rank partition kernel's name."""
+    adaptive_workspace_size(p, ad)  # raises on a rejected configuration
+    return lib().lrattn_adaptive_kernel(ctypes.byref(p), ctypes.byref(ad)).decode()
 
 
 def _check_importance(p: Params, importance):

@@ -333,6 +333,13 @@ int lrattn_adaptive_workspace_size(const lrattn_params* p, const lrattn_adaptive
   return LRATTN_OK;
 }
 
+const char* lrattn_adaptive_kernel(const lrattn_params* p, const lrattn_adaptive* ad) {
+  Plan pl;
+  size_t lo, so, total;
+  if (adaptive_check(p, ad, &pl, &lo, &so, &total) != LRATTN_OK) return nullptr;
+  return lrattn::adaptive_kernel_name(p->latent_dtype, p->rank, group_of(p));
+}
+
 int lrattn_adaptive_decode(const lrattn_params* p, const lrattn_adaptive* ad, const void* q,
                            const void* L_K, const void* L_V, const void* B_K, const void* B_V,
                            const float* scales, const int32_t* seq_lens, float* importance,

@@ -111,6 +111,8 @@ bool partition_supported(int latent_dtype, int rank, int group);
 // Name of the partition kernel launch_partition uses for these arguments
 // (static text; "" when unsupported).
 const char* partition_kernel_name(int latent_dtype, int rank, int group);
+// The adaptive-rank partition kernel's name ("" when unsupported).
+const char* adaptive_kernel_name(int latent_dtype, int rank, int group);
 // Launch the partition grid (P, Hkv, B) on `s`.  Returns the launch error.
 hipError_t launch_partition(int latent_dtype, int rank, int group,
                             const PartitionArgs& a, hipStream_t s);

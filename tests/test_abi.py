@@ -336,3 +336,19 @@ def test_adaptive_decode_validates_on_host():
     lg = (p.batch * p.num_q_heads * p.max_seq_len * 4 + 255) // 256 * 256
     assert need == rec + lg + 256          # records, logits [B, Hq, T], row statistics
 
+
+
+def test_adaptive_kernel_names():
+    ad = lr.AdaptiveParams(16, 0.5, 0.9)
+    # bf16 latents with r a multiple of 32 and 4 or 8 heads: the matrix-core kernel
+    for r in (32, 48, 64):
+        for G in (1, 2, 4, 8):
+            p = params(rank=r, num_q_heads=2 * G, num_kv_heads=2)
+            want = "partition_mfma_kernel" if r % 32 == 0 and G >= 4 else "partition_kernel"
+            assert lr.adaptive_kernel(p, lr.AdaptiveParams(8, 0.5, 0.9)) == want, (r, G)
+    assert lr.adaptive_kernel(params(latent_dtype=lr.I8, rank=32, num_q_heads=8,
+                                     num_kv_heads=2), ad) == "partition_kernel"
+    assert lr.lib().lrattn_adaptive_kernel(ctypes.byref(params(rank=128)), ctypes.byref(ad)) is None
+    assert lr.lib().lrattn_adaptive_kernel(ctypes.byref(params()), None) is None
+    with pytest.raises(lr.LrattnError):
+        lr.adaptive_kernel(params(latent_dtype=lr.F16), ad)
