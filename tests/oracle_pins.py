@@ -100,7 +100,8 @@ BRUTE_CASES = [
 
 def pin_brute(decode, cases=BRUTE_CASES, tol=1e-13):
     for name, ov in cases:
-        w = workloads.make(name, seed=11, **ov)
+        ov = dict(ov)
+        w = workloads.make(name, seed=ov.pop("seed", 11), **ov)
         args = _f64(w)
         got = decode(*args[:6], scales=args[6])
         ref = brute.decode_decimal(*args[:6], scales=args[6])

@@ -37,3 +37,14 @@ def test_bf16_decode_exact():
     assert vals[0] == 1.0 and vals[1] == -2.0 and vals[2] == 0.0
     assert vals[3] == 0.333984375        # 0x3EAB = 1.0101011b x 2^-2
     assert vals[4] == (2 - 2 ** -7) * 2.0 ** 127
+
+
+def test_brute_force_on_the_tiny_workload_itself():
+    """The tiny workload at its own size and seed (1 sequence, 4 heads, d 64,
+    r 16, 256 tokens, fp32) through the 40-digit decimal definition: the
+    oracle agrees to 1e-13 per row (about 8 s of decimal arithmetic, so it
+    runs here once rather than inside every planted-mistake check)."""
+    import workloads
+    w = workloads.make("tiny")
+    assert (w.batch, w.num_q_heads, w.head_dim, w.rank, w.max_seq_len) == (1, 4, 64, 16, 256)
+    P.pin_brute(oracle.decode, cases=[("tiny", dict(seed=1))], tol=1e-13)
