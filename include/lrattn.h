@@ -107,7 +107,9 @@ typedef enum lrattn_status {
   LRATTN_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
   LRATTN_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than lrattn_workspace_size */
   LRATTN_ERR_SPLITS = -7,      /* num_splits < 0 or > max_seq_len */
-  LRATTN_ERR_HIP = -8          /* a kernel launch failed */
+  LRATTN_ERR_HIP = -8,         /* a kernel launch failed */
+  LRATTN_ERR_SCRATCH = -9      /* lrattn_decode_static: the records need more than
+                                  LRATTN_STATIC_SCRATCH_BYTES */
 } lrattn_status;
 
 typedef struct lrattn_params {
@@ -174,6 +176,39 @@ int lrattn_decode(const lrattn_params* p,
                   void* workspace,
                   size_t workspace_bytes,
                   lrattn_stream stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * lrattn_decode with no workspace argument.  The partial records go to a
+ * static device buffer of LRATTN_STATIC_SCRATCH_BYTES (16 MiB), one per
+ * device, which the library holds from the first call on a device until the
+ * process ends; the call allocates nothing.  Same operation, kernels, plan,
+ * results (bitwise equal to lrattn_decode's for the same p) and argument
+ * rules as lrattn_decode, plus:
+ *   - a request whose lrattn_workspace_size exceeds LRATTN_STATIC_SCRATCH_BYTES
+ *     returns LRATTN_ERR_SCRATCH before any device work (the five reference
+ *     workloads need at most 8.5 MB: 4 x 40 heads x 256 partitions x r 48);
+ *   - the buffer used is the current device's: `stream` must belong to the
+ *     current device (else LRATTN_ERR_UNSUPPORTED);
+ *   - every call on one device shares that device's buffer, so calls that
+ *     overlap in time on one device (different streams or threads without
+ *     ordering) race and give undefined results; calls ordered on one
+ *     stream are safe;
+ *   - the first call on a device resolves the buffer's address
+ *     (hipGetSymbolAddress); make it outside graph capture.
+ */
+#define LRATTN_STATIC_SCRATCH_BYTES (16u << 20)
+int lrattn_decode_static(const lrattn_params* p,
+                         const void* q,
+                         const void* L_K,
+                         const void* L_V,
+                         const void* B_K,
+                         const void* B_V,
+                         const float* scales,
+                         const int32_t* seq_lens,
+                         void* out,
+                         lrattn_stream stream);
 
 /*
  * First half of lrattn_decode alone (for measurement and testing): absorb

@@ -24,7 +24,7 @@ from typing import Optional, Tuple
 __all__ = [
     "LrattnError", "Params", "lib", "library_path", "version", "status_string",
     "params_for", "plan", "workspace_size", "partition_kernel", "decode", "partition",
-    "combine", "Decoder",
+    "combine", "Decoder", "decode_static", "STATIC_SCRATCH_BYTES",
     "dense_params_for", "dense_decode", "DenseDecoder",
     "rebuild_plan", "rebuild_workspace_size", "rebuild_decode", "RebuildDecoder",
     "AppendParams", "append_workspace_size", "append", "Appender",
@@ -114,6 +114,7 @@ def lib() -> ctypes.CDLL:
         L.lrattn_shared_decode.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                            ctypes.c_size_t, _VP]
         L.lrattn_shared_workspace_size.argtypes = [_PP, ctypes.POINTER(ctypes.c_size_t)]
+        L.lrattn_decode_static.argtypes = [_PP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
         L.lrattn_partition_kernel.argtypes = [_PP]
         L.lrattn_partition_kernel.restype = ctypes.c_char_p
         L.lrattn_adaptive_kernel.argtypes = [_PP, ctypes.POINTER(AdaptiveParams)]
@@ -126,7 +127,8 @@ def lib() -> ctypes.CDLL:
         L.lrattn_probe_sink_floats.restype = ctypes.c_size_t
         L.lrattn_probe_read.argtypes = [_VP, ctypes.c_size_t, _VP, _VP]
         L.lrattn_probe_copy.argtypes = [_VP, _VP, ctypes.c_size_t, _VP]
-        for fn in ("lrattn_plan", "lrattn_workspace_size", "lrattn_decode", "lrattn_partition",
+        for fn in ("lrattn_plan", "lrattn_workspace_size", "lrattn_decode",
+                   "lrattn_decode_static", "lrattn_partition",
                    "lrattn_combine", "lrattn_dense_decode", "lrattn_rebuild_decode",
                    "lrattn_rebuild_plan", "lrattn_rebuild_workspace_size",
                    "lrattn_modal_decode", "lrattn_modal_workspace_size",
@@ -267,6 +269,26 @@ def decode(q, L_K, L_V, B_K, B_V, seq_lens, scales=None, *, out=None, workspace=
                              _ptr(scales), _ptr(seq_lens), _ptr(out), _ptr(ws), ws_bytes,
                              _stream(stream))
     _check(st, "lrattn_decode")
+    return out
+
+
+STATIC_SCRATCH_BYTES = 16 << 20   # LRATTN_STATIC_SCRATCH_BYTES
+
+
+def decode_static(q, L_K, L_V, B_K, B_V, seq_lens, scales=None, *, out, softmax_scale=None,
+                  num_splits: int = 0, stream=None):
+    """lrattn_decode_static: the decode with its records in the library's
+    static per-device buffer (no workspace; the call allocates nothing).
+    `out` [B, Hq, d] (fp32 or bf16) is required and returned."""
+    p = params_for(q, L_K, B_K, out_dtype=out.dtype, softmax_scale=softmax_scale,
+                   num_splits=num_splits)
+    _check_shapes(p, L_V, B_V, scales, seq_lens)
+    if tuple(out.shape) != (p.batch, p.num_q_heads, p.head_dim):
+        raise ValueError("out must be [B, Hq, d]")
+    st = lib().lrattn_decode_static(ctypes.byref(p), _ptr(q), _ptr(L_K), _ptr(L_V), _ptr(B_K),
+                                    _ptr(B_V), _ptr(scales), _ptr(seq_lens), _ptr(out),
+                                    _stream(stream))
+    _check(st, "lrattn_decode_static")
     return out
 
 

@@ -199,6 +199,7 @@ const char* lrattn_status_string(int status) {
     case LRATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case LRATTN_ERR_SPLITS: return "num_splits out of range";
     case LRATTN_ERR_HIP: return "HIP launch failed";
+    case LRATTN_ERR_SCRATCH: return "records exceed the static scratch buffer (LRATTN_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
