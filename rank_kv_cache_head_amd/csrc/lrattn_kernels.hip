@@ -161,19 +161,39 @@ struct Step {
   float imp[Geo<LT, R, G>::kU];  // adaptive rank: the rows' importance scores
 };
 
+// Attention-aware rank: the importance scores of a step's rows (lane slot's
+// rows cb + slot + RPW u), loaded a step ahead of the rows' latents.
+template <class LT, int R, int G>
+__device__ __forceinline__ void load_imp(int cb, int slot, __amdgpu_buffer_rsrc_t rimp,
+                                         float (&imp)[Geo<LT, R, G>::kU]) {
+  using Gm = Geo<LT, R, G>;
+#pragma unroll
+  for (int u = 0; u < Gm::kU; ++u) imp[u] = bload4f(rimp, (uint32_t)(cb + u * Gm::kRPW + slot) * 4u);
+}
+
+// A step's latent loads.  With attention-aware rank (kAd) the rows'
+// importance scores `imp` are already in registers: a row below `thr` keeps
+// only coordinates [0, low_rank), so a lane whose whole piece lies past
+// low_rank (`drop`) gives that row's loads an offset past the buffer, which
+// fetches nothing and returns the zeros the masking would produce.
 template <class LT, int R, int G, int kAux = kNonTemporal, bool kAd = false>
 __device__ __forceinline__ void load_step(Step<LT, R, G>& st, int cb, int slot, uint32_t lane_off,
                                           __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                           __amdgpu_buffer_rsrc_t rsk, __amdgpu_buffer_rsrc_t rsv,
-                                          __amdgpu_buffer_rsrc_t rimp) {
+                                          const float* imp = nullptr, float thr = 0.f,
+                                          bool drop = false) {
   using Gm = Geo<LT, R, G>;
   constexpr int U = Gm::kU, RPW = Gm::kRPW;
+  uint32_t off[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u)
-    load_words<Gm::kWords, kAux>(st.k[u], rk, (uint32_t)(cb + u * RPW) * Gm::kRowBytes + lane_off);
+  for (int u = 0; u < U; ++u) {
+    off[u] = (uint32_t)(cb + u * RPW) * Gm::kRowBytes + lane_off;
+    if constexpr (kAd) off[u] = drop && imp[u] < thr ? kOffNone : off[u];
+  }
 #pragma unroll
-  for (int u = 0; u < U; ++u)
-    load_words<Gm::kWords, kAux>(st.v[u], rv, (uint32_t)(cb + u * RPW) * Gm::kRowBytes + lane_off);
+  for (int u = 0; u < U; ++u) load_words<Gm::kWords, kAux>(st.k[u], rk, off[u]);
+#pragma unroll
+  for (int u = 0; u < U; ++u) load_words<Gm::kWords, kAux>(st.v[u], rv, off[u]);
   if constexpr (std::is_same<LT, LatI8>::value) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -184,7 +204,7 @@ __device__ __forceinline__ void load_step(Step<LT, R, G>& st, int cb, int slot, 
   }
   if constexpr (kAd) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) st.imp[u] = bload4f(rimp, (uint32_t)(cb + u * RPW + slot) * 4u);
+    for (int u = 0; u < U; ++u) st.imp[u] = imp[u];
   }
 }
 
@@ -804,6 +824,10 @@ void partition_kernel(PartitionArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = lane / LPR, cc = lane % LPR;
+  // first row of this wave's steps and the distance between its steps (the
+  // four waves take the partition's steps in turn)
+  constexpr int kStride = kWaves * CH;
+  const int cb0 = wave * CH;
   const bool colact = cc < Gm::kAct;
 
   const size_t bg = (size_t)b * a.Hkv + g;
@@ -832,10 +856,17 @@ void partition_kernel(PartitionArgs a) {
   }
 
   // q and B_K are requested first, then the first step's latents; the
-  // absorption then runs while the latents are in flight.
+  // absorption then runs while the latents are in flight.  Attention-aware
+  // rank: the importance scores of each step's rows are requested a step
+  // ahead (the first step's before q), so the loads of dropped latent
+  // pieces can be left out.
   Step<LT, R, G> cur;
+  float inx[Gm::kU];
+  const bool drop = kAd && ad.keep == 0;
+  if constexpr (kAd) load_imp<LT, R, G>(cb0, slot, rimp, inx);
   prologue<R, G, kValuAfter>(a, b, hg, g, q_lds, qt_lds, [&]() {
-    load_step<LT, R, G, kAux, kAd>(cur, wave * CH, slot, lane_off, rk, rv, rsk, rsv, rimp);
+    load_step<LT, R, G, kAux, kAd>(cur, cb0, slot, lane_off, rk, rv, rsk, rsv, inx, ad.thr, drop);
+    if constexpr (kAd) load_imp<LT, R, G>(cb0 + kStride, slot, rimp, inx);
   });
 
   QtView<LT, R, G> qt;
@@ -861,12 +892,14 @@ void partition_kernel(PartitionArgs a) {
   // one step in flight per wave: the next step's loads are issued once this
   // step's registers are free (past the partition they return zero without
   // touching memory)
-  for (int cb = wave * CH; cb < ntok; cb += kWaves * CH) {
+  for (int cb = cb0; cb < ntok; cb += kStride) {
     if (cb + CH <= ntok)
       compute_step<LT, R, G, false, kAd>(cur, cb, ntok, slot, qt, m, l, acc, ad);
     else
       compute_step<LT, R, G, true, kAd>(cur, cb, ntok, slot, qt, m, l, acc, ad);
-    load_step<LT, R, G, kAux, kAd>(cur, cb + kWaves * CH, slot, lane_off, rk, rv, rsk, rsv, rimp);
+    load_step<LT, R, G, kAux, kAd>(cur, cb + kStride, slot, lane_off, rk, rv, rsk, rsv, inx,
+                                   ad.thr, drop);
+    if constexpr (kAd) load_imp<LT, R, G>(cb + 2 * kStride, slot, rimp, inx);
   }
 
   // ---- merge the slots of this wave (lanes with equal cc)
@@ -985,23 +1018,36 @@ __device__ __forceinline__ uint32_t keep_word(uint32_t w, int keep, int e0) {
   return w & (keep > e0 + 1 ? 0xffffffffu : keep > e0 ? 0x0000ffffu : 0u);
 }
 
-template <int R, int G, int NT, int kAux = kNonTemporal>
+// A step's latent loads.  With attention-aware rank (kAd) the rows'
+// importance scores `im` are already in registers: a 16-byte piece that
+// lies wholly past low_rank (keep 0 in this lane) is not fetched for a row
+// below the threshold (an offset past the buffer returns zeros).
+template <int R, int G, int NT, int kAux = kNonTemporal, bool kAd = false>
 __device__ __forceinline__ void load_mstep(MStep<R, G, NT>& st, int cb, uint32_t koff,
                                            uint32_t voff, __amdgpu_buffer_rsrc_t rk,
-                                           __amdgpu_buffer_rsrc_t rv) {
+                                           __amdgpu_buffer_rsrc_t rv,
+                                           const MImp<NT, MGeo<R, G, NT>::kVU>* im = nullptr,
+                                           const MAdaptive* ad = nullptr) {
   using Mg = MGeo<R, G, NT>;
 #pragma unroll
   for (int t = 0; t < Mg::kNT; ++t) {
     const uint32_t base = (uint32_t)(cb + 16 * t) * Mg::kRowBytes;
 #pragma unroll
-    for (int c = 0; c < Mg::kKC; ++c) load_words<4, kAux>(st.k[t][c], rk, base + koff + 64u * c);
+    for (int c = 0; c < Mg::kKC; ++c) {
+      uint32_t off = base + koff + 64u * c;
+      if constexpr (kAd) off = ad->keepk[c] == 0 && im->k[t] < ad->thr ? kOffNone : off;
+      load_words<4, kAux>(st.k[t][c], rk, off);
+    }
   }
 #pragma unroll
   for (int t = 0; t < Mg::kNT; ++t) {
     const uint32_t base = (uint32_t)(cb + 16 * t) * Mg::kRowBytes;
 #pragma unroll
-    for (int u = 0; u < Mg::kVU; ++u)
-      load_words<4, kAux>(st.v[t][u], rv, base + voff + (uint32_t)(u * Mg::kRPW) * Mg::kRowBytes);
+    for (int u = 0; u < Mg::kVU; ++u) {
+      uint32_t off = base + voff + (uint32_t)(u * Mg::kRPW) * Mg::kRowBytes;
+      if constexpr (kAd) off = ad->keepv == 0 && im->v[t][u] < ad->thr ? kOffNone : off;
+      load_words<4, kAux>(st.v[t][u], rv, off);
+    }
   }
 }
 
@@ -1277,11 +1323,18 @@ void partition_mfma_kernel(PartitionArgs a) {
                        (uint32_t)ntok * G * 4u);
   }
 
+  // attention-aware rank: the importance scores of each step's rows are
+  // requested a step ahead of its latents (the first step's before the
+  // prologue), so the loads of dropped latent pieces can be left out
   MStep<R, G> cur;
-  MImp<Mg::kNT, Mg::kVU> icur;
+  MImp<Mg::kNT, Mg::kVU> icur, inxt;
+  if constexpr (kAd) load_mimp<R, G, Mg::kNT>(inxt, wave * CH, lane, slot, rimp);
   prologue<R, G, kMfmaAfter>(a, b, hg, g, lds.base.q, lds.base.qt, [&]() {
-    load_mstep<R, G, Mg::kNT, kAux>(cur, wave * CH, koff, voff, rk, rv);
-    if constexpr (kAd) load_mimp<R, G, Mg::kNT>(icur, wave * CH, lane, slot, rimp);
+    load_mstep<R, G, Mg::kNT, kAux, kAd>(cur, wave * CH, koff, voff, rk, rv, &inxt, &ad);
+    if constexpr (kAd) {
+      icur = inxt;
+      load_mimp<R, G, Mg::kNT>(inxt, wave * CH + kWaves * CH, lane, slot, rimp);
+    }
   });
 
   // A operands: row lane % 16 is head (lane % 16) % G; k-group lane / 16
@@ -1317,8 +1370,11 @@ void partition_mfma_kernel(PartitionArgs a) {
       compute_mstep<R, G, false, kAd>(cur, cb, ntok, lane, qa, mm, ll, acc, wl, &icur, &ad);
     else
       compute_mstep<R, G, true, kAd>(cur, cb, ntok, lane, qa, mm, ll, acc, wl, &icur, &ad);
-    load_mstep<R, G, Mg::kNT, kAux>(cur, cb + kWaves * CH, koff, voff, rk, rv);
-    if constexpr (kAd) load_mimp<R, G, Mg::kNT>(icur, cb + kWaves * CH, lane, slot, rimp);
+    load_mstep<R, G, Mg::kNT, kAux, kAd>(cur, cb + kWaves * CH, koff, voff, rk, rv, &inxt, &ad);
+    if constexpr (kAd) {
+      icur = inxt;
+      load_mimp<R, G, Mg::kNT>(inxt, cb + 2 * kWaves * CH, lane, slot, rimp);
+    }
   }
 
   mfma_epilogue<R, G, Mg::kNT, kSeg>(a, b, hg, p, mm, ll, acc, lds.base);
@@ -1466,9 +1522,12 @@ __device__ __forceinline__ void rebuild_scores(const MStep<R, G, 1>& lat, const 
   const bool hi_half = G == 8 && ((lane >> 4) & 1);
   const int tok = lane & 15;
   const bool masked = cb + tok >= ntok;  // a select, not a branch
+  // a select on the two values (a conditional over the two array elements
+  // would pick an address at run time and put sq in scratch memory)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float x = (QH == 2 && hi_half) ? sq[QH - 1][i] : sq[0][i];
+    const uint32_t x0 = __float_as_uint(sq[0][i]), x1 = __float_as_uint(sq[QH - 1][i]);
+    const float x = __uint_as_float(QH == 2 && hi_half ? x1 : x0);
     s[0][i] = masked ? -INFINITY : x;
   }
 }
@@ -1731,10 +1790,17 @@ void partition_rebuild_kernel(PartitionArgs a) {
 //      and the NG partials of each column are added in ascending order.
 // Every order is fixed, so results are bitwise reproducible.
 
-template <int R>
+// kStage floats of records are staged per round trip: 4096 (16 KB), or
+// 16384 (64 KB) for a head with more records than that (a long context cut
+// into hundreds of partitions), so that every record of the head arrives in
+// one round trip instead of one per 16 KB chunk.
+constexpr int kStageSmall = 4096;
+constexpr int kStageLarge = 16384;
+
+template <int R, int kStageFloats = kStageSmall>
 struct CombineLds {
   static constexpr int kNPG = kThreads / R;                 // partition groups
-  static constexpr int kStage = 4096;                       // staged floats
+  static constexpr int kStage = kStageFloats;               // staged floats
   static constexpr int kChunk = kStage / (R + kRecPad);     // partitions per chunk
   float4 stage[kStage / 4];
   float m[kNPG * R];
@@ -1794,13 +1860,13 @@ struct ProjTile {
 
 // 16-byte loads of records [p0, p0 + n) of one head into this thread's
 // share of the stage (slots tid + k * kThreads).
-template <int R>
+template <int R, int kStageFloats>
 __device__ __forceinline__ void load_chunk(const float* rec0, int p0, int n,
-                                           float4 (&v4)[CombineLds<R>::kStage / 4 / kThreads]) {
+                                           float4 (&v4)[kStageFloats / 4 / kThreads]) {
   constexpr int RS = R + kRecPad;
   const auto rr = make_rsrc(rec0 + (size_t)p0 * RS, (uint32_t)n * RS * 4u);
 #pragma unroll
-  for (int k = 0; k < CombineLds<R>::kStage / 4 / kThreads; ++k) {
+  for (int k = 0; k < kStageFloats / 4 / kThreads; ++k) {
     const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
         rr, (int)((threadIdx.x + k * kThreads) * 16u), 0, 0);
     v4[k] = make_float4(__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
@@ -1812,10 +1878,10 @@ __device__ __forceinline__ void load_chunk(const float* rec0, int p0, int n,
 // section 2.A compresses the modalities apart): the records of each set fold
 // into their own latent-space sum under the common running max and
 // denominator, and out = (acc_img . B_V_img[g] + acc_txt . B_V_txt[g]) / L.
-template <int R, int D, bool kModal, int ES>
+template <int R, int D, bool kModal, int ES, int kStageFloats = kStageSmall>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void combine_kernel(CombineArgs a) {
-  using CL = CombineLds<R>;
+  using CL = CombineLds<R, kStageFloats>;
   constexpr int RS = R + kRecPad;
   constexpr int kNPG = CL::kNPG, kChunk = CL::kChunk;
   constexpr int kPer = CL::kStage / 4 / kThreads;
@@ -1845,7 +1911,7 @@ void combine_kernel(CombineArgs a) {
   PT::load(rbv, tid, 0, bw);
   const float* rec0 = a.ws + ((size_t)b * a.Hq + hq) * (size_t)a.P * RS;
   float4 v4[kPer];
-  load_chunk<R>(rec0, 0, min(kChunk, a.P), v4);
+  load_chunk<R, kStageFloats>(rec0, 0, min(kChunk, a.P), v4);
 
   // No early exit for an empty sequence (np == 0): it runs the same steps
   // with nothing to fold and writes a zero row.  A branch here would let the
@@ -1882,7 +1948,7 @@ void combine_kernel(CombineArgs a) {
     for (int p0 = 0; p0 < cnt[st]; p0 += kChunk) {
       if (st > 0 || p0 > 0) {
         __syncthreads();  // previous chunk consumed
-        load_chunk<R>(rec0, beg[st] + p0, min(kChunk, cnt[st] - p0), v4);
+        load_chunk<R, kStageFloats>(rec0, beg[st] + p0, min(kChunk, cnt[st] - p0), v4);
       }
       // 2. stage (every slot is written: zeros past the chunk)
 #pragma unroll
@@ -2155,6 +2221,17 @@ hipError_t launch_cge(const CombineArgs& a, hipStream_t s) {
       return hipGetLastError();
     }
     return hipErrorInvalidValue;
+  }
+  if ((int64_t)a.P * (R + kRecPad) > kStageSmall) {
+    // every record of a head in one round trip (64 KB stage)
+    constexpr int K = kStageLarge;
+    switch (a.d) {
+      case 64: hipLaunchKernelGGL((combine_kernel<R, 64, false, ES, K>), grid, block, 0, s, a); break;
+      case 128: hipLaunchKernelGGL((combine_kernel<R, 128, false, ES, K>), grid, block, 0, s, a); break;
+      case 256: hipLaunchKernelGGL((combine_kernel<R, 256, false, ES, K>), grid, block, 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
   }
   switch (a.d) {
     case 64: hipLaunchKernelGGL((combine_kernel<R, 64, false, ES>), grid, block, 0, s, a); break;
