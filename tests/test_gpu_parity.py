@@ -188,6 +188,40 @@ def test_instantiation_matrix(lt, r, G, d):
     assert err <= TOL[lt], err
 
 
+@pytest.mark.parametrize("lt,r,G", [("bf16", 48, 1), ("bf16", 32, 2), ("bf16", 48, 8),
+                                    ("f32", 16, 1), ("f16", 64, 4), ("i8", 32, 1),
+                                    ("i8", 64, 8), ("bf16", 128, 1)])
+@pytest.mark.parametrize("splits", [16, 37, 64])
+def test_many_short_partitions(lt, r, G, splits):
+    """Many short partitions (16 to 64 per sequence, as the long-context
+    workload's 256) on the VALU partition kernel: lengths end inside, at and
+    one past a multiple of four partitions, one token into a partition, at
+    one token, and at zero (a zero row, the other rows unchanged); the result
+    matches the oracle and repeats bit for bit."""
+    import torch
+    T = 2000
+    S = -(-T // splits)
+    grp = 4 * S
+    lens = [T, grp, grp + 1, grp - 1, 1, S + 1, 3 * grp + 7]
+    base = "int8" if lt == "i8" else "tiny"
+    fdt = "f32" if lt == "f32" else ("f16" if lt == "f16" else "bf16")
+    kw = dict(B=len(lens), Hq=2 * G, Hkv=2, d=128, r=r, T=T, seq_lens=lens,
+              q_dtype=fdt, factor_dtype=fdt, factor_std=1.0 / np.sqrt(r))
+    if lt != "i8":
+        kw["latent_dtype"] = lt
+    w = workloads.make(base, seed=1500 + r + G + splits, **kw)
+    dev = to_device(w)
+    say(f"many short partitions latent={lt} r={r} G={G} splits={splits} lens={lens}")
+    got = run_decode(w, dev, num_splits=splits).cpu().numpy()
+    assert rel_rowmax(got, _full_oracle(w)) <= TOL[lt]
+    again = run_decode(w, dev, num_splits=splits).cpu().numpy()
+    assert np.array_equal(got, again)
+    # a sequence of length 0 gives a zero row
+    dev["seq_lens"] = torch.tensor([0] + lens[1:], dtype=torch.int32, device="cuda")
+    z = run_decode(w, dev, num_splits=splits).cpu().numpy()
+    assert (z[0] == 0).all() and np.array_equal(z[1:], got[1:])
+
+
 @pytest.mark.parametrize("r,d,fdt", [(128, 256, "f32"), (128, 64, "f32"), (48, 64, "bf16"),
                                      (16, 64, "f32"), (128, 128, "f16"), (48, 256, "f32")])
 def test_combine_projection_tiles(r, d, fdt):
@@ -269,12 +303,13 @@ def _dense_oracle(w):
                                     ("f16", 128, 2), ("f32", 64, 4), ("i8", 128, 1),
                                     ("i8", 64, 4)])
 def test_dense_decode_matches_oracle(lt, d, G):
-    """The dense baseline is exact attention over the uncompressed cache."""
+    """The dense baseline is exact attention over the uncompressed cache
+    (20 splits: one partition per wave on the VALU kernel)."""
     import rank_kv_cache_head_amd as lr
     w = _dense_case(lt, d, G, seed=500 + d + G)
     dev = to_device(w)
     say(f"dense {lt} d={d} G={G} lens={list(w.seq_lens)}")
-    for splits in (0, 3):
+    for splits in (0, 3, 20):
         got = lr.dense_decode(dev["q"], dev["L_K"], dev["L_V"], dev["seq_lens"], dev["scales"],
                               softmax_scale=w.softmax_scale, num_splits=splits)
         import torch
