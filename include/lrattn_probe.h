@@ -1,8 +1,8 @@
 /*
- * lrattn_probe.h - plain HBM streaming kernels shipped beside lrattn for
- * measurement: the attainable read / copy bandwidth of the device, and a copy
- * of known size against which hardware byte counters are calibrated.  They
- * compute nothing of the attention method.
+ * lrattn_probe.h - plain kernels shipped beside lrattn for measurement: the
+ * attainable read / copy bandwidth of the device, a copy of known size
+ * against which hardware byte counters are calibrated, and a shader-clock
+ * sample.  They compute nothing of the attention method.
  *
  * Same conventions as lrattn.h: device pointers, 16-byte aligned, caller-owned,
  * asynchronous on `stream`, negative lrattn_status on error, host-side
@@ -32,6 +32,16 @@ int lrattn_probe_read(const void* src, size_t bytes, float* sink, lrattn_stream 
 
 /* Copy `bytes` bytes (a multiple of 16) from `src` to `dst` (no overlap). */
 int lrattn_probe_copy(void* dst, const void* src, size_t bytes, lrattn_stream stream);
+
+/*
+ * Shader clock: one lane of one workgroup spins for about 5 us of the
+ * 100 MHz real-time counter and writes out[0] = shader-clock cycles
+ * (s_memtime) and out[1] = real-time ticks over that spin, so the clock in
+ * GHz is out[0] / out[1] / 10.  Enqueued on `stream` between other launches,
+ * it samples the clock they run at.  `out`: 2 uint64 of device memory,
+ * 16-byte aligned.
+ */
+int lrattn_probe_clock(uint64_t* out, lrattn_stream stream);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,7 @@ __all__ = [
     "modal_params_for", "modal_workspace_size", "modal_decode", "ModalDecoder",
     "AdaptiveParams", "adaptive_workspace_size", "adaptive_kernel", "adaptive_decode",
     "AdaptiveDecoder",
-    "probe_read", "probe_copy", "probe_sink_floats", "declared_symbols",
+    "probe_read", "probe_copy", "probe_clock", "probe_sink_floats", "declared_symbols",
     "F32", "BF16", "F16", "I8",
 ]
 
@@ -127,6 +127,7 @@ def lib() -> ctypes.CDLL:
         L.lrattn_probe_sink_floats.restype = ctypes.c_size_t
         L.lrattn_probe_read.argtypes = [_VP, ctypes.c_size_t, _VP, _VP]
         L.lrattn_probe_copy.argtypes = [_VP, _VP, ctypes.c_size_t, _VP]
+        L.lrattn_probe_clock.argtypes = [_VP, _VP]
         for fn in ("lrattn_plan", "lrattn_workspace_size", "lrattn_decode",
                    "lrattn_decode_static", "lrattn_partition",
                    "lrattn_combine", "lrattn_dense_decode", "lrattn_rebuild_decode",
@@ -136,7 +137,7 @@ def lib() -> ctypes.CDLL:
                    "lrattn_append", "lrattn_append_workspace_size",
                    "lrattn_shared_decode", "lrattn_shared_workspace_size",
                    "lrattn_probe_read",
-                   "lrattn_probe_copy"):
+                   "lrattn_probe_copy", "lrattn_probe_clock"):
             getattr(L, fn).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -662,6 +663,16 @@ def probe_read(src, sink, stream=None) -> None:
     nbytes = src.numel() * src.element_size()
     _check(lib().lrattn_probe_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)),
            "lrattn_probe_read")
+
+
+def probe_clock(out, stream=None) -> None:
+    """lrattn_probe_clock: enqueue a shader-clock sample into `out` (a
+    contiguous int64 tensor of 2 values): shader cycles and 100 MHz ticks
+    over ~5 us; GHz = out[0] / out[1] / 10."""
+    import torch
+    if out.dtype != torch.int64 or out.numel() < 2 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int64 tensor of at least 2 values")
+    _check(lib().lrattn_probe_clock(_ptr(out), _stream(stream)), "lrattn_probe_clock")
 
 
 def probe_copy(dst, src, stream=None) -> None:

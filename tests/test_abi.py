@@ -140,6 +140,8 @@ def test_probe_validation():
     assert L.lrattn_probe_read(ALIGNED, 15, ALIGNED, None) == -2
     assert L.lrattn_probe_read(ALIGNED, 0, ALIGNED, None) == -2
     assert L.lrattn_probe_copy(ALIGNED, MISALIGNED, 32, None) == -5
+    assert L.lrattn_probe_clock(None, None) == -1
+    assert L.lrattn_probe_clock(MISALIGNED, None) == -5
 
 
 def test_supported_matrix_plans():

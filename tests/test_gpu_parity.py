@@ -655,6 +655,22 @@ def test_probe_copy_and_read():
     assert torch.equal(dst, src)
 
 
+def test_probe_clock():
+    """The shader-clock sample reads a plausible clock (the part runs at up
+    to 2.4 GHz) over its ~5 us spin of the 100 MHz real-time counter."""
+    import torch
+    import rank_kv_cache_head_amd as lr
+    out = torch.zeros(4, dtype=torch.int64, device="cuda")
+    say("probe clock")
+    lr.probe_clock(out)
+    lr.probe_clock(out[2:])
+    torch.cuda.synchronize()
+    o = out.cpu().tolist()
+    for j in range(2):
+        assert 400 <= o[2 * j + 1] <= 5000, o
+        assert 0.3 <= o[2 * j] / o[2 * j + 1] / 10.0 <= 3.5, o
+
+
 def test_back_to_back_inputs_share_a_workspace():
     """Two different inputs decoded back to back on one workspace, no host
     sync in between: each result must come from its own call's partials."""
