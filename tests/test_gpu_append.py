@@ -1,12 +1,20 @@
 """GPU parity of the append step (lrattn_append) against the fp64 oracle.
 
 Float latents: the kernel sums exact products in fp32 and rounds once to the
-storage type, so every stored value must be a faithful rounding of the exact
-latent (within one storage step plus the fp32 summation bound), and nearly all
-must equal the oracle's nearest-even rounding.  int8 latents: the code is a
-floating-point decision taken in fp32 on the fp32 sums; codes must equal the
-oracle's except by one step where the exact value of row / scale lies within
-the fp32 error of a rounding tie, and scales must agree to fp32 accuracy.
+storage type.  Every stored value must be a faithful rounding of the exact
+latent (within one storage step plus the a-priori fp32 summation bound), and
+it may differ from the oracle's nearest-even rounding only where the exact
+value lies within the kernel's measured fp32 error of the midpoint between
+the two candidates.  int8 latents: the code is a floating-point decision taken
+in fp32 on the fp32 sums; codes must equal the oracle's except by one step
+where the exact row / scale lies within that measured error (plus the
+rounding of the scale and the division) of a rounding tie, and scales must
+agree to fp32 accuracy.
+
+The measured error comes from the same append stored as fp32 latents (the
+same kernels and summation order when the launch path is the same): its
+distance to the exact latent sizes the windows above.  No expected value
+comes from the GPU: every comparison is against the oracle.
 """
 import numpy as np
 import pytest
@@ -68,7 +76,25 @@ def _ulp(e, ldt):
     return np.exp2(np.maximum(ex, emin) - mant)
 
 
-def _check(inp, LK, LV, sc, positions, T, ldt):
+def _f32_error(B, Hkv, D, r, T, xdt, positions, seed):
+    """|fp32 sum - exact latent| of the kernel for these inputs, per row
+    [2, B, Hkv] (max over the r coordinates): the same append stored as
+    fp32 latents, compared with the oracle.  Sizes the tolerance windows
+    only."""
+    inp, LK, LV, _ = _run(B, Hkv, D, r, T, xdt, "f32", positions, seed)
+    x = oracle.as_float64(inp["x"], xdt)
+    exact = np.stack([ap.project(x, oracle.as_float64(inp["A_K"], xdt)),
+                      ap.project(x, oracle.as_float64(inp["A_V"], xdt))])
+    got = [_as_f64(LK, "f32"), _as_f64(LV, "f32")]
+    err = np.zeros((2, B, Hkv))
+    for kv in range(2):
+        for b, p in enumerate(positions):
+            if 0 <= p < T:
+                err[kv, b] = np.abs(got[kv][b, :, p, :] - exact[kv, b]).max(axis=1)
+    return err
+
+
+def _check(inp, LK, LV, sc, positions, T, ldt, meas=None):
     xdt = inp["dtype"]
     x = oracle.as_float64(inp["x"], xdt)
     AK = oracle.as_float64(inp["A_K"], xdt)
@@ -79,6 +105,7 @@ def _check(inp, LK, LV, sc, positions, T, ldt):
     bound = np.stack([np.einsum("bd,grd->bgr", np.abs(x), np.abs(AK)),
                       np.einsum("bd,grd->bgr", np.abs(x), np.abs(AV))]) * 2.0 ** -16
     B = x.shape[0]
+    counts = {"codes": 0, "window": 0}
     got_all = [_as_f64(LK, ldt), _as_f64(LV, ldt)]
     for kv in range(2):
         got = got_all[kv]
@@ -88,6 +115,9 @@ def _check(inp, LK, LV, sc, positions, T, ldt):
                 continue
             g = got[b, :, p, :]
             e, bd = exact[kv, b], bound[kv, b]
+            # the summation error allowed per row: measured (same launch
+            # path), else the a-priori bound
+            eb = bd if meas is None else np.broadcast_to(meas[kv, b][:, None], bd.shape)
             if ldt == "i8":
                 s_ex = scales[kv, b]
                 s_got = sc[kv, b, :, p].cpu().numpy().astype(np.float64)
@@ -95,16 +125,32 @@ def _check(inp, LK, LV, sc, positions, T, ldt):
                 assert (np.abs(s_got - s_ex) <= (bd.max(axis=1) + 1e-7 * s_ex) / 127.0 * 2).all()
                 safe = np.where(s_ex > 0, s_ex, 1.0)[:, None]
                 ratio = e / safe
-                err = bd / safe + np.abs(ratio) * 1e-5      # fp32 sums, scale and division
+                # fp32 sums, then the fp32 scale and division (2^-21 relative)
+                err = eb / safe + np.abs(ratio) * 2.0 ** -21
                 near_tie = np.abs(np.abs(ratio) % 1.0 - 0.5) <= err
                 diff = g - rows[kv, b]
                 assert (np.abs(diff) <= 1).all(), (kv, b)
                 assert (diff[~near_tie] == 0).all(), (kv, b)
+                if meas is not None:
+                    counts["codes"] += diff.size
+                    counts["window"] += int((diff != 0).sum())
             else:
                 assert (np.abs(g - e) <= _ulp(e, ldt) + bd).all(), (kv, b)
                 if ldt != "f32":   # fp32 storage keeps the fp32 sum itself
-                    same = (g == _round_to(e, ldt)).mean()
-                    assert same >= 0.98, same
+                    rne = _round_to(e, ldt)
+                    off = g != rne
+                    # a value off the nearest-even rounding of the exact
+                    # latent is the other neighbour of a near-tie: the exact
+                    # value lies within the summation error of their midpoint
+                    mid = (g + rne) / 2.0
+                    assert (np.abs(e - mid)[off] <= eb[off] * (1 + 2.0 ** -20)).all(), (kv, b)
+                    counts["codes"] += g.size
+                    counts["window"] += int(off.sum())
+    if meas is not None and counts["codes"]:
+        frac = counts["window"] / counts["codes"]
+        say(f"  {counts['window']} of {counts['codes']} values off the nearest rounding "
+            f"(exact value within the measured fp32 error of a tie)")
+        assert frac <= 5e-3, frac
     return got_all
 
 
@@ -134,8 +180,15 @@ def test_append_matches_oracle(B, Hkv, D, r, ldt, xdt):
     if B > 2:
         positions[1], positions[2] = -1, T        # outside the cache: not written
     say(f"append B={B} Hkv={Hkv} D={D} r={r} latent={ldt} x={xdt}")
-    inp, LK, LV, sc = _run(B, Hkv, D, r, T, xdt, ldt, positions, seed=900 + B + r)
-    got = _check(inp, LK, LV, sc, positions, T, ldt)
+    seed = 900 + B + r
+    meas = None
+    # int8 takes the two-launch path always, float latents the one-launch
+    # path on wide shapes: measure where the fp32 run shares the path
+    # (the header's rule: one launch when Hkv * 2 * r / 16 >= 192)
+    if ldt != "f32" and (ldt != "i8" or Hkv * 2 * (r // 16) < 192):
+        meas = _f32_error(B, Hkv, D, r, T, xdt, positions, seed)
+    inp, LK, LV, sc = _run(B, Hkv, D, r, T, xdt, ldt, positions, seed=seed)
+    got = _check(inp, LK, LV, sc, positions, T, ldt, meas)
     _untouched(got, positions, T, ldt)
 
 
