@@ -1803,11 +1803,24 @@ struct CombineLds {
   static constexpr int kStage = kStageFloats;               // staged floats
   static constexpr int kChunk = kStage / (R + kRecPad);     // partitions per chunk
   float4 stage[kStage / 4];
-  float m[kNPG * R];
-  float l[kNPG * R];
+  float w[kChunk];     // weight 2^(m_p - M) of each staged partition
+  float red[kWaves];   // per-wave maxima
+  float l[kNPG];
   float v[kNPG * R];
   float vt[R];
 };
+
+// Maximum of x over the workgroup (every thread gets it).  `red` is free
+// on entry; the caller synchronizes before writing it again.
+__device__ __forceinline__ float block_max(float x, float* red) {
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
 
 // The projection out[i] = sum_j v~[j] B_V[g][j][i] in 16-byte pieces of B_V
 // (ES bytes per element: EPP = 16 / ES columns a piece): thread (rg, c)
@@ -1940,7 +1953,11 @@ void combine_kernel(CombineArgs a) {
   // kNPG * R <= kThreads (r = 48 leaves 16 threads without a group)
   const int pg = tid / R, j = tid - pg * R;
   const bool folds = pg < kNPG;
-  float m = -FLT_MAX, L = 0.f, acc[NSET];
+  // One reference M for every partial of a staged chunk: the running
+  // maximum of the partitions' maxima, moved (and the sums rescaled) only
+  // between chunks.  Within a chunk each partition's weight 2^(m_p - M) is
+  // computed once, and the sums are plain weighted sums in a fixed order.
+  float M = -FLT_MAX, L = 0.f, acc[NSET];
 #pragma unroll
   for (int st = 0; st < NSET; ++st) acc[st] = 0.f;
 #pragma unroll
@@ -1954,46 +1971,53 @@ void combine_kernel(CombineArgs a) {
 #pragma unroll
       for (int k = 0; k < kPer; ++k) sm.stage[tid + k * kThreads] = v4[k];
       __syncthreads();
-      // 3. fold this chunk's partitions pg, pg + NPG, ... into set st
-      const int pc = folds ? min(kChunk, cnt[st] - p0) : 0;
-      for (int pp = pg; pp < pc; pp += kNPG) {
-        const float* rec = stage + pp * RS;
-        const float mp = rec[R];
-        const float nm = fmaxf(m, mp);
-        const float fa = fast_exp2(m - nm), fb = fast_exp2(mp - nm);
-        L = fmaf(L, fa, rec[R + 1] * fb);
+      // 3. the chunk's reference, its weights, then the weighted sums of
+      //    partitions pg, pg + NPG, ... into set st
+      const int pc = min(kChunk, cnt[st] - p0);
+      float mx = -FLT_MAX;
+      for (int i = tid; i < pc; i += kThreads) mx = fmaxf(mx, stage[i * RS + R]);
+      const float Mn = fmaxf(M, block_max(mx, sm.red));
+      for (int i = tid; i < pc; i += kThreads) sm.w[i] = fast_exp2(stage[i * RS + R] - Mn);
+      __syncthreads();
+      const float sc = fast_exp2(M - Mn);  // 0 on the first chunk
+      L *= sc;
 #pragma unroll
-        for (int u = 0; u < NSET; ++u) acc[u] = u == st ? fmaf(acc[u], fa, rec[j] * fb) : acc[u] * fa;
-        m = nm;
+      for (int u = 0; u < NSET; ++u) acc[u] *= sc;
+      M = Mn;
+      if (folds) {
+#pragma unroll 4
+        for (int pp = pg; pp < pc; pp += kNPG) {
+          const float wp = sm.w[pp];
+          const float* rec = stage + pp * RS;
+          acc[st] = fmaf(wp, rec[j], acc[st]);
+          L = fmaf(wp, rec[R + 1], L);
+        }
       }
     }
   }
+  // the groups' sums share M: the row is their plain sum, in ascending group
   if (folds) {
-    sm.m[tid] = m;
-    sm.l[tid] = L;
     sm.v[tid] = acc[0];
     if constexpr (kModal) vt1[tid] = acc[1];
+    if (j == 0) sm.l[pg] = L;
   }
   __syncthreads();
   if (tid < R) {
+    float s0 = sm.v[tid], s1 = 0.f, Lt = sm.l[0];
+    if constexpr (kModal) s1 = vt1[tid];
 #pragma unroll
     for (int q = 1; q < kNPG; ++q) {
-      const int item = q * R + tid;
-      const float mp = sm.m[item];
-      const float nm = fmaxf(m, mp);
-      const float fa = fast_exp2(m - nm), fb = fast_exp2(mp - nm);
-      L = fmaf(L, fa, sm.l[item] * fb);
-      acc[0] = fmaf(acc[0], fa, sm.v[item] * fb);
-      if constexpr (kModal) acc[1] = fmaf(acc[1], fa, vt1[item] * fb);
-      m = nm;
+      s0 += sm.v[q * R + tid];
+      if constexpr (kModal) s1 += vt1[q * R + tid];
+      Lt += sm.l[q];
     }
-    sm.vt[tid] = np > 0 ? acc[0] / L : 0.f;
-    if constexpr (kModal) vt1[kNPG * R + tid] = np > 0 ? acc[1] / L : 0.f;
+    sm.vt[tid] = np > 0 ? s0 / Lt : 0.f;
+    if constexpr (kModal) vt1[kNPG * R + tid] = np > 0 ? s1 / Lt : 0.f;
     // the row's final reference and denominator (attention weights of the
-    // step: 2^(logit - m) / L)
+    // step: 2^(logit - M) / L)
     if (a.stats != nullptr && tid == 0) {
-      a.stats[((size_t)b * a.Hq + hq) * 2] = m;
-      a.stats[((size_t)b * a.Hq + hq) * 2 + 1] = L;
+      a.stats[((size_t)b * a.Hq + hq) * 2] = M;
+      a.stats[((size_t)b * a.Hq + hq) * 2 + 1] = Lt;
     }
   }
   __syncthreads();

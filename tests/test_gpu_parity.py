@@ -191,18 +191,20 @@ def test_instantiation_matrix(lt, r, G, d):
 @pytest.mark.parametrize("lt,r,G", [("bf16", 48, 1), ("bf16", 32, 2), ("bf16", 48, 8),
                                     ("f32", 16, 1), ("f16", 64, 4), ("i8", 32, 1),
                                     ("i8", 64, 8), ("bf16", 128, 1)])
-@pytest.mark.parametrize("splits", [16, 37, 64])
-def test_many_short_partitions(lt, r, G, splits):
-    """Many short partitions (16 to 64 per sequence, as the long-context
-    workload's 256) on the VALU partition kernel: lengths end inside, at and
-    one past a multiple of four partitions, one token into a partition, at
-    one token, and at zero (a zero row, the other rows unchanged); the result
-    matches the oracle and repeats bit for bit."""
+@pytest.mark.parametrize("T,splits", [(2000, 16), (2000, 37), (2000, 64), (16384, 64),
+                                      (16640, 65), (8192, 256)])
+def test_many_short_partitions(lt, r, G, T, splits):
+    """Many short partitions per sequence on the VALU partition kernel (the
+    long-context workload takes 256), on short and long rows (256 splits of
+    8192 tokens: 32-token partitions; 64 and 65 splits of 16384 and 16640
+    tokens: 256-token partitions, an even and an odd count of them).
+    Lengths end inside, at and one past a run of two and of four partitions,
+    one token into a partition, at one token, and at zero (a zero row, the
+    other rows unchanged); the result matches the oracle and repeats bit for
+    bit."""
     import torch
-    T = 2000
     S = -(-T // splits)
-    grp = 4 * S
-    lens = [T, grp, grp + 1, grp - 1, 1, S + 1, 3 * grp + 7]
+    lens = [T, 4 * S, 4 * S + 1, 4 * S - 1, 2 * S, 2 * S + 1, 1, S + 1, 3 * S + 5]
     base = "int8" if lt == "i8" else "tiny"
     fdt = "f32" if lt == "f32" else ("f16" if lt == "f16" else "bf16")
     kw = dict(B=len(lens), Hq=2 * G, Hkv=2, d=128, r=r, T=T, seq_lens=lens,
@@ -211,7 +213,7 @@ def test_many_short_partitions(lt, r, G, splits):
         kw["latent_dtype"] = lt
     w = workloads.make(base, seed=1500 + r + G + splits, **kw)
     dev = to_device(w)
-    say(f"many short partitions latent={lt} r={r} G={G} splits={splits} lens={lens}")
+    say(f"many short partitions latent={lt} r={r} G={G} T={T} splits={splits} lens={lens}")
     got = run_decode(w, dev, num_splits=splits).cpu().numpy()
     assert rel_rowmax(got, _full_oracle(w)) <= TOL[lt]
     again = run_decode(w, dev, num_splits=splits).cpu().numpy()
