@@ -454,7 +454,7 @@ namespace {
 // (partitions x kv-heads x quads of sequences) to give every CU about three
 // workgroups; a partition is a whole number of 32-token steps, at least
 // kRebuildMinTokens.  An explicit num_splits is used as given.
-constexpr int64_t kRebuildBlocks = 768;
+constexpr int64_t kRebuildBlocks = 512;
 constexpr int64_t kRebuildMinTokens = 128;
 
 int rebuild_plan(const lrattn_params* p, Plan* pl) {

@@ -1457,9 +1457,24 @@ struct RQuads {
   static constexpr int kQ = G == 8 ? 2 : 1;
 };
 
-template <int R, int G, int D, class Rope>
+// B_K^T fragment (n, c) of this lane: held in registers (64 for r = 64,
+// d = 128) so the rebuild reads no LDS per tile, or, with 8 heads, whose
+// accumulators leave no room for them, read from the LDS copy.
+template <int R, int D>
+struct FragRegs {
+  u32x4 r[D / 16][R / 32];
+  __device__ u32x4 at(int n, int c) const { return r[n][c]; }
+};
+struct FragLds {
+  const u32x4* base;
+  int lane;
+  int kc;
+  __device__ u32x4 at(int n, int c) const { return base[(n * kc + c) * 64 + lane]; }
+};
+
+template <int R, int G, int D, class Rope, class Frag>
 __device__ __forceinline__ void rebuild_scores(const MStep<R, G, 1>& lat, const Rope& rope,
-                                               int cb, int ntok, int lane, const u32x4* frag,
+                                               int cb, int ntok, int lane, const Frag& fr,
                                                const float (&qf)[RQuads<G>::kQ][D / 16][4],
                                                float (&s)[1][4]) {
   using Rg = RGeo<R, D>;
@@ -1485,7 +1500,7 @@ __device__ __forceinline__ void rebuild_scores(const MStep<R, G, 1>& lat, const 
       kd[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        const u32x4 bk = frag[(nb * KC + c) * 64 + lane];
+        const u32x4 bk = fr.at(nb, c);
         const u32x4 lk = {lat.k[0][c][0], lat.k[0][c][1], lat.k[0][c][2], lat.k[0][c][3]};
         kd[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bk),
                                                          __builtin_bit_cast(bf16x8, lk), kd[hf], 0, 0, 0);
@@ -1544,7 +1559,7 @@ struct RPartLds {
 };
 
 template <int R, int G, int D, bool kRot>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G == 8 ? 2 : 3)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void partition_rebuild_kernel(PartitionArgs a) {
   using Mg = MGeo<R, G, 1>;
   using Rg = RGeo<R, D>;
@@ -1663,6 +1678,16 @@ void partition_rebuild_kernel(PartitionArgs a) {
     }
   }
   __syncthreads();  // the stage is free: its space holds the table tiles
+  using Frag = std::conditional_t<(G < 8), FragRegs<R, D>, FragLds>;
+  Frag fr;
+  if constexpr (G < 8) {
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) fr.r[n][c] = lds.frag[(n * KC + c) * 64 + lane];
+  } else {
+    fr = FragLds{lds.frag, lane, KC};
+  }
 
   // ---- the tiles.  Two tiles of latents in flight per wave: the loads of
   // tile k + 2 are issued as soon as tile k is done, so each tile's latency is
@@ -1709,9 +1734,9 @@ void partition_rebuild_kernel(PartitionArgs a) {
   auto tile = [&](MStep<R, G, 1>& lt, int cb, int buf) {
     float s[1][4];
     if constexpr (kRot)
-      rebuild_scores<R, G, D>(lt, RopeLds{&lds.rope[buf][0][0], lane}, cb, ntok, lane, lds.frag, qf, s);
+      rebuild_scores<R, G, D>(lt, RopeLds{&lds.rope[buf][0][0], lane}, cb, ntok, lane, fr, qf, s);
     else
-      rebuild_scores<R, G, D>(lt, RopeNone{}, cb, ntok, lane, lds.frag, qf, s);
+      rebuild_scores<R, G, D>(lt, RopeNone{}, cb, ntok, lane, fr, qf, s);
     softmax_values<R, G, 1>(s, lt, lane, mm, ll, acc, wl);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kRot) {
@@ -1772,7 +1797,10 @@ void partition_rebuild_kernel(PartitionArgs a) {
 // is what makes every partition's records visible to it: on this multi-XCD
 // part an in-kernel hand-off (last-arriving workgroup merges) needs an
 // agent-scope fence per workgroup, i.e. an L2 writeback each, which measured
-// several times slower than the second launch.
+// several times slower than the second launch; records stored write-through
+// (device-scope stores, no writeback) with a counter per head still cost
+// each workgroup two round trips at its end, 14% on the 256-partition
+// long-context workload before any merging.
 //
 // The kernel is latency-bound, so its loads are issued together, before
 // anything waits, as raw buffer loads bounded by their slices with no branch
@@ -1782,10 +1810,13 @@ void partition_rebuild_kernel(PartitionArgs a) {
 //      chunk of the head's records (16 bytes per load) -- speculatively, as
 //      the records past seq_len's last partition are never folded;
 //   2. the chunk is staged in LDS (further chunks: one round trip each);
-//   3. thread (pg, j) folds coordinate j over partitions pg, pg + NPG, ...
-//      in ascending order (online log-sum-exp rule; NPG = kThreads / r
-//      groups shorten the chain), then the NPG groups are folded in
-//      ascending order: v~ = acc / l;
+//   3. the chunk's reference M (the maximum of the running reference and
+//      the chunk's partition maxima; the running sums are rescaled when it
+//      moves) and each partition's weight 2^(m_p - M), once per partition;
+//      thread (pg, j) then adds w_p acc_p[j] and w_p l_p over partitions
+//      pg, pg + NPG, ... in ascending order (NPG = kThreads / r groups),
+//      and the NPG group sums, which share M, are added in ascending
+//      order: v~ = acc / l;
 //   4. thread (rg, c) forms the partial of its column chunk over its rows
 //      and the NG partials of each column are added in ascending order.
 // Every order is fixed, so results are bitwise reproducible.
