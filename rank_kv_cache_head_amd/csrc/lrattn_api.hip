@@ -451,8 +451,9 @@ int lrattn_modal_decode(const lrattn_params* p, int32_t image_tokens, const void
 namespace {
 // Rebuilt keys: each wave owns one sequence's partition, four sequences per
 // workgroup, so the default plan splits T into enough partitions for the grid
-// (partitions x kv-heads x quads of sequences) to give every CU about three
-// workgroups; a partition is a whole number of 32-token steps, at least
+// (partitions x kv-heads x quads of sequences) to give every CU about two
+// workgroups (the kernel runs two per CU); a partition is a whole number of
+// 32-token steps, at least
 // kRebuildMinTokens.  An explicit num_splits is used as given.
 constexpr int64_t kRebuildBlocks = 512;
 constexpr int64_t kRebuildMinTokens = 128;

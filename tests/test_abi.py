@@ -215,11 +215,11 @@ def test_rebuild_decode_validates_on_host():
 
 def test_rebuild_plan():
     """One wave per sequence partition, four sequences per workgroup: the
-    default plan gives about 768 workgroups of whole 32-token steps."""
+    default plan gives about 512 workgroups of whole 32-token steps."""
     for kw, want in [(dict(batch=16, num_q_heads=32, num_kv_heads=8, rank=64, max_seq_len=16384),
-                      (24, 704)),                 # 8 kv-heads x 4 quads x 24 partitions
+                      (16, 1024)),                # 8 kv-heads x 4 quads x 16 partitions
                      (dict(batch=8, num_q_heads=32, num_kv_heads=32, rank=32, max_seq_len=4096),
-                      (12, 352)),                 # 32 x 2 x 12
+                      (8, 512)),                  # 32 x 2 x 8
                      (dict(batch=5, num_q_heads=8, num_kv_heads=2, rank=64, max_seq_len=700),
                       (6, 128)),                  # floor of 128 tokens
                      (dict(batch=5, num_q_heads=8, num_kv_heads=2, rank=64, max_seq_len=700,
