@@ -28,7 +28,7 @@ __all__ = [
     "dense_params_for", "dense_decode", "DenseDecoder",
     "rebuild_plan", "rebuild_workspace_size", "rebuild_decode", "RebuildDecoder",
     "AppendParams", "append_workspace_size", "append", "Appender",
-    "shared_params_for", "shared_workspace_size", "shared_decode",
+    "shared_params_for", "shared_workspace_size", "shared_decode", "SharedDecoder",
     "modal_params_for", "modal_workspace_size", "modal_decode", "ModalDecoder",
     "AdaptiveParams", "adaptive_workspace_size", "adaptive_kernel", "adaptive_decode",
     "AdaptiveDecoder",
@@ -732,6 +732,36 @@ class Decoder:
     def combine(self):
         fn, args = self._combine
         _check(fn(*args), "lrattn_combine")
+        return self.out
+
+
+class SharedDecoder:
+    """lrattn_shared_decode on fixed buffers, marshalled once (see Decoder)."""
+
+    def __init__(self, q, L_K, L_V, B_K, B_V, seq_lens, scales=None, *, out=None,
+                 workspace=None, softmax_scale=None, num_splits: int = 0, out_dtype=None,
+                 stream=None):
+        import torch
+        p = shared_params_for(q, L_K, B_K, out_dtype=out_dtype, softmax_scale=softmax_scale,
+                              num_splits=num_splits)
+        if tuple(L_V.shape) != tuple(L_K.shape) or tuple(B_V.shape) != tuple(B_K.shape):
+            raise ValueError("L_V / B_V shapes differ from L_K / B_K")
+        if tuple(seq_lens.shape) != (p.batch,) or seq_lens.dtype != torch.int32:
+            raise ValueError("seq_lens must be int32 [B]")
+        if out is None:
+            out = torch.empty((p.batch, p.num_q_heads, p.head_dim),
+                              dtype=torch.float32 if p.out_dtype == F32 else torch.bfloat16,
+                              device=q.device)
+        ws, ws_bytes = _workspace(p, workspace, q.device, shared_workspace_size(p))
+        self.params, self.out, self.workspace = p, out, ws
+        self._keep = (q, L_K, L_V, B_K, B_V, seq_lens, scales)
+        self._fn = lib().lrattn_shared_decode
+        self._args = (ctypes.byref(p), _ptr(q), _ptr(L_K), _ptr(L_V), _ptr(B_K), _ptr(B_V),
+                      _ptr(scales), _ptr(seq_lens), _ptr(out), _ptr(ws), ws_bytes,
+                      _stream(stream))
+
+    def __call__(self):
+        _check(self._fn(*self._args), "lrattn_shared_decode")
         return self.out
 
 

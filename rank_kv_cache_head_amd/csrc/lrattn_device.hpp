@@ -88,6 +88,23 @@ __device__ __forceinline__ float row_max16(float x) {
   return x;
 }
 
+// Sum (maximum) over the lanes l, l ^ 16, l ^ 32 and l ^ 48, i.e. over the
+// four 16-lane rows at one position, in the order (x_a + x_b) + (x_c + x_d)
+// with a, b and c, d the pairs l ^ 16 joins; every lane of the four gets the
+// same bits.
+__device__ __forceinline__ float sum_quarters(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+__device__ __forceinline__ float max_quarters(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
 __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }

@@ -1441,16 +1441,6 @@ struct RopeLds {
   __device__ u32x4 sin(int n) const { return base[(2 * n + 1) * 64 + lane]; }
 };
 
-// Adds x over the lanes l, l ^ 16, l ^ 32 and l ^ 48 in the order
-// (x_a + x_b) + (x_c + x_d), with a, b and c, d the pairs l ^ 16 joins; every
-// lane of the four gets the same bits.
-__device__ __forceinline__ float sum_quarters(float x) {
-  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
-}
-
 // head quads of the score instruction: heads 0..3, and 4..7 for G = 8
 template <int G>
 struct RQuads {

@@ -159,59 +159,65 @@ hipError_t launch_r(const AbsorbHeadsArgs& a, hipStream_t s) {
 // Reading them once per head group multiplies the stream's traffic, and the
 // value sums of many heads (heads x r accumulators) are more than the VALU
 // can keep up with.  This kernel reads each tile once for up to 64 heads
-// (NHB blocks of 16) and runs both products on the matrix cores:
+// (NHB blocks of 16) and runs both products on the matrix cores, with the
+// token axis of each 16-token tile along the rows of the scores:
 //
-//   scores  S (16 heads x 16 tokens) = q~ . L_K^T with v_mfma_f32_16x16x32_bf16,
-//           q~ split exactly into three bf16 terms (the latents are bf16, so
-//           every product is exact and the sums are fp32);
-//   values  acc (16 heads x 16 coordinates) += P (16 heads x 32 tokens) .
-//           L_V (32 tokens x 16 coordinates), the weights P split into two
-//           bf16 terms (relative error below 2^-16).  The contraction runs
-//           over tokens, so L_V is needed with tokens contiguous: the
-//           workgroup stages each 64-token tile of L_V in LDS transposed
-//           ([coordinate][token], two buffers, one barrier per tile), and P
-//           goes through a small LDS tile per wave to the operand layout.
+//   scores  S^T (16 tokens x 16 heads) = L_K . q~^T with
+//           v_mfma_f32_16x16x32_bf16: the A operand is the K tile's rows as
+//           stored, the B operand q~ split exactly into three bf16 terms
+//           (the latents are bf16, so every product is exact and the sums
+//           are fp32).  Lane l receives tokens 4 (l / 16) + i (i < 4) of head
+//           l % 16, so every lane keeps the softmax state of one head.
+//   values  acc^T (16 coordinates x 16 heads) += L_V^T (16 coordinates x 32
+//           tokens) . P^T (32 tokens x 16 heads), the weights P split into two
+//           bf16 terms (relative error below 2^-16).  The weights are the
+//           B operand in the registers the scores left them in (k slots
+//           0-3: the first tile's tokens 4 (l / 16) + i, slots 4-7: the
+//           second tile's), and the A operand takes the same tokens of L_V
+//           from the LDS tile, stored as it arrives ([token][coordinate]),
+//           with the transposing LDS read ds_read_b64_tr_b16: in each 16-lane
+//           row, result slot k of lane i is element i % 4 of the 8-byte read
+//           of lane 4 k + i / 4, so lane j reads row j / 4 at columns
+//           4 (j % 4) .. + 3 of its 4 x 16 block and every lane receives one
+//           coordinate of 4 consecutive tokens.
 //
 // Workgroup: one (sequence, stream, group of up to 16 NHB heads, partition),
 // 2 NHB waves; wave w takes head block w % NHB (16 heads) and token half
 // w / NHB of every 64-token step; the two halves are merged at the end
-// (fixed order).  Waves 0-3 stage the tiles.  Scores and value accumulators
-// share one layout (lane l, register i: head 4 (l / 16) + i), so the lazily
-// moved softmax reference and its rescale stay within a lane.
+// (fixed order).  Waves 0-3 stage the tiles.
 
 namespace {
 
 constexpr int kOnceStep = 64;            // tokens per step (32 per wave)
-constexpr int kVtStride = 144;           // bytes per transposed V row: 64 tokens + pad
-constexpr int kPStride = 36;             // floats per P row: 32 tokens + pad
 
-// Transposed L_V row `row` keeps its tokens XOR 8 ((row / 8) % 8) (whole
-// 8-token chunks move): a staging write (at r = 128, 16 rows 8 apart with 4
-// consecutive tokens each) then spreads over the banks instead of hitting
-// one group, and an operand read (8 consecutive tokens of one row) stays
-// one contiguous 16-byte piece.
-__device__ __forceinline__ int vt_swizzle(int row) { return 8 * ((row >> 3) & 7); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Four consecutive tokens of one coordinate from a [token][coordinate] LDS
+// tile (see above for the lane pattern of the transposing read).
+__device__ __forceinline__ s16x4 read_tr(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<unsigned char*>(p)));
+}
 
 template <int R, int NHB>
 struct OnceLds {
-  static constexpr int kKStride = 2 * R + 16;  // bytes per K row: r bf16 + pad
-  alignas(16) unsigned char kt[2][kOnceStep * kKStride];  // L_K tiles [token][coordinate]
-  alignas(16) unsigned char vt[2][R * kVtStride];         // L_V tiles [coordinate][token]
-  alignas(16) float pw[2 * NHB][16 * kPStride];           // per wave: P [head][token]
+  static constexpr int kStride = 2 * R + 16;  // bytes per latent row: r bf16 + pad
+  alignas(16) unsigned char kt[2][kOnceStep * kStride];  // L_K tiles [token][coordinate]
+  alignas(16) unsigned char vt[2][kOnceStep * kStride];  // L_V tiles [token][coordinate]
   // the final merge reuses both K buffers: [head block][16 heads][R], m, l
-  static_assert(NHB * 16 * (R + 2) * 4 <= 2 * kOnceStep * kKStride, "merge area");
+  static_assert(NHB * 16 * (R + 2) * 4 <= 2 * kOnceStep * kStride, "merge area");
 };
 
 // Two waves per SIMD: at R = 128 the registers fit 256 without spills, and
-// with NHB = 2 two workgroups' LDS (2 x 79 KB) fit a CU, so a CU can run a
-// second workgroup while the first waits on memory.
+// with NHB = 2 two workgroups' LDS fit a CU, so a CU can run a second
+// workgroup while the first waits on memory.
 template <int R, int NHB>
 __global__ __launch_bounds__(128 * NHB) __attribute__((amdgpu_waves_per_eu(2)))
 void shared_once_kernel(SharedOnceArgs a) {
   constexpr int KC = R / 32;          // 32-wide steps of r (scores)
   constexpr int NBV = R / 16;         // 16-wide blocks of r (values)
   constexpr int RowB = 2 * R;         // bytes per latent row
-  constexpr int KS = OnceLds<R, NHB>::kKStride;
+  constexpr int KS = OnceLds<R, NHB>::kStride;
   constexpr int KV = kOnceStep * RowB / 16 / 256;  // 16-byte pieces per thread, tile and K|V
   const int p = blockIdx.x, b = blockIdx.z;
   constexpr int GH = 16 * NHB;        // heads per group
@@ -219,6 +225,7 @@ void shared_once_kernel(SharedOnceArgs a) {
   const int s = blockIdx.y / hgs, hg = blockIdx.y % hgs;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hb = wave % NHB, th = wave / NHB;
+  const int grp = lane >> 4, col = lane & 15;  // lane row (token quad) and head / coordinate
   const bool stager = NHB == 2 || wave < 4;  // waves 0-3 stage the tiles
   const int len = __builtin_amdgcn_readfirstlane(min(max(a.seq_lens[b], 0), a.T));
   const int t0 = p * a.Stok;
@@ -238,11 +245,11 @@ void shared_once_kernel(SharedOnceArgs a) {
   // Staging: piece k of thread t (t < 256) is piece 256 k + t of the tile's
   // 16-byte pieces in memory order (CPR = r / 8 pieces a row), so every load
   // instruction reads 1 KB of consecutive rows (16 rows x 64 bytes per
-  // instruction streamed 14% slower).  K goes to LDS as it is (rows padded
-  // by 16 bytes: the score operand reads of 16 rows at one column are
-  // conflict-free); V goes transposed (vt_swizzle).  Waves past the fourth
-  // load nothing (an offset past the buffer: zeros, no memory access) and
-  // write nothing.
+  // instruction streamed 14% slower).  Both tiles go to LDS as they are,
+  // rows padded by 16 bytes (the score operand reads of 16 rows at one
+  // column and the transposing reads of 16 rows spread over the banks).
+  // Waves past the fourth load nothing (an offset past the buffer: zeros,
+  // no memory access) and write nothing.
   constexpr int CPR = RowB / 16;
   const uint32_t soff = stager ? (uint32_t)(tid & 255) * 16u : kOffNone;
   struct Tile {
@@ -258,22 +265,17 @@ void shared_once_kernel(SharedOnceArgs a) {
   };
   auto stage_tile = [&](const Tile& tl, int buf) {
     if (!stager) return;
-    uint16_t* vt = reinterpret_cast<uint16_t*>(lds.vt[buf]);
 #pragma unroll
     for (int k = 0; k < KV; ++k) {
-      const int pc = 256 * k + (tid & 255), tk = pc / CPR, cg = pc % CPR, col = 8 * cg;
+      const int pc = 256 * k + (tid & 255), tk = pc / CPR, cg = pc % CPR;
       *reinterpret_cast<u32x4*>(lds.kt[buf] + tk * KS + cg * 16) = tl.k[k];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = col + j;
-        vt[row * (kVtStride / 2) + (tk ^ vt_swizzle(row))] = (uint16_t)(tl.v[k][j / 2] >> (16 * (j & 1)));
-      }
+      *reinterpret_cast<u32x4*>(lds.vt[buf] + tk * KS + cg * 16) = tl.v[k];
     }
   };
 
-  // ---- prologue: q~ of the wave's 16 heads (A operands), the first tiles
+  // ---- prologue: q~ of the wave's 16 heads (B operands), the first tiles
   Tile ta, tb;
-  bf16x8 qa[3][KC];
+  bf16x8 qb[3][KC];
   {
     const auto rq = make_rsrc(a.qt + ((size_t)b * a.Hq + head0) * R, (uint32_t)nvalid * R * 4u);
     u32x4 qw[KC][2];
@@ -282,7 +284,7 @@ void shared_once_kernel(SharedOnceArgs a) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         qw[c][h] = __builtin_amdgcn_raw_buffer_load_b128(
-            rq, (int)(((lane & 15) * R + 32 * c + 8 * (lane >> 4) + 4 * h) * 4u), 0, 0);
+            rq, (int)((col * R + 32 * c + 8 * grp + 4 * h) * 4u), 0, 0);
     }
     load_tile(ta, 0);
     load_tile(tb, kOnceStep);
@@ -294,22 +296,21 @@ void shared_once_kernel(SharedOnceArgs a) {
       bf16x8 t3[3];
       split3x8(x, t3);
 #pragma unroll
-      for (int term = 0; term < 3; ++term) qa[term][c] = t3[term];
+      for (int term = 0; term < 3; ++term) qb[term][c] = t3[term];
     }
     stage_tile(ta, 0);
   }
   __syncthreads();
 
+  // acc[n][i]: coordinate 16 n + 4 grp + i of head col; mm, ll: head col's
+  // reference max and (this lane's part of) its sum
   f32x4 acc[NBV];
 #pragma unroll
   for (int n = 0; n < NBV; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mm[4], ll[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    mm[i] = -FLT_MAX;
-    ll[i] = 0.f;
-  }
-  float* pw = lds.pw[wave];
+  float mm = -FLT_MAX, ll = 0.f;
+  // this lane's transposing-read address in a V tile, for the first tile's
+  // token quad: row 32 th + 4 grp + col / 4, columns 4 (col % 4) .. + 3
+  const int vaddr = (32 * th + 4 * grp + (col >> 2)) * KS + 8 * (col & 3);
   // One 64-token step at cb from LDS buffer buf: the tile two steps ahead is
   // requested into tn, the next step's (requested a step earlier, in tp) is
   // staged into the other buffer at the end, so every latent load has a
@@ -318,7 +319,7 @@ void shared_once_kernel(SharedOnceArgs a) {
   // masked scores and adds nothing.
   auto step = [&](int cb, int buf, Tile& tn, const Tile& tp) {
     load_tile(tn, cb + 2 * kOnceStep);
-    // scores of the wave's two 16-token tiles (B operand: token l % 16,
+    // scores of the wave's two 16-token tiles (A operand: token l % 16,
     // columns 32 c + 8 (l / 16) .. + 7, from the K tile)
     const unsigned char* kt = lds.kt[buf];
     f32x4 sc[2];
@@ -327,78 +328,75 @@ void shared_once_kernel(SharedOnceArgs a) {
       sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        const u32x4 kb = *reinterpret_cast<const u32x4*>(
-            kt + (32 * th + 16 * t + (lane & 15)) * KS + 64 * c + 16 * (lane >> 4));
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(
+            kt + (32 * th + 16 * t + col) * KS + 64 * c + 16 * grp);
 #pragma unroll
         for (int term = 0; term < 3; ++term)
           sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              qa[term][c], __builtin_bit_cast(bf16x8, kb), sc[t], 0, 0, 0);
+              __builtin_bit_cast(bf16x8, ka), qb[term][c], sc[t], 0, 0, 0);
       }
     }
-    // mask, then the lazily moved reference per head (lanes with equal l / 16)
+    // mask, then the lazily moved reference of head col (lanes col + 16 q)
     float sv[2][4];
     bool need = false;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const bool masked = cb + 32 * th + 16 * t + (lane & 15) >= ntok;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        const bool masked = cb + 32 * th + 16 * t + 4 * grp + i >= ntok;
         sv[t][i] = masked ? -INFINITY : sc[t][i];
-        need |= sv[t][i] > mm[i] + kLazyLog2;
+        need |= sv[t][i] > mm + kLazyLog2;
       }
     }
     if (__builtin_amdgcn_ballot_w64(need)) {
+      float x = sv[0][0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = row_max16(fmaxf(sv[0][i], sv[1][i]));
-        const float nm = x > mm[i] + kLazyLog2 ? x : mm[i];
-        const float corr = fast_exp2(mm[i] - nm);
-        mm[i] = nm;
-        ll[i] *= corr;
+      for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int n = 0; n < NBV; ++n) acc[n][i] *= corr;
+        for (int i = 0; i < 4; ++i) x = fmaxf(x, sv[t][i]);
+      }
+      x = max_quarters(x);
+      const float nm = x > mm + kLazyLog2 ? x : mm;
+      const float corr = fast_exp2(mm - nm);
+      mm = nm;
+      ll *= corr;
+#pragma unroll
+      for (int n = 0; n < NBV; ++n) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[n][i] *= corr;
       }
     }
-    // weights into the wave's P tile [head][token]
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = fast_exp2(sv[t][i] - mm[i]);
-        ll[i] += e;
-        pw[(4 * (lane >> 4) + i) * kPStride + 16 * t + (lane & 15)] = e;
-      }
-    }
-    // the other lanes' weights are read below
-    wave_sync();
-    // A operand: head l % 16, tokens 8 (l / 16) .. + 7, as hi + lo bf16
-    bf16x8 pa[2];
+    // weights as the B operand (k slot 4 t + i: token 16 t + 4 grp + i of
+    // the wave's half), hi + lo bf16
+    bf16x8 pb[2];
     {
-      const float4 w0 = *reinterpret_cast<const float4*>(pw + (lane & 15) * kPStride + 8 * (lane >> 4));
-      const float4 w1 = *reinterpret_cast<const float4*>(pw + (lane & 15) * kPStride + 8 * (lane >> 4) + 4);
-      const float x[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
       u32x4 hw, lw;
 #pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const bf16x2 h = cvt2(x[j], x[j + 1]);
-        const bf16x2 l = cvt2(x[j] - (float)h[0], x[j + 1] - (float)h[1]);
-        hw[j / 2] = __builtin_bit_cast(uint32_t, h);
-        lw[j / 2] = __builtin_bit_cast(uint32_t, l);
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float e0 = fast_exp2(sv[t][i] - mm), e1 = fast_exp2(sv[t][i + 1] - mm);
+          ll += e0;
+          ll += e1;
+          const bf16x2 h = cvt2(e0, e1);
+          const bf16x2 l = cvt2(e0 - (float)h[0], e1 - (float)h[1]);
+          hw[2 * t + i / 2] = __builtin_bit_cast(uint32_t, h);
+          lw[2 * t + i / 2] = __builtin_bit_cast(uint32_t, l);
+        }
       }
-      pa[0] = __builtin_bit_cast(bf16x8, hw);
-      pa[1] = __builtin_bit_cast(bf16x8, lw);
+      pb[0] = __builtin_bit_cast(bf16x8, hw);
+      pb[1] = __builtin_bit_cast(bf16x8, lw);
     }
-    // values: acc[n] += P . L_V[:, 16 n .. 16 n + 15]
-    const unsigned char* vt = lds.vt[buf];
+    // values: acc[n] += L_V[tokens, 16 n .. 16 n + 15]^T . P^T
+    const unsigned char* vt = lds.vt[buf] + vaddr;
 #pragma unroll
     for (int n = 0; n < NBV; ++n) {
-      const int row = 16 * n + (lane & 15);
-      const u32x4 vb = *reinterpret_cast<const u32x4*>(
-          vt + row * kVtStride + ((32 * th + 8 * (lane >> 4)) ^ vt_swizzle(row)) * 2);
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], __builtin_bit_cast(bf16x8, vb),
-                                                       acc[n], 0, 0, 0);
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], __builtin_bit_cast(bf16x8, vb),
-                                                       acc[n], 0, 0, 0);
+      const s16x4 v0 = read_tr(vt + 32 * n);
+      const s16x4 v1 = read_tr(vt + 16 * KS + 32 * n);
+      const s16x4 v8[2] = {v0, v1};
+      const bf16x8 va = __builtin_bit_cast(bf16x8, v8);
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0], acc[n], 0, 0, 0);
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[1], acc[n], 0, 0, 0);
     }
     stage_tile(tp, buf ^ 1);
     __syncthreads();
@@ -409,46 +407,36 @@ void shared_once_kernel(SharedOnceArgs a) {
   }
 
   // ---- merge the two token halves of each head block, write the records
-  float l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) l[i] = group_sum<16>(ll[i]);
+  const float lsum = sum_quarters(ll);
   float* mrg = reinterpret_cast<float*>(lds.kt[0]);  // [hb][16 heads][R], then m, l
   float* mrg_m = mrg + NHB * 16 * R;
   float* mrg_l = mrg_m + NHB * 16;
   if (th == 1) {
 #pragma unroll
-    for (int n = 0; n < NBV; ++n) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        mrg[(hb * 16 + 4 * (lane >> 4) + i) * R + 16 * n + (lane & 15)] = acc[n][i];
-    }
-    if ((lane & 15) == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        mrg_m[hb * 16 + 4 * (lane >> 4) + i] = mm[i];
-        mrg_l[hb * 16 + 4 * (lane >> 4) + i] = l[i];
-      }
+    for (int n = 0; n < NBV; ++n)
+      *reinterpret_cast<f32x4*>(&mrg[(hb * 16 + col) * R + 16 * n + 4 * grp]) = acc[n];
+    if (grp == 0) {
+      mrg_m[hb * 16 + col] = mm;
+      mrg_l[hb * 16 + col] = lsum;
     }
   }
   __syncthreads();
-  if (th == 0) {
+  if (th == 0 && col < nvalid) {
+    const float m1 = mrg_m[hb * 16 + col], l1 = mrg_l[hb * 16 + col];
+    const float M = fmaxf(mm, m1);
+    const float f0 = fast_exp2(mm - M), f1 = fast_exp2(m1 - M);
+    float* rec = a.ws + (((size_t)b * a.Hq + head0 + col) * a.P + p) * (R + kRecPad);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hr = 4 * (lane >> 4) + i;  // head row in the block
-      if (hr >= nvalid) continue;
-      const float m1 = mrg_m[hb * 16 + hr], l1 = mrg_l[hb * 16 + hr];
-      const float M = fmaxf(mm[i], m1);
-      const float f0 = fast_exp2(mm[i] - M), f1 = fast_exp2(m1 - M);
-      float* rec = a.ws + (((size_t)b * a.Hq + head0 + hr) * a.P + p) * (R + kRecPad);
+    for (int n = 0; n < NBV; ++n) {
+      const f32x4 o = *reinterpret_cast<const f32x4*>(&mrg[(hb * 16 + col) * R + 16 * n + 4 * grp]);
+      f32x4 r;
 #pragma unroll
-      for (int n = 0; n < NBV; ++n) {
-        const float o = mrg[(hb * 16 + hr) * R + 16 * n + (lane & 15)];
-        rec[16 * n + (lane & 15)] = fmaf(acc[n][i], f0, o * f1);
-      }
-      if ((lane & 15) == 0) {
-        rec[R] = M;
-        rec[R + 1] = fmaf(l[i], f0, l1 * f1);
-      }
+      for (int i = 0; i < 4; ++i) r[i] = fmaf(acc[n][i], f0, o[i] * f1);
+      *reinterpret_cast<f32x4*>(&rec[16 * n + 4 * grp]) = r;
+    }
+    if (grp == 0) {
+      rec[R] = M;
+      rec[R + 1] = fmaf(lsum, f0, l1 * f1);
     }
   }
 }
