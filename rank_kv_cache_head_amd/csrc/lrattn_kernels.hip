@@ -795,9 +795,17 @@ __device__ __forceinline__ void write_records(const PartitionArgs& a, int b, int
   }
 }
 
+// Occupancy target of a VALU partition kernel: the geometry's, except that
+// the two-segment form of fp32 latents with 8 heads needs a few registers
+// more than 128 (one spilled at 4 waves per SIMD).
+template <class LT, int R, int G, bool kSeg>
+constexpr int valu_waves() {
+  return kSeg && LT::kBytes == 4 && G == 8 ? 2 : Geo<LT, R, G>::kWavesPerEU;
+}
+
 template <class LT, int R, int G, int kAux = kNonTemporal, bool kAd = false, bool kSeg = false>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(Geo<LT, R, G>::kWavesPerEU)))
+__attribute__((amdgpu_waves_per_eu(valu_waves<LT, R, G, kSeg>())))
 void partition_kernel(PartitionArgs a) {
   using Gm = Geo<LT, R, G>;
   constexpr int EPL = Gm::kEPL, LPR = Gm::kLPR, CH = Gm::kChunk;
@@ -1462,11 +1470,23 @@ struct FragLds {
   __device__ u32x4 at(int n, int c) const { return base[(n * kc + c) * 64 + lane]; }
 };
 
-template <int R, int G, int D, class Rope, class Frag>
+// The query operand of the score instruction, q'[head][16 n + 4 (l / 16) + i]
+// for quad qh: held in registers, or, with 8 heads (whose accumulators and
+// fragments leave no room for them), read from the wave's LDS copy of q'.
+template <int G, int D>
+struct QfRegs {
+  float v[RQuads<G>::kQ][D / 16][4];
+  __device__ float at(int qh, int n, int i) const { return v[qh][n][i]; }
+};
+struct QfLds {
+  const float* row[2];  // the lane's q' row of each quad, from column 4 (l / 16)
+  __device__ float at(int qh, int n, int i) const { return row[qh][16 * n + i]; }
+};
+
+template <int R, int G, int D, class Rope, class Frag, class Qf>
 __device__ __forceinline__ void rebuild_scores(const MStep<R, G, 1>& lat, const Rope& rope,
                                                int cb, int ntok, int lane, const Frag& fr,
-                                               const float (&qf)[RQuads<G>::kQ][D / 16][4],
-                                               float (&s)[1][4]) {
+                                               const Qf& qf, float (&s)[1][4]) {
   using Rg = RGeo<R, D>;
   constexpr int KC = Rg::kKC, NH = Rg::kHalf, QH = RQuads<G>::kQ;
   constexpr bool kRot = !std::is_same<Rope, RopeNone>::value;
@@ -1512,7 +1532,7 @@ __device__ __forceinline__ void rebuild_scores(const MStep<R, G, 1>& lat, const 
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int qh = 0; qh < QH; ++qh)
-          sd[qh] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[qh][n + hf * NH][i], kd[hf][i], sd[qh], 0, 0, 0);
+          sd[qh] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf.at(qh, n + hf * NH, i), kd[hf][i], sd[qh], 0, 0, 0);
       }
     }
   }
@@ -1541,7 +1561,8 @@ template <int R, int G, int D>
 struct RPartLds {
   union {
     uint16_t stage[R * D];                         // B_K[g] as stored, for the gather
-    u32x4 rope[2][RGeo<R, D>::kRopeEntries / 64][64];  // table tiles, two buffers
+    // table rows of two 16-token tiles per buffer, two buffers: [buffer][tile][piece][lane]
+    u32x4 rope[2][2][RGeo<R, D>::kRopeEntries / 64][64];
   };
   u32x4 frag[D * R / 8];       // B_K^T fragments [n][c][lane]
   float q[kWaves][G * D];      // q' = qscale * rotate(q, seq_len - 1) of each wave's sequence
@@ -1657,15 +1678,21 @@ void partition_rebuild_kernel(PartitionArgs a) {
   }
   // query operand of the score instruction: lane l is row l % 4 of its block,
   // head (l % 4) % G of quad qh; instruction (n, i) takes d = 16 n + 4 (l / 16) + i
-  float qf[RQuads<G>::kQ][D / 16][4];
+  using Qf = std::conditional_t<(G < 8), QfRegs<G, D>, QfLds>;
+  Qf qf;
+  if constexpr (G < 8) {
 #pragma unroll
-  for (int qh = 0; qh < RQuads<G>::kQ; ++qh) {
-    const float* qrow = lds.q[wave] + (4 * qh + (lane & 3) % G) * D + 4 * (lane >> 4);
+    for (int qh = 0; qh < RQuads<G>::kQ; ++qh) {
+      const float* qrow = lds.q[wave] + (4 * qh + (lane & 3) % G) * D + 4 * (lane >> 4);
 #pragma unroll
-    for (int n = 0; n < D / 16; ++n) {
+      for (int n = 0; n < D / 16; ++n) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qf[qh][n][i] = qrow[16 * n + i];
+        for (int i = 0; i < 4; ++i) qf.v[qh][n][i] = qrow[16 * n + i];
+      }
     }
+  } else {
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) qf.row[qh] = lds.q[wave] + (4 * qh + (lane & 3)) * D + 4 * (lane >> 4);
   }
   __syncthreads();  // the stage is free: its space holds the table tiles
   using Frag = std::conditional_t<(G < 8), FragRegs<R, D>, FragLds>;
@@ -1681,27 +1708,39 @@ void partition_rebuild_kernel(PartitionArgs a) {
 
   // ---- the tiles.  Two tiles of latents in flight per wave: the loads of
   // tile k + 2 are issued as soon as tile k is done, so each tile's latency is
-  // covered by a whole tile of work.  The table tile k + 1 is loaded into
-  // registers during tile k and written to the other LDS buffer at its end.
+  // covered by a whole tile of work.  The table rows go through LDS two tiles
+  // (32 tokens) at a time: those of the next pair are loaded into registers
+  // during a pair and written to the other LDS buffer at its end, before the
+  // one barrier per pair.
   // The loop runs to the quad's longest partition (every wave takes part in
   // every barrier); a wave past its own end, or an odd last tile, sees loads
   // that return zeros (outside its buffer's range) and scores masked to -inf,
   // and adds nothing.  The scheduling barriers keep the issue order, which
   // the waits on in-order load returns rely on.
-  u32x4 rp[EPT];
+  u32x4 rp[2][EPT];
+  auto load_table = [&](int row) {  // the pair of table tiles from row t0 + row
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int k = 0; k < EPT; ++k)
+        rp[u][k] = __builtin_amdgcn_raw_buffer_load_b128(
+            rr, (int)(roff[k] + (uint32_t)(row + u * CH) * D * 4u), 0, 0);
+    }
+  };
+  auto store_table = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) (&lds.rope[buf][u][0][0])[tid + k * kThreads] = rp[u][k];
+    }
+  };
   if constexpr (kRot) {
-#pragma unroll
-    for (int k = 0; k < EPT; ++k) rp[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)roff[k], 0, 0);
-#pragma unroll
-    for (int k = 0; k < EPT; ++k) (&lds.rope[0][0][0])[tid + k * kThreads] = rp[k];
+    load_table(0);
+    store_table(0);
   }
   MStep<R, G, 1> l0, l1;
   load_mstep<R, G, 1>(l0, 0, koff, voff, rk, rv);
-  if constexpr (kRot) {
-#pragma unroll
-    for (int k = 0; k < EPT; ++k)
-      rp[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(roff[k] + CH * D * 4u), 0, 0);
-  }
+  if constexpr (kRot) load_table(2 * CH);
   __builtin_amdgcn_sched_barrier(0);
   load_mstep<R, G, 1>(l1, CH, koff, voff, rk, rv);
   __builtin_amdgcn_sched_barrier(0);
@@ -1719,30 +1758,33 @@ void partition_rebuild_kernel(PartitionArgs a) {
     ll[i] = 0.f;
   }
   float* wl = lds.w + wave * CH * G;
-  // one tile: scores, softmax and values; then the next table tile into the
-  // other buffer, the loads two tiles ahead, and the barrier
-  auto tile = [&](MStep<R, G, 1>& lt, int cb, int buf) {
+  // one tile (tile u of the pair in table buffer buf): scores, softmax and
+  // values, then the latent loads two tiles ahead; after the pair's second
+  // tile, the next pair's table rows into the other buffer, the rows of the
+  // pair after it into registers, and the barrier
+  auto tile = [&](MStep<R, G, 1>& lt, int cb, int buf, int u) {
     float s[1][4];
     if constexpr (kRot)
-      rebuild_scores<R, G, D>(lt, RopeLds{&lds.rope[buf][0][0], lane}, cb, ntok, lane, fr, qf, s);
+      rebuild_scores<R, G, D>(lt, RopeLds{&lds.rope[buf][u][0][0], lane}, cb, ntok, lane, fr, qf, s);
     else
       rebuild_scores<R, G, D>(lt, RopeNone{}, cb, ntok, lane, fr, qf, s);
     softmax_values<R, G, 1>(s, lt, lane, mm, ll, acc, wl);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kRot) {
-#pragma unroll
-      for (int k = 0; k < EPT; ++k) (&lds.rope[buf ^ 1][0][0])[tid + k * kThreads] = rp[k];
-#pragma unroll
-      for (int k = 0; k < EPT; ++k)
-        rp[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(roff[k] + (uint32_t)(cb + 2 * CH) * D * 4u), 0, 0);
+      if (u == 1) {
+        store_table(buf ^ 1);
+        load_table(cb - CH + 4 * CH);
+      }
     }
     load_mstep<R, G, 1>(lt, cb + 2 * CH, koff, voff, rk, rv);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kRot) __syncthreads();
+    if constexpr (kRot) {
+      if (u == 1) __syncthreads();
+    }
   };
-  for (int cb = 0; cb < nmax; cb += 2 * CH) {
-    tile(l0, cb, 0);
-    tile(l1, cb + CH, 1);
+  for (int cb = 0, buf = 0; cb < nmax; cb += 2 * CH, buf ^= 1) {
+    tile(l0, cb, buf, 0);
+    tile(l1, cb + CH, buf, 1);
   }
 
   // ---- this wave's records: (acc, m, l) of its G heads
