@@ -1561,8 +1561,7 @@ template <int R, int G, int D>
 struct RPartLds {
   union {
     uint16_t stage[R * D];                         // B_K[g] as stored, for the gather
-    // table rows of two 16-token tiles per buffer, two buffers: [buffer][tile][piece][lane]
-    u32x4 rope[2][2][RGeo<R, D>::kRopeEntries / 64][64];
+    u32x4 rope[2][RGeo<R, D>::kRopeEntries / 64][64];  // table tiles, two buffers
   };
   u32x4 frag[D * R / 8];       // B_K^T fragments [n][c][lane]
   float q[kWaves][G * D];      // q' = qscale * rotate(q, seq_len - 1) of each wave's sequence
@@ -1708,39 +1707,27 @@ void partition_rebuild_kernel(PartitionArgs a) {
 
   // ---- the tiles.  Two tiles of latents in flight per wave: the loads of
   // tile k + 2 are issued as soon as tile k is done, so each tile's latency is
-  // covered by a whole tile of work.  The table rows go through LDS two tiles
-  // (32 tokens) at a time: those of the next pair are loaded into registers
-  // during a pair and written to the other LDS buffer at its end, before the
-  // one barrier per pair.
+  // covered by a whole tile of work.  The table tile k + 1 is loaded into
+  // registers during tile k and written to the other LDS buffer at its end.
   // The loop runs to the quad's longest partition (every wave takes part in
   // every barrier); a wave past its own end, or an odd last tile, sees loads
   // that return zeros (outside its buffer's range) and scores masked to -inf,
   // and adds nothing.  The scheduling barriers keep the issue order, which
   // the waits on in-order load returns rely on.
-  u32x4 rp[2][EPT];
-  auto load_table = [&](int row) {  // the pair of table tiles from row t0 + row
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int k = 0; k < EPT; ++k)
-        rp[u][k] = __builtin_amdgcn_raw_buffer_load_b128(
-            rr, (int)(roff[k] + (uint32_t)(row + u * CH) * D * 4u), 0, 0);
-    }
-  };
-  auto store_table = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int k = 0; k < EPT; ++k) (&lds.rope[buf][u][0][0])[tid + k * kThreads] = rp[u][k];
-    }
-  };
+  u32x4 rp[EPT];
   if constexpr (kRot) {
-    load_table(0);
-    store_table(0);
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) rp[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)roff[k], 0, 0);
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) (&lds.rope[0][0][0])[tid + k * kThreads] = rp[k];
   }
   MStep<R, G, 1> l0, l1;
   load_mstep<R, G, 1>(l0, 0, koff, voff, rk, rv);
-  if constexpr (kRot) load_table(2 * CH);
+  if constexpr (kRot) {
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+      rp[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(roff[k] + CH * D * 4u), 0, 0);
+  }
   __builtin_amdgcn_sched_barrier(0);
   load_mstep<R, G, 1>(l1, CH, koff, voff, rk, rv);
   __builtin_amdgcn_sched_barrier(0);
@@ -1758,33 +1745,30 @@ void partition_rebuild_kernel(PartitionArgs a) {
     ll[i] = 0.f;
   }
   float* wl = lds.w + wave * CH * G;
-  // one tile (tile u of the pair in table buffer buf): scores, softmax and
-  // values, then the latent loads two tiles ahead; after the pair's second
-  // tile, the next pair's table rows into the other buffer, the rows of the
-  // pair after it into registers, and the barrier
-  auto tile = [&](MStep<R, G, 1>& lt, int cb, int buf, int u) {
+  // one tile: scores, softmax and values; then the next table tile into the
+  // other buffer, the loads two tiles ahead, and the barrier
+  auto tile = [&](MStep<R, G, 1>& lt, int cb, int buf) {
     float s[1][4];
     if constexpr (kRot)
-      rebuild_scores<R, G, D>(lt, RopeLds{&lds.rope[buf][u][0][0], lane}, cb, ntok, lane, fr, qf, s);
+      rebuild_scores<R, G, D>(lt, RopeLds{&lds.rope[buf][0][0], lane}, cb, ntok, lane, fr, qf, s);
     else
       rebuild_scores<R, G, D>(lt, RopeNone{}, cb, ntok, lane, fr, qf, s);
     softmax_values<R, G, 1>(s, lt, lane, mm, ll, acc, wl);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kRot) {
-      if (u == 1) {
-        store_table(buf ^ 1);
-        load_table(cb - CH + 4 * CH);
-      }
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) (&lds.rope[buf ^ 1][0][0])[tid + k * kThreads] = rp[k];
+#pragma unroll
+      for (int k = 0; k < EPT; ++k)
+        rp[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(roff[k] + (uint32_t)(cb + 2 * CH) * D * 4u), 0, 0);
     }
     load_mstep<R, G, 1>(lt, cb + 2 * CH, koff, voff, rk, rv);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kRot) {
-      if (u == 1) __syncthreads();
-    }
+    if constexpr (kRot) __syncthreads();
   };
-  for (int cb = 0, buf = 0; cb < nmax; cb += 2 * CH, buf ^= 1) {
-    tile(l0, cb, buf, 0);
-    tile(l1, cb + CH, buf, 1);
+  for (int cb = 0; cb < nmax; cb += 2 * CH) {
+    tile(l0, cb, 0);
+    tile(l1, cb + CH, 1);
   }
 
   // ---- this wave's records: (acc, m, l) of its G heads
