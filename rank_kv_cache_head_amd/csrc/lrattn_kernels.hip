@@ -1498,9 +1498,11 @@ __device__ __forceinline__ void rebuild_scores(const MStep<R, G, 1>& lat, const 
   // quad's tokens, and each instruction adds one d of the quarter
   // (d = 16 n + 4 (l / 16) + i, lane l's own rebuilt value); then the four
   // quarters are added across lanes.
-  f32x4 sd[QH];
+  // two accumulators per quad (first and second half of each rotary pair),
+  // so consecutive score instructions do not wait on each other's results
+  f32x4 sd[QH][2];
 #pragma unroll
-  for (int qh = 0; qh < QH; ++qh) sd[qh] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int qh = 0; qh < QH; ++qh) sd[qh][0] = sd[qh][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int n = 0; n < NH; ++n) {
     f32x4 kd[2];
@@ -1532,7 +1534,7 @@ __device__ __forceinline__ void rebuild_scores(const MStep<R, G, 1>& lat, const 
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int qh = 0; qh < QH; ++qh)
-          sd[qh] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf.at(qh, n + hf * NH, i), kd[hf][i], sd[qh], 0, 0, 0);
+          sd[qh][hf] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf.at(qh, n + hf * NH, i), kd[hf][i], sd[qh][hf], 0, 0, 0);
       }
     }
   }
@@ -1540,7 +1542,7 @@ __device__ __forceinline__ void rebuild_scores(const MStep<R, G, 1>& lat, const 
 #pragma unroll
   for (int qh = 0; qh < QH; ++qh) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sq[qh][i] = sum_quarters(sd[qh][i]);
+    for (int i = 0; i < 4; ++i) sq[qh][i] = sum_quarters(sd[qh][0][i] + sd[qh][1][i]);
   }
   // lane l keeps heads 4 (l / 16 % 2) + i for G = 8 (the score layout of
   // partition_mfma_kernel), heads i % G otherwise
