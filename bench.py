@@ -15,9 +15,12 @@ and reported under `other_workloads`.
 Printed: one JSON line.  `value` = decode tokens/s = B * K / (wall time of K
 steps), bracketed by device synchronization.  `roofline` describes the
 dominant (partition) kernel: algorithmic bytes per launch / mean launch time
-measured with HIP events on the launch stream, the counted HBM traffic of a
-launch from the committed rocprofv3 counter record (and its GB/s at the
-launch time measured here), and the read probe's attainable GB/s.
+measured with HIP events on the launch stream (with 64 or more partitions
+per head the timed partition step also holds the small query-absorption
+kernel launched ahead of it; `roofline.launch` names both), the counted HBM
+traffic of a launch from the committed rocprofv3 counter record (and its
+GB/s at the launch time measured here), and the read probe's attainable
+GB/s.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
 workload.
 """
@@ -102,6 +105,11 @@ def device_tensors(w, torch, copies):
         else:
             sets.append((lk.clone(), lv.clone(), None if sc is None else sc.clone()))
     return base, sets
+
+
+def lr_pre_absorb_splits() -> int:
+    import rank_kv_cache_head_amd as lr
+    return lr.PRE_ABSORB_SPLITS
 
 
 def kernel_source_sha() -> str:
@@ -250,6 +258,10 @@ class Measured:
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": None if tr is None else tr[0],
             "kernel": self.kernel,
+            # with many partitions per head the timed partition step is two
+            # launches: the query absorption, then the partition kernel
+            "launch": (f"absorb_heads_kernel + {self.kernel}" if self.P >= lr_pre_absorb_splits()
+                       else self.kernel),
             "mean_launch_us": self.launch_mean_s * 1e6,
             "isolated_launch_us": float(self.launch_ms.mean()) * 1e3,
             "min_isolated_launch_us": float(self.launch_ms.min()) * 1e3,

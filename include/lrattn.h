@@ -153,14 +153,26 @@ int lrattn_plan(const lrattn_params* p, int32_t* num_splits, int32_t* split_toke
 const char* lrattn_partition_kernel(const lrattn_params* p);
 
 /*
+ * Partitions per head from which lrattn_decode (and lrattn_partition) forms
+ * q . B_K^T once per query head in a small kernel ahead of the partition
+ * kernel, instead of in the prologue of every partition's workgroup.  With
+ * fewer partitions the absorption stays in the partition kernel.
+ */
+#define LRATTN_PRE_ABSORB_SPLITS 64
+
+/*
  * Host-only.  Bytes of device workspace lrattn_decode needs for `p`:
  * B * Hq * num_splits * (r + 4) * 4 (one fp32 partial record per query head
- * and partition), rounded up to 256.
+ * and partition), rounded up to 256, plus, when num_splits >=
+ * LRATTN_PRE_ABSORB_SPLITS, B * Hq * r * 4 for the absorbed queries, rounded
+ * up to 256.
  */
 int lrattn_workspace_size(const lrattn_params* p, size_t* bytes);
 
 /*
- * The decode step: partition kernel then combine kernel, both on `stream`.
+ * The decode step: partition kernel then combine kernel, both on `stream`
+ * (with at least LRATTN_PRE_ABSORB_SPLITS partitions per head, the query
+ * absorption kernel first).
  * `workspace` holds workspace_bytes >= lrattn_workspace_size(p) bytes; its
  * contents on entry do not matter and are scratch afterwards.
  */
@@ -212,9 +224,12 @@ int lrattn_decode_static(const lrattn_params* p,
 
 /*
  * First half of lrattn_decode alone (for measurement and testing): absorb
- * q . B_K^T, stream the latents, write one partial record per (b, query head,
- * non-empty partition) into the workspace.  Records of partitions that lie
- * past seq_len are not written.
+ * q . B_K^T (in the partition kernel, or, with at least
+ * LRATTN_PRE_ABSORB_SPLITS partitions per head, once per query head in a
+ * kernel launched ahead of it), stream the latents, write one partial record
+ * per (b, query head, non-empty partition) into the workspace.  Records of
+ * partitions that lie past seq_len are not written.  The workspace is
+ * lrattn_workspace_size(p) bytes, as for lrattn_decode.
  */
 int lrattn_partition(const lrattn_params* p,
                      const void* q,

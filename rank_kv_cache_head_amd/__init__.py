@@ -24,7 +24,7 @@ from typing import Optional, Tuple
 __all__ = [
     "LrattnError", "Params", "lib", "library_path", "version", "status_string",
     "params_for", "plan", "workspace_size", "partition_kernel", "decode", "partition",
-    "combine", "Decoder", "decode_static", "STATIC_SCRATCH_BYTES",
+    "combine", "Decoder", "decode_static", "STATIC_SCRATCH_BYTES", "PRE_ABSORB_SPLITS",
     "dense_params_for", "dense_decode", "DenseDecoder",
     "rebuild_plan", "rebuild_workspace_size", "rebuild_decode", "RebuildDecoder",
     "AppendParams", "append_workspace_size", "append", "Appender",
@@ -39,6 +39,10 @@ __all__ = [
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_PKG)
 F32, BF16, F16, I8 = 0, 1, 2, 3
+
+# LRATTN_PRE_ABSORB_SPLITS (lrattn.h): from this many partitions per head the
+# decode step absorbs the queries in a kernel of their own
+PRE_ABSORB_SPLITS = 64
 
 STATUS = {0: "LRATTN_OK", -1: "LRATTN_ERR_NULL", -2: "LRATTN_ERR_SHAPE",
           -3: "LRATTN_ERR_DTYPE", -4: "LRATTN_ERR_UNSUPPORTED", -5: "LRATTN_ERR_ALIGN",

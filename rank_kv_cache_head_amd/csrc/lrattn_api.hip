@@ -111,16 +111,48 @@ size_t workspace_bytes_for(const lrattn_params* p, const Plan& pl) {
   return lrattn::records_bytes(p->batch, p->num_q_heads, pl.P, p->rank);
 }
 
+// With many partitions per head, the decode step absorbs q . B_K^T once per
+// query head in a small kernel ahead of the partition kernel, instead of once
+// per partition in each workgroup's prologue; the absorbed queries [B, Hq, r]
+// fp32 follow the records in the workspace.  Measured on MI355X at 256
+// partitions per head (4 x 40 heads, r 48, up to 131072 tokens): the step
+// 237.9 -> 235.2 us; with 4 partitions per head the extra launch costs ~4 us
+// (gqa_vlm 87.8 -> 92.0 us), hence the threshold.
+bool pre_absorb(const Plan& pl) { return pl.P >= LRATTN_PRE_ABSORB_SPLITS; }
+
+size_t decode_workspace_bytes(const lrattn_params* p, const Plan& pl) {
+  size_t b = workspace_bytes_for(p, pl);
+  if (pre_absorb(pl)) b += ((size_t)p->batch * p->num_q_heads * p->rank * 4 + 255) & ~(size_t)255;
+  return b;
+}
+
 float qscale_for(const lrattn_params* p) {
   const float scale = p->softmax_scale > 0.f ? p->softmax_scale
                                              : (float)(1.0 / sqrt((double)p->head_dim));
   return (float)((double)scale * 1.4426950408889634);  // log2(e): logits in base 2
 }
 
-int check_workspace(const lrattn_params* p, const Plan& pl, const void* ws, size_t ws_bytes) {
+// Launches absorb_heads_kernel into the workspace's q~ area and points the
+// partition arguments at it, when the plan asks for it.
+int launch_pre_absorb(const lrattn_params* p, const Plan& pl, const void* q, const void* BK,
+                      void* ws, lrattn::PartitionArgs* pa, hipStream_t s) {
+  if (!pre_absorb(pl)) return LRATTN_OK;
+  float* qt = reinterpret_cast<float*>(static_cast<char*>(ws) + workspace_bytes_for(p, pl));
+  lrattn::AbsorbHeadsArgs ab;
+  ab.q = q; ab.BK = BK; ab.qt = qt;
+  ab.B = p->batch; ab.Hq = p->num_q_heads; ab.d = p->head_dim; ab.r = p->rank;
+  ab.hpf = p->num_q_heads / p->num_kv_heads;
+  ab.q_dtype = p->q_dtype; ab.f_dtype = p->factor_dtype; ab.qscale = qscale_for(p);
+  if (lrattn::launch_absorb_heads(ab, s) != hipSuccess) return LRATTN_ERR_HIP;
+  pa->qt_pre = qt;
+  return LRATTN_OK;
+}
+
+int check_workspace(const lrattn_params* p, const Plan& pl, const void* ws, size_t ws_bytes,
+                    size_t need = 0) {
   if (!ws) return LRATTN_ERR_WORKSPACE;
   if (!aligned16(ws)) return LRATTN_ERR_ALIGN;
-  if (ws_bytes < workspace_bytes_for(p, pl)) return LRATTN_ERR_WORKSPACE;
+  if (ws_bytes < (need ? need : workspace_bytes_for(p, pl))) return LRATTN_ERR_WORKSPACE;
   return LRATTN_OK;
 }
 
@@ -224,7 +256,7 @@ int lrattn_workspace_size(const lrattn_params* p, size_t* bytes) {
   Plan pl;
   const int st = check_params(p, &pl);
   if (st != LRATTN_OK) return st;
-  *bytes = workspace_bytes_for(p, pl);
+  *bytes = decode_workspace_bytes(p, pl);
   return LRATTN_OK;
 }
 
@@ -234,11 +266,14 @@ int lrattn_partition(const lrattn_params* p, const void* q, const void* L_K, con
   Plan pl;
   int st = check_params(p, &pl);
   if (st == LRATTN_OK) st = check_partition_ptrs(p, q, L_K, L_V, B_K, scales, seq_lens);
-  if (st == LRATTN_OK) st = check_workspace(p, pl, workspace, workspace_bytes);
+  if (st == LRATTN_OK)
+    st = check_workspace(p, pl, workspace, workspace_bytes, decode_workspace_bytes(p, pl));
   if (st != LRATTN_OK) return st;
-  const auto a = partition_args(p, pl, q, L_K, L_V, B_K, scales, seq_lens, workspace);
-  if (lrattn::launch_partition(p->latent_dtype, p->rank, group_of(p), a,
-                               reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto a = partition_args(p, pl, q, L_K, L_V, B_K, scales, seq_lens, workspace);
+  st = launch_pre_absorb(p, pl, q, B_K, workspace, &a, s);
+  if (st != LRATTN_OK) return st;
+  if (lrattn::launch_partition(p->latent_dtype, p->rank, group_of(p), a, s) != hipSuccess)
     return LRATTN_ERR_HIP;
   return LRATTN_OK;
 }
@@ -263,10 +298,13 @@ int lrattn_decode(const lrattn_params* p, const void* q, const void* L_K, const 
   int st = check_params(p, &pl);
   if (st == LRATTN_OK) st = check_partition_ptrs(p, q, L_K, L_V, B_K, scales, seq_lens);
   if (st == LRATTN_OK) st = check_combine_ptrs(B_V, seq_lens, out);
-  if (st == LRATTN_OK) st = check_workspace(p, pl, workspace, workspace_bytes);
+  if (st == LRATTN_OK)
+    st = check_workspace(p, pl, workspace, workspace_bytes, decode_workspace_bytes(p, pl));
   if (st != LRATTN_OK) return st;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const auto pa = partition_args(p, pl, q, L_K, L_V, B_K, scales, seq_lens, workspace);
+  auto pa = partition_args(p, pl, q, L_K, L_V, B_K, scales, seq_lens, workspace);
+  st = launch_pre_absorb(p, pl, q, B_K, workspace, &pa, s);
+  if (st != LRATTN_OK) return st;
   if (lrattn::launch_partition(p->latent_dtype, p->rank, group_of(p), pa, s) != hipSuccess)
     return LRATTN_ERR_HIP;
   const auto ca = combine_args(p, pl, B_V, seq_lens, out, workspace);
@@ -659,6 +697,7 @@ int lrattn_shared_decode(const lrattn_params* p, const void* q, const void* L_K,
   lrattn::AbsorbHeadsArgs ab;
   ab.q = q; ab.BK = B_K; ab.qt = qt;
   ab.B = p->batch; ab.Hq = p->num_q_heads; ab.d = p->head_dim; ab.r = p->rank;
+  ab.hpf = 1;  // one factor block per query head
   ab.q_dtype = p->q_dtype; ab.f_dtype = p->factor_dtype; ab.qscale = qscale_for(p);
   if (lrattn::launch_absorb_heads(ab, s) != hipSuccess) return LRATTN_ERR_HIP;
   if (once) {

@@ -127,9 +127,10 @@ bool rebuild_supported(int head_dim, int rank, int group);
 // qt[b][h][j] = qscale * sum_i q[b][h][i] * B_K[h][j][i], fp32.
 struct AbsorbHeadsArgs {
   const void* q;    // [B, Hq, d]
-  const void* BK;   // [Hq, r, d]
+  const void* BK;   // [Hq / hpf, r, d]
   float* qt;        // [B, Hq, r]
   int32_t B, Hq, d, r;
+  int32_t hpf;      // query heads per factor block: head h uses B_K[h / hpf]
   int32_t q_dtype, f_dtype;
   float qscale;
 };

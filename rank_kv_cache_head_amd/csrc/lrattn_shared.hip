@@ -8,6 +8,10 @@
 // single product per kv-head does not apply), formed here once per decode
 // step; the partition kernels then read it instead of absorbing.
 //
+// The decode step of a grouped cache takes the same kernel when its plan has
+// many partitions per head: head h then uses its kv-head's factor B_K[h / G]
+// (hpf = G), and q~ is formed once per head instead of once per partition.
+//
 // Grid (Hq, sequence blocks of 8); thread (coordinate j, block row s) forms
 // q~ for sequences s, s + 256 / r, ... of the block: the factor row B_K[h][j]
 // is streamed once per thread, 256 bytes per round, and reused across those
@@ -66,7 +70,7 @@ __device__ __forceinline__ void absorb_body(const AbsorbHeadsArgs& a) {
   const int tid = threadIdx.x, j = tid % R, s0 = tid / R;
   const int d = a.d, npieces = d / EPP;
   // the head's factor block (a wave-uniform resource); row j at j d ES bytes
-  const auto rb = make_rsrc(static_cast<const char*>(a.BK) + (size_t)h * R * d * ES,
+  const auto rb = make_rsrc(static_cast<const char*>(a.BK) + (size_t)(h / a.hpf) * R * d * ES,
                             (uint32_t)(R * d * ES));
   u32x4 w[kAbsorbPieces];
   auto load_round = [&](int r0) {

@@ -58,6 +58,19 @@ def test_workspace_size_formula():
     assert lr.workspace_size(p) == (records + 255) // 256 * 256
 
 
+def test_workspace_size_with_absorbed_queries():
+    """From LRATTN_PRE_ABSORB_SPLITS partitions per head the workspace also
+    holds the absorbed queries [B, Hq, r] fp32 after the records."""
+    assert lr.PRE_ABSORB_SPLITS == 64
+    for splits, extra in ((63, False), (64, True), (200, True)):
+        p = params(num_splits=splits, max_seq_len=1024)
+        P, _ = lr.plan(p)
+        records = (2 * 8 * P * (64 + 4) * 4 + 255) // 256 * 256
+        qt = (2 * 8 * 64 * 4 + 255) // 256 * 256 if P >= 64 else 0
+        assert (P >= 64) == extra, (splits, P)
+        assert lr.workspace_size(p) == records + qt, splits
+
+
 @pytest.mark.parametrize("kw,exp_P,exp_S", [
     # the five workloads' shapes and storage types
     (dict(batch=1, num_q_heads=4, num_kv_heads=4, head_dim=64, rank=16, max_seq_len=256,

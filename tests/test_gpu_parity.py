@@ -570,6 +570,30 @@ def test_shared_equals_per_head_cache():
     assert rel_rowmax(a.cpu().numpy(), b.cpu().numpy().astype(np.float64)) <= 2e-5
 
 
+def test_shared_decoder_object_equals_function():
+    """SharedDecoder (arguments marshalled once, as the benchmark times it)
+    gives the bits of shared_decode on the same inputs, call after call, on
+    the one-pass shape (32 heads, one stream of rank 128)."""
+    import torch
+    import rank_kv_cache_head_amd as lr
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1300)
+    B, Hq, T, R, d = 2, 32, 700, 128, 128
+    LK = torch.randn((B, 1, T, R), generator=g, device="cuda").to(torch.bfloat16)
+    LV = torch.randn((B, 1, T, R), generator=g, device="cuda").to(torch.bfloat16)
+    BK = (torch.randn((Hq, R, d), generator=g, device="cuda") / R ** 0.5).to(torch.bfloat16)
+    BV = (torch.randn((Hq, R, d), generator=g, device="cuda") / R ** 0.5).to(torch.bfloat16)
+    q = torch.randn((B, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    sl = torch.tensor([700, 333], dtype=torch.int32, device="cuda")
+    say("SharedDecoder == shared_decode")
+    ref = lr.shared_decode(q, LK, LV, BK, BV, sl).clone()
+    dec = lr.SharedDecoder(q, LK, LV, BK, BV, sl)
+    for _ in range(3):
+        out = dec()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+
+
 def test_guard_bands_untouched():
     import torch
     import rank_kv_cache_head_amd as lr
