@@ -168,8 +168,8 @@ def cpu_baseline(w, gpu_out, seconds: float):
                                      BV[g:g + 1], np.array([n]), rows, scales=sc)
             if done < w.batch:
                 got = gpu_out[b, g * G:(g + 1) * G]
-                e = np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)
-                err = max(err, float(e.max()))
+                e = float((np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)).max())
+                err = max(err, e) if np.isfinite(e) else float("inf")  # a NaN row must show
         done += 1
         if time.perf_counter() - t0 >= seconds:
             break
