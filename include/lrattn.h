@@ -200,7 +200,8 @@ int lrattn_decode(const lrattn_params* p,
  * rules as lrattn_decode, plus:
  *   - a request whose lrattn_workspace_size exceeds LRATTN_STATIC_SCRATCH_BYTES
  *     returns LRATTN_ERR_SCRATCH before any device work (the five reference
- *     workloads need at most 8.5 MB: 4 x 40 heads x 256 partitions x r 48);
+ *     workloads need at most 8.6 MB: 4 x 40 heads x 256 partitions x r 48,
+ *     and the absorbed queries);
  *   - the buffer used is the current device's: `stream` must belong to the
  *     current device (else LRATTN_ERR_UNSUPPORTED);
  *   - every call on one device shares that device's buffer, so calls that
