@@ -192,8 +192,9 @@ int lrattn_decode(const lrattn_params* p,
 /*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):
- * lrattn_decode with no workspace argument.  The partial records go to a
- * static device buffer of LRATTN_STATIC_SCRATCH_BYTES (16 MiB), one per
+ * lrattn_decode with no workspace argument.  The partial records (and the
+ * absorbed queries, when the plan has them) go to a static device buffer of
+ * LRATTN_STATIC_SCRATCH_BYTES (16 MiB), one per
  * device, which the library holds from the first call on a device until the
  * process ends; the call allocates nothing.  Same operation, kernels, plan,
  * results (bitwise equal to lrattn_decode's for the same p) and argument

@@ -1,8 +1,9 @@
-// lrattn_decode_static: the decode step with its partial records in a static
+// lrattn_decode_static: the decode step with its workspace (the partial
+// records, and the absorbed queries when the plan has them) in a static
 // device buffer instead of a caller workspace, for callers that cannot
 // allocate device memory (code under HIP graph capture, tight serving loops,
 // harnesses that forbid allocation).  The kernels are lrattn_decode's; only
-// the place of the records differs.
+// the place of the workspace differs.
 #include <atomic>
 #include <mutex>
 
@@ -12,7 +13,7 @@
 
 namespace {
 
-// The records of every lrattn_decode_static call on a device.  Each device
+// The workspace of every lrattn_decode_static call on a device.  Each device
 // holds its own copy (at its own address) from the first call on it until
 // the process ends.  In host code `scratch` names a host-side stand-in, not
 // the device address: the address comes from hipGetSymbolAddress, resolved
