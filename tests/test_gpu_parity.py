@@ -618,19 +618,25 @@ def test_guard_bands_untouched():
     assert rel_rowmax(out.cpu().numpy(), _full_oracle(w)) <= 2e-3
 
 
-def test_partition_then_combine_equals_decode():
+@pytest.mark.parametrize("name,splits", [("int8", 5), ("int8", 100), ("gqa_vlm", 80)])
+def test_partition_then_combine_equals_decode(name, splits):
+    """lrattn_partition then lrattn_combine give lrattn_decode's bits, also
+    with the queries absorbed ahead of the partition kernel (64 or more
+    partitions per head)."""
     import torch
     import rank_kv_cache_head_amd as lr
-    w = workloads.make("int8", **SMALL["int8"])
+    w = workloads.make(name, **SMALL[name])
     dev = to_device(w)
-    say("partition + combine")
-    ref = run_decode(w, dev, num_splits=5).cpu().numpy()
+    say(f"partition + combine {name} splits={splits}")
+    ref = run_decode(w, dev, num_splits=splits).cpu().numpy()
     ws = lr.partition(dev["q"], dev["L_K"], dev["L_V"], dev["B_K"], dev["seq_lens"],
-                      dev["scales"], num_splits=5)
-    p = lr.params_for(dev["q"], dev["L_K"], dev["B_K"], num_splits=5)
+                      dev["scales"], num_splits=splits)
+    p = lr.params_for(dev["q"], dev["L_K"], dev["B_K"], num_splits=splits)
+    assert (lr.plan(p)[0] >= lr.PRE_ABSORB_SPLITS) == (splits >= 64)
     out = lr.combine(p, dev["B_V"], dev["seq_lens"], ws)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), ref)
+    assert rel_rowmax(out.cpu().numpy(), _full_oracle(w)) <= TOL[w.latent_dtype]
 
 
 def test_side_stream():
