@@ -391,6 +391,7 @@ def main():
         line["modal_factors"] = leg(modal_factors, *base_sets, step_ms, vlm_first=True)
     if not args.no_adaptive:
         line["adaptive_rank"] = leg(adaptive_rank, *base_sets, step_ms, vlm_first=True)
+        line["adaptive_rank_r128"] = leg(adaptive_rank_wide, vlm_first=True)
     gpu_out = m.gpu_out
     m.release(torch)
     for o in aux.values():
@@ -563,11 +564,14 @@ def append_step(w, torch, lr, args):
 def adaptive_rank(w, torch, lr, args, splits, base, sets, plain_ms):
     """The same step with attention-aware rank (AttentionPack's adaptive
     decompression): tokens whose importance score is below 0.5 keep r/2
-    latent coordinates; the step writes its logits and updates the scores
-    (decay 0.9).  Scores drawn U(0, 1) on the device.  None where the shape
-    has no adaptive kernel."""
+    latent coordinates; the step writes its logits and updates the scores.
+    Scores drawn U(0, 1) on the device; decay 1.0, so the update runs in
+    full but leaves the scores, and with them the half of the rows at low
+    rank, the same from step to step (with decay < 1 the scores would sink
+    below the threshold within a few steps: a step's attention weights are
+    ~1/T each).  None where the shape has no adaptive kernel."""
     G = w.num_q_heads // w.num_kv_heads
-    ok = {"bf16": w.rank in (32, 48, 64), "i8": w.rank == 32 and G in (1, 4),
+    ok = {"bf16": w.rank in (32, 48, 64, 128), "i8": w.rank == 32 and G in (1, 4),
           "f32": w.rank == 16 and G == 1}.get(w.latent_dtype, False)
     if not ok:
         return None
@@ -576,7 +580,7 @@ def adaptive_rank(w, torch, lr, args, splits, base, sets, plain_ms):
     imp = torch.rand((w.batch, w.num_kv_heads, w.max_seq_len), generator=g, device="cuda")
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     decs = [lr.AdaptiveDecoder(base["q"], lk, lv, base["B_K"], base["B_V"], base["seq_lens"],
-                               imp, low_rank=w.rank // 2, threshold=0.5, decay=0.9, scales=sc,
+                               imp, low_rank=w.rank // 2, threshold=0.5, decay=1.0, scales=sc,
                                out=out, num_splits=splits)
             for lk, lv, sc in sets]
     n = len(decs)
@@ -598,6 +602,61 @@ def adaptive_rank(w, torch, lr, args, splits, base, sets, plain_ms):
                 vs_plain=ms / plain_ms, added_bytes_per_step=extra,
                 step_GBps=moved / (ms / 1e3) / 1e9, frac_of_8TBps=moved / (ms / 1e3) / 8e12,
                 kernel=f"{kern} (adaptive) + combine_kernel + importance_kernel")
+
+
+def adaptive_rank_wide(w, torch, lr, args, splits):
+    """Attention-aware rank where a dropped half row is a whole HBM line: the
+    workload's batch, heads and lengths with r = 128 bf16 latents (256-byte
+    rows, two 128-byte lines), low rank 64, scores U(0, 1) against threshold
+    0.5 (half the rows drop their second line; decay 1.0 keeps that half
+    from step to step, see adaptive_rank), timed against the plain
+    decode of the same r = 128 cache.  Random values drawn on the device;
+    copies rotated over more than 1 GiB as in the main loop.  None for
+    workloads whose queries are not bf16."""
+    if not (w.q_dtype == w.factor_dtype == "bf16"):
+        return None
+    import numpy as np
+    R, d = 128, w.head_dim
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2027)
+    shp = (w.batch, w.num_kv_heads, w.max_seq_len, R)
+    LK = torch.randn(shp, generator=g, device="cuda").to(torch.bfloat16)
+    LV = torch.randn(shp, generator=g, device="cuda").to(torch.bfloat16)
+    copies = max(1, -(-ROTATE_BYTES // (2 * LK.nbytes)))
+    lats = [(LK, LV)] + [(LK.clone(), LV.clone()) for _ in range(copies - 1)]
+    BK = (torch.randn((w.num_kv_heads, R, d), generator=g, device="cuda") / R ** 0.5).to(torch.bfloat16)
+    BV = (torch.randn((w.num_kv_heads, R, d), generator=g, device="cuda") / R ** 0.5).to(torch.bfloat16)
+    q = torch.randn((w.batch, w.num_q_heads, d), generator=g, device="cuda").to(torch.bfloat16)
+    sl = torch.from_numpy(w.seq_lens.astype(np.int32)).cuda()
+    imp = torch.rand((w.batch, w.num_kv_heads, w.max_seq_len), generator=g, device="cuda")
+    out = torch.empty((w.batch, w.num_q_heads, d), dtype=torch.float32, device="cuda")
+
+    def timed(decs):
+        for i in range(args.warmup):
+            decs[i % copies]()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            decs[i % copies]()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps * 1e3
+
+    plain = [lr.Decoder(q, lk, lv, BK, BV, sl, out=out, num_splits=splits) for lk, lv in lats]
+    plain_ms = timed(plain)
+    del plain
+    ad = [lr.AdaptiveDecoder(q, lk, lv, BK, BV, sl, imp, low_rank=R // 2, threshold=0.5,
+                             decay=1.0, out=out, num_splits=splits) for lk, lv in lats]
+    ad_ms = timed(ad)
+    kern = lr.adaptive_kernel(ad[0].params, ad[0].adaptive)
+    del ad, lats, LK, LV
+    torch.cuda.empty_cache()
+    valid = int(w.seq_lens.sum())
+    lat = valid * w.num_kv_heads * 2 * R * 2
+    return dict(rank=R, low_rank=R // 2, plain_ms_per_step=plain_ms, ms_per_step=ad_ms,
+                vs_plain=ad_ms / plain_ms, latent_bytes_plain=lat,
+                latent_lines_dropped=lat // 4,
+                kernel=f"{kern} (adaptive) + combine_kernel + importance_kernel",
+                input_copies_rotated=copies)
 
 
 def modal_factors(w, torch, lr, args, splits, base, sets, one_set_ms):

@@ -340,7 +340,7 @@ int lrattn_rebuild_decode(const lrattn_params* p,
  * the combine (which also writes each row's final max and denominator), the
  * update.  The workspace (lrattn_adaptive_workspace_size bytes) holds the
  * records, the logits and the row statistics.  Supported: bf16
- * latents with r in {32, 48, 64} and group in {1, 2, 4, 8}; int8 latents
+ * latents with r in {32, 48, 64, 128} and group in {1, 2, 4, 8}; int8 latents
  * with r = 32 and group 1 or 4; fp32 latents with r = 16 and group 1; and
  * group * T * 4 < 2^31 bytes; else LRATTN_ERR_UNSUPPORTED.  Other tensors,
  * dtypes, seq_lens handling,

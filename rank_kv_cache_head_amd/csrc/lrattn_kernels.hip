@@ -2360,7 +2360,7 @@ bool adaptive_supported(int latent_dtype, int rank, int group) {
   const bool g = group == 1 || group == 2 || group == 4 || group == 8;
   switch (latent_dtype) {
     case LRATTN_F32: return rank == 16 && group == 1;
-    case LRATTN_BF16: return (rank == 32 || rank == 48 || rank == 64) && g;
+    case LRATTN_BF16: return (rank == 32 || rank == 48 || rank == 64 || rank == 128) && g;
     case LRATTN_I8: return rank == 32 && (group == 1 || group == 4);
     default: return false;
   }
@@ -2379,6 +2379,7 @@ hipError_t launch_adaptive(int latent_dtype, int rank, int group, const Partitio
   switch (rank) {
     case 32: return launch_ag<LatBF16, 32>(group, a, s);
     case 48: return launch_ag<LatBF16, 48>(group, a, s);
+    case 128: return launch_ag<LatBF16, 128>(group, a, s);
     default: return launch_ag<LatBF16, 64>(group, a, s);
   }
 }

@@ -336,7 +336,8 @@ def test_adaptive_decode_validates_on_host():
                                         sc, seq, imp, out, ws, ws_bytes, None)
     p = params()                                       # bf16, d 128, r 64, G 4
     assert call(params(latent_dtype=lr.F16)) == -4     # bf16, int8 (r 32), fp32 (r 16)
-    assert call(params(rank=128)) == -4
+    assert call(params(rank=16)) == -4                 # bf16: r in {32, 48, 64, 128}
+    assert call(params(rank=128, latent_dtype=lr.I8)) == -4
     assert call(p, ad=lr.AdaptiveParams(0, 0.5, 0.9)) == -2       # low_rank in [1, r]
     assert call(p, ad=lr.AdaptiveParams(65, 0.5, 0.9)) == -2
     assert call(p, ad=lr.AdaptiveParams(8, 0.5, 1.5)) == -2       # decay in [0, 1]
@@ -356,14 +357,14 @@ def test_adaptive_decode_validates_on_host():
 def test_adaptive_kernel_names():
     ad = lr.AdaptiveParams(16, 0.5, 0.9)
     # bf16 latents with r a multiple of 32 and 4 or 8 heads: the matrix-core kernel
-    for r in (32, 48, 64):
+    for r in (32, 48, 64, 128):
         for G in (1, 2, 4, 8):
             p = params(rank=r, num_q_heads=2 * G, num_kv_heads=2)
             want = "partition_mfma_kernel" if r % 32 == 0 and G >= 4 else "partition_kernel"
             assert lr.adaptive_kernel(p, lr.AdaptiveParams(8, 0.5, 0.9)) == want, (r, G)
     assert lr.adaptive_kernel(params(latent_dtype=lr.I8, rank=32, num_q_heads=8,
                                      num_kv_heads=2), ad) == "partition_kernel"
-    assert lr.lib().lrattn_adaptive_kernel(ctypes.byref(params(rank=128)), ctypes.byref(ad)) is None
+    assert lr.lib().lrattn_adaptive_kernel(ctypes.byref(params(rank=16)), ctypes.byref(ad)) is None
     assert lr.lib().lrattn_adaptive_kernel(ctypes.byref(params()), None) is None
     with pytest.raises(lr.LrattnError):
         lr.adaptive_kernel(params(latent_dtype=lr.F16), ad)

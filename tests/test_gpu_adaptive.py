@@ -66,6 +66,11 @@ CASES = {
     # the matrix-core kernel's other shapes (8 heads at r = 64, 4 at r = 32)
     "g8_bf16_r64": ("gqa_vlm", dict(B=2, Hq=16, Hkv=2, T=700, seq_lens=[700, 129])),
     "g4_bf16_r32": ("gqa_vlm", dict(B=2, Hq=8, Hkv=2, r=32, T=600, seq_lens=[600, 77])),
+    # r = 128: a row is two 128-byte lines, and a low row's second line is
+    # not read (matrix-core kernel at 4 and 8 heads, VALU kernel at 1)
+    "g4_bf16_r128": ("gqa_vlm", dict(B=2, Hq=8, Hkv=2, r=128, T=900, seq_lens=[900, 301])),
+    "g8_bf16_r128": ("gqa_vlm", dict(B=2, Hq=16, Hkv=2, r=128, T=500, seq_lens=[500, 64])),
+    "g1_bf16_r128": ("llm7b", dict(B=2, Hq=2, Hkv=2, r=128, T=700, seq_lens=[700, 150])),
 }
 
 
