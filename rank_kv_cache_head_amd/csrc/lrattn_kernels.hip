@@ -990,35 +990,22 @@ struct MStep {
 };
 
 // Attention-aware rank on the matrix-core kernel (AttentionPack page, section
-// 2.B): the importance scores of the step's rows in both layouts, and this
-// lane's masks.  A row below the threshold keeps latent columns
-// [0, low_rank); keepk[c] and keepv count the kept columns among the 8 this
-// lane holds (score layout, 32-column step c; value layout).
-template <int NT, int VU>
-struct MImp {
-  float k[NT];      // row 16 t + lane % 16 (score layout)
-  float v[NT][VU];  // rows 16 t + slot + RPW u (value layout)
-};
-
+// 2.B).  A row below the threshold keeps latent columns [0, low_rank).  A
+// 16-byte piece a lane loads that lies wholly past low_rank is simply not
+// fetched for such a row (an offset past the buffer returns the zeros the
+// reduced rank means).  When low_rank is not a multiple of 8 (the kernel's
+// kCut form) one piece per row is cut: its columns past low_rank are
+// cleared in registers.  dropk bit c: this lane's piece of 32-column step c
+// (score layout) lies past low_rank; dropv: its value piece does.
 struct MAdaptive {
   float thr;
-  int keepk[4];
-  int keepv;
+  uint32_t dropk;
+  bool dropv;
+  int pk;      // the 32-column step whose piece of this lane is cut, or -1
+  int keepk;   // columns that piece keeps (1..7)
+  int keepv;   // columns this lane's value piece keeps (8 when it is not cut)
   __amdgpu_buffer_rsrc_t rlg;  // the group's logits [token][G] from the partition start
 };
-
-template <int R, int G, int NT>
-__device__ __forceinline__ void load_mimp(MImp<NT, MGeo<R, G, NT>::kVU>& im, int cb, int lane,
-                                          int slot, __amdgpu_buffer_rsrc_t rimp) {
-  using Mg = MGeo<R, G, NT>;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    im.k[t] = bload4f(rimp, (uint32_t)(cb + 16 * t + (lane & 15)) * 4u);
-#pragma unroll
-    for (int u = 0; u < Mg::kVU; ++u)
-      im.v[t][u] = bload4f(rimp, (uint32_t)(cb + 16 * t + slot + Mg::kRPW * u) * 4u);
-  }
-}
 
 // Latent word holding elements e0 (low half) and e0 + 1 (high half): the
 // elements at or past `keep` become zero.
@@ -1026,25 +1013,44 @@ __device__ __forceinline__ uint32_t keep_word(uint32_t w, int keep, int e0) {
   return w & (keep > e0 + 1 ? 0xffffffffu : keep > e0 ? 0x0000ffffu : 0u);
 }
 
-// A step's latent loads.  With attention-aware rank (kAd) the rows'
-// importance scores `im` are already in registers: a 16-byte piece that
-// lies wholly past low_rank (keep 0 in this lane) is not fetched for a row
-// below the threshold (an offset past the buffer returns zeros).
+// The importance scores of a wave's step (rows cb .. cb + CH - 1), one per
+// lane, requested a step ahead of the rows' latents ...
+template <int CH>
+__device__ __forceinline__ float load_step_imp(__amdgpu_buffer_rsrc_t rimp, int cb, int lane) {
+  static_assert(CH <= 64, "one score per lane");
+  return bload4f(rimp, lane < CH ? (uint32_t)(cb + lane) * 4u : kOffNone);
+}
+
+// ... and, when they have arrived, the step's low rows as one wave-uniform
+// mask (bit i: row cb + i is below the threshold).  Rows past the partition
+// read 0; their latents lie past the buffer whatever the mask says.
+template <int CH>
+__device__ __forceinline__ uint64_t low_rows(float imp, int lane, float thr) {
+  return __builtin_amdgcn_ballot_w64(lane < CH && imp < thr);
+}
+
+// A step's latent loads.  With attention-aware rank (kAd) `low` marks the
+// step's rows below the threshold: their pieces past low_rank get an offset
+// past the buffer, so they are not fetched and arrive as zeros.
 template <int R, int G, int NT, int kAux = kNonTemporal, bool kAd = false>
 __device__ __forceinline__ void load_mstep(MStep<R, G, NT>& st, int cb, uint32_t koff,
                                            uint32_t voff, __amdgpu_buffer_rsrc_t rk,
-                                           __amdgpu_buffer_rsrc_t rv,
-                                           const MImp<NT, MGeo<R, G, NT>::kVU>* im = nullptr,
+                                           __amdgpu_buffer_rsrc_t rv, uint64_t low = 0,
                                            const MAdaptive* ad = nullptr) {
   using Mg = MGeo<R, G, NT>;
+  const int lane = threadIdx.x & 63, slot = lane / Mg::kLPR;
 #pragma unroll
   for (int t = 0; t < Mg::kNT; ++t) {
     const uint32_t base = (uint32_t)(cb + 16 * t) * Mg::kRowBytes;
+    const bool lowk = kAd && ((low >> (16 * t + (lane & 15))) & 1u);
 #pragma unroll
     for (int c = 0; c < Mg::kKC; ++c) {
-      uint32_t off = base + koff + 64u * c;
-      if constexpr (kAd) off = ad->keepk[c] == 0 && im->k[t] < ad->thr ? kOffNone : off;
-      load_words<4, kAux>(st.k[t][c], rk, off);
+      // only the lane's part is selected, so the step base and the piece
+      // offset stay scalar and immediate (kOffNone plus them is still past
+      // the buffer)
+      uint32_t lo = koff;
+      if constexpr (kAd) lo = lowk && ((ad->dropk >> c) & 1u) ? kOffNone : lo;
+      load_words<4, kAux>(st.k[t][c], rk, base + lo + 64u * c);
     }
   }
 #pragma unroll
@@ -1052,20 +1058,22 @@ __device__ __forceinline__ void load_mstep(MStep<R, G, NT>& st, int cb, uint32_t
     const uint32_t base = (uint32_t)(cb + 16 * t) * Mg::kRowBytes;
 #pragma unroll
     for (int u = 0; u < Mg::kVU; ++u) {
-      uint32_t off = base + voff + (uint32_t)(u * Mg::kRPW) * Mg::kRowBytes;
-      if constexpr (kAd) off = ad->keepv == 0 && im->v[t][u] < ad->thr ? kOffNone : off;
-      load_words<4, kAux>(st.v[t][u], rv, off);
+      uint32_t lo = voff;
+      if constexpr (kAd) {
+        const bool lowv = (low >> (16 * t + slot + Mg::kRPW * u)) & 1u;
+        lo = lowv && ad->dropv ? kOffNone : lo;
+      }
+      load_words<4, kAux>(st.v[t][u], rv, base + lo + (uint32_t)(u * Mg::kRPW) * Mg::kRowBytes);
     }
   }
 }
 
 // Scores of the step's tiles: s[t][i] = base-2 logit of token 16 t + l % 16
 // for this lane's head i (rows 4 * (l / 16) + i of the product).
-template <int R, int G, int NT, bool kMask, bool kAd = false>
+template <int R, int G, int NT, bool kMask, bool kAd = false, bool kCut = false>
 __device__ __forceinline__ void mfma_scores(const MStep<R, G, NT>& st, int cb, int ntok, int lane,
                                             const bf16x8 (&qa)[3][MGeo<R, G, NT>::kKC],
-                                            float (&s)[NT][4],
-                                            const MImp<NT, MGeo<R, G, NT>::kVU>* im = nullptr,
+                                            float (&s)[NT][4], uint64_t low = 0,
                                             const MAdaptive* ad = nullptr) {
   constexpr int KC = MGeo<R, G, NT>::kKC;
   const int tok = lane & 15;
@@ -1075,10 +1083,14 @@ __device__ __forceinline__ void mfma_scores(const MStep<R, G, NT>& st, int cb, i
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       kw[c] = u32x4{st.k[t][c][0], st.k[t][c][1], st.k[t][c][2], st.k[t][c][3]};
-      if constexpr (kAd) {
-        const bool low = im->k[t] < ad->thr;
+    }
+    if constexpr (kCut) {
+      const bool lowk = (low >> (16 * t + tok)) & 1u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kw[c][j] = low ? keep_word(kw[c][j], ad->keepk[c], 2 * j) : kw[c][j];
+      for (int c = 0; c < KC; ++c) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          kw[c][j] = lowk && c == ad->pk ? keep_word(kw[c][j], ad->keepk, 2 * j) : kw[c][j];
       }
     }
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
@@ -1115,11 +1127,10 @@ __device__ __forceinline__ void mfma_scores(const MStep<R, G, NT>& st, int cb, i
 // latent-space value accumulation in the slot layout.  Lane l's result i is
 // head (4 * (l / 16) + i) % G: with G < 4 results i >= G repeat heads and are
 // not used.
-template <int R, int G, int NT, bool kAd = false>
+template <int R, int G, int NT, bool kCut = false>
 __device__ __forceinline__ void softmax_values(const float (&s)[NT][4], const MStep<R, G, NT>& st,
                                                int lane, float (&mm)[4], float (&ll)[4],
-                                               float (&acc)[G][8], float* wl,
-                                               const MImp<NT, MGeo<R, G, NT>::kVU>* im = nullptr,
+                                               float (&acc)[G][8], float* wl, uint64_t low = 0,
                                                const MAdaptive* ad = nullptr) {
   using Mg = MGeo<R, G, NT>;
   constexpr int VU = Mg::kVU, RPW = Mg::kRPW, HL = Mg::kHL;
@@ -1202,10 +1213,10 @@ __device__ __forceinline__ void softmax_values(const float (&s)[NT][4], const MS
       }
       float x[8];
       Unpack<LatBF16>::run(st.v[t][u], x);
-      if constexpr (kAd) {
-        const bool low = im->v[t][u] < ad->thr;
+      if constexpr (kCut) {
+        const bool lowv = (low >> (16 * t + slot + RPW * u)) & 1u;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = (low && j >= ad->keepv) ? 0.f : x[j];
+        for (int j = 0; j < 8; ++j) x[j] = lowv && j >= ad->keepv ? 0.f : x[j];
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -1218,14 +1229,14 @@ __device__ __forceinline__ void softmax_values(const float (&s)[NT][4], const MS
   wave_sync();
 }
 
-template <int R, int G, bool kMask, bool kAd = false>
+template <int R, int G, bool kMask, bool kAd = false, bool kCut = false>
 __device__ __forceinline__ void compute_mstep(
     const MStep<R, G>& st, int cb, int ntok, int lane, const bf16x8 (&qa)[3][MGeo<R, G>::kKC],
-    float (&mm)[4], float (&ll)[4], float (&acc)[G][8], float* wl,
-    const MImp<MGeo<R, G>::kNT, MGeo<R, G>::kVU>* im = nullptr, const MAdaptive* ad = nullptr) {
+    float (&mm)[4], float (&ll)[4], float (&acc)[G][8], float* wl, uint64_t low = 0,
+    const MAdaptive* ad = nullptr) {
   float s[MGeo<R, G>::kNT][4];
-  mfma_scores<R, G, MGeo<R, G>::kNT, kMask, kAd>(st, cb, ntok, lane, qa, s, im, ad);
-  softmax_values<R, G, MGeo<R, G>::kNT, kAd>(s, st, lane, mm, ll, acc, wl, im, ad);
+  mfma_scores<R, G, MGeo<R, G>::kNT, kMask, kAd, kCut>(st, cb, ntok, lane, qa, s, low, ad);
+  softmax_values<R, G, MGeo<R, G>::kNT, kCut>(s, st, lane, mm, ll, acc, wl, low, ad);
 }
 
 // End of a matrix-core partition: the wave's exp-sums over its 16 token
@@ -1281,17 +1292,24 @@ struct MPartLds {
   float w[kWaves * MGeo<R, G>::kChunk * G];
 };
 
-// The adaptive form holds the rows' importance scores and masks besides:
-// with 8 heads that no longer fits three waves per SIMD without spills.
-template <int R, int G, bool kAd>
+// Occupancy targets (waves per SIMD) of the attention-aware forms, each the
+// highest without spills: with 8 heads the adaptive form needs more registers
+// than three waves per SIMD allow; with 4 heads it fits the plain form's;
+// the plain form does; the kCut form with 8 heads at r = 128 needs more than
+// 256 registers.
+template <int R, int G, bool kAd, bool kCut>
 constexpr int mfma_waves() {
-  return kAd && G == 8 && MGeo<R, G>::kWavesPerEU > 2 ? 2 : MGeo<R, G>::kWavesPerEU;
+  if constexpr (kCut && G == 8 && R == 128) return 1;
+  else if constexpr (kAd && G == 8 && MGeo<R, G>::kWavesPerEU > 2) return 2;
+  else return MGeo<R, G>::kWavesPerEU;
 }
 
-template <int R, int G, int kAux = kNonTemporal, bool kSeg = false, bool kAd = false>
+template <int R, int G, int kAux = kNonTemporal, bool kSeg = false, bool kAd = false,
+          bool kCut = false>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(mfma_waves<R, G, kAd>())))
+__attribute__((amdgpu_waves_per_eu(mfma_waves<R, G, kAd, kCut>())))
 void partition_mfma_kernel(PartitionArgs a) {
+  static_assert(kAd || !kCut, "a cut piece only exists with attention-aware rank");
   using Mg = MGeo<R, G>;
   constexpr int KC = Mg::kKC, LPR = Mg::kLPR, CH = Mg::kChunk;
 
@@ -1325,7 +1343,17 @@ void partition_mfma_kernel(PartitionArgs a) {
     rimp = make_rsrc(a.imp + row0, (uint32_t)ntok * 4u);
     ad.thr = a.imp_thr;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) ad.keepk[c] = min(max(a.low_rank - (32 * c + 8 * (lane >> 4)), 0), 8);
+    for (int c = 0; c < KC; ++c) ad.dropk |= (32 * c + 8 * (lane >> 4) >= a.low_rank ? 1u : 0u) << c;
+    ad.dropv = cc * 8 >= a.low_rank;
+    ad.pk = -1;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const int keep = a.low_rank - (32 * c + 8 * (lane >> 4));
+      if (keep > 0 && keep < 8) {
+        ad.pk = c;
+        ad.keepk = keep;
+      }
+    }
     ad.keepv = min(max(a.low_rank - cc * 8, 0), 8);
     ad.rlg = make_rsrc(a.logits + (((size_t)b * a.HG + hg) * (size_t)a.T + (size_t)t0) * G,
                        (uint32_t)ntok * G * 4u);
@@ -1335,14 +1363,13 @@ void partition_mfma_kernel(PartitionArgs a) {
   // requested a step ahead of its latents (the first step's before the
   // prologue), so the loads of dropped latent pieces can be left out
   MStep<R, G> cur;
-  MImp<Mg::kNT, Mg::kVU> icur, inxt;
-  if constexpr (kAd) load_mimp<R, G, Mg::kNT>(inxt, wave * CH, lane, slot, rimp);
+  float imp_next = 0.f;
+  uint64_t low = 0;  // the low rows of the step in `cur`
+  if constexpr (kAd) imp_next = load_step_imp<CH>(rimp, wave * CH, lane);
   prologue<R, G, kMfmaAfter>(a, b, hg, g, lds.base.q, lds.base.qt, [&]() {
-    load_mstep<R, G, Mg::kNT, kAux, kAd>(cur, wave * CH, koff, voff, rk, rv, &inxt, &ad);
-    if constexpr (kAd) {
-      icur = inxt;
-      load_mimp<R, G, Mg::kNT>(inxt, wave * CH + kWaves * CH, lane, slot, rimp);
-    }
+    if constexpr (kAd) low = low_rows<CH>(imp_next, lane, ad.thr);
+    load_mstep<R, G, Mg::kNT, kAux, kAd>(cur, wave * CH, koff, voff, rk, rv, low, &ad);
+    if constexpr (kAd) imp_next = load_step_imp<CH>(rimp, wave * CH + kWaves * CH, lane);
   });
 
   // A operands: row lane % 16 is head (lane % 16) % G; k-group lane / 16
@@ -1375,14 +1402,12 @@ void partition_mfma_kernel(PartitionArgs a) {
   float* wl = lds.w + wave * CH * G;
   for (int cb = wave * CH; cb < ntok; cb += kWaves * CH) {
     if (cb + CH <= ntok)
-      compute_mstep<R, G, false, kAd>(cur, cb, ntok, lane, qa, mm, ll, acc, wl, &icur, &ad);
+      compute_mstep<R, G, false, kAd, kCut>(cur, cb, ntok, lane, qa, mm, ll, acc, wl, low, &ad);
     else
-      compute_mstep<R, G, true, kAd>(cur, cb, ntok, lane, qa, mm, ll, acc, wl, &icur, &ad);
-    load_mstep<R, G, Mg::kNT, kAux, kAd>(cur, cb + kWaves * CH, koff, voff, rk, rv, &inxt, &ad);
-    if constexpr (kAd) {
-      icur = inxt;
-      load_mimp<R, G, Mg::kNT>(inxt, cb + 2 * kWaves * CH, lane, slot, rimp);
-    }
+      compute_mstep<R, G, true, kAd, kCut>(cur, cb, ntok, lane, qa, mm, ll, acc, wl, low, &ad);
+    if constexpr (kAd) low = low_rows<CH>(imp_next, lane, ad.thr);
+    load_mstep<R, G, Mg::kNT, kAux, kAd>(cur, cb + kWaves * CH, koff, voff, rk, rv, low, &ad);
+    if constexpr (kAd) imp_next = load_step_imp<CH>(rimp, cb + 2 * kWaves * CH, lane);
   }
 
   mfma_epilogue<R, G, Mg::kNT, kSeg>(a, b, hg, p, mm, ll, acc, lds.base);
@@ -2231,23 +2256,41 @@ template <class LT, int R>
 hipError_t launch_ag(int group, const PartitionArgs& a, hipStream_t s) {
   const dim3 grid(a.P, a.HG, a.B), block(kThreads);
   // bf16 latents with 4 or 8 heads per kv-head and r a multiple of 32: the
-  // matrix-core kernel, as for the plain decode
+  // matrix-core kernel, as for the plain decode (the kCut form when low_rank
+  // splits a 16-byte piece)
   if constexpr (mfma_scores(std::is_same<LT, LatBF16>::value ? LRATTN_BF16 : -1, R, 4)) {
     constexpr int X = kNonTemporal;
+    const bool cut = a.low_rank % 8 != 0;
     if (group == 4) {
-      hipLaunchKernelGGL((partition_mfma_kernel<R, 4, X, false, true>), grid, block, 0, s, a);
+      if (cut) hipLaunchKernelGGL((partition_mfma_kernel<R, 4, X, false, true, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((partition_mfma_kernel<R, 4, X, false, true>), grid, block, 0, s, a);
       return hipGetLastError();
     }
     if (group == 8) {
-      hipLaunchKernelGGL((partition_mfma_kernel<R, 8, X, false, true>), grid, block, 0, s, a);
+      if (cut) hipLaunchKernelGGL((partition_mfma_kernel<R, 8, X, false, true, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((partition_mfma_kernel<R, 8, X, false, true>), grid, block, 0, s, a);
       return hipGetLastError();
     }
   }
+  // the VALU form for the other shapes only: where the matrix-core kernel
+  // takes 4 and 8 heads, the VALU form of those groups is not built
+  constexpr bool kMfmaShape =
+      mfma_scores(std::is_same<LT, LatBF16>::value ? LRATTN_BF16 : -1, R, 4);
   switch (group) {
     case 1: hipLaunchKernelGGL((partition_kernel<LT, R, 1, kNonTemporal, true>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((partition_kernel<LT, R, 2, kNonTemporal, true>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((partition_kernel<LT, R, 4, kNonTemporal, true>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((partition_kernel<LT, R, 8, kNonTemporal, true>), grid, block, 0, s, a); break;
+    case 4:
+      if constexpr (!kMfmaShape) {
+        hipLaunchKernelGGL((partition_kernel<LT, R, 4, kNonTemporal, true>), grid, block, 0, s, a);
+        break;
+      }
+      return hipErrorInvalidValue;
+    case 8:
+      if constexpr (!kMfmaShape) {
+        hipLaunchKernelGGL((partition_kernel<LT, R, 8, kNonTemporal, true>), grid, block, 0, s, a);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

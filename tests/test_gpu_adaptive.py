@@ -71,6 +71,8 @@ CASES = {
     "g4_bf16_r128": ("gqa_vlm", dict(B=2, Hq=8, Hkv=2, r=128, T=900, seq_lens=[900, 301])),
     "g8_bf16_r128": ("gqa_vlm", dict(B=2, Hq=16, Hkv=2, r=128, T=500, seq_lens=[500, 64])),
     "g1_bf16_r128": ("llm7b", dict(B=2, Hq=2, Hkv=2, r=128, T=700, seq_lens=[700, 150])),
+    # 8 heads per kv-head on the VALU kernel (r = 48 is not a multiple of 32)
+    "g8_bf16_r48": ("ragged", dict(B=2, Hq=16, Hkv=2, T=900, seq_lens=[900, 203])),
 }
 
 
