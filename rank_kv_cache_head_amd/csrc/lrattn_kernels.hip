@@ -1025,8 +1025,9 @@ __device__ __forceinline__ float load_step_imp(__amdgpu_buffer_rsrc_t rimp, int 
 // mask (bit i: row cb + i is below the threshold).  Rows past the partition
 // read 0; their latents lie past the buffer whatever the mask says.
 template <int CH>
-__device__ __forceinline__ uint64_t low_rows(float imp, int lane, float thr) {
-  return __builtin_amdgcn_ballot_w64(lane < CH && imp < thr);
+__device__ __forceinline__ uint32_t low_rows(float imp, int lane, float thr) {
+  static_assert(CH <= 32, "one mask bit per row of the step");
+  return (uint32_t)__builtin_amdgcn_ballot_w64(lane < CH && imp < thr);
 }
 
 // A step's latent loads.  With attention-aware rank (kAd) `low` marks the
@@ -1035,7 +1036,7 @@ __device__ __forceinline__ uint64_t low_rows(float imp, int lane, float thr) {
 template <int R, int G, int NT, int kAux = kNonTemporal, bool kAd = false>
 __device__ __forceinline__ void load_mstep(MStep<R, G, NT>& st, int cb, uint32_t koff,
                                            uint32_t voff, __amdgpu_buffer_rsrc_t rk,
-                                           __amdgpu_buffer_rsrc_t rv, uint64_t low = 0,
+                                           __amdgpu_buffer_rsrc_t rv, uint32_t low = 0,
                                            const MAdaptive* ad = nullptr) {
   using Mg = MGeo<R, G, NT>;
   const int lane = threadIdx.x & 63, slot = lane / Mg::kLPR;
@@ -1073,7 +1074,7 @@ __device__ __forceinline__ void load_mstep(MStep<R, G, NT>& st, int cb, uint32_t
 template <int R, int G, int NT, bool kMask, bool kAd = false, bool kCut = false>
 __device__ __forceinline__ void mfma_scores(const MStep<R, G, NT>& st, int cb, int ntok, int lane,
                                             const bf16x8 (&qa)[3][MGeo<R, G, NT>::kKC],
-                                            float (&s)[NT][4], uint64_t low = 0,
+                                            float (&s)[NT][4], uint32_t low = 0,
                                             const MAdaptive* ad = nullptr) {
   constexpr int KC = MGeo<R, G, NT>::kKC;
   const int tok = lane & 15;
@@ -1130,7 +1131,7 @@ __device__ __forceinline__ void mfma_scores(const MStep<R, G, NT>& st, int cb, i
 template <int R, int G, int NT, bool kCut = false>
 __device__ __forceinline__ void softmax_values(const float (&s)[NT][4], const MStep<R, G, NT>& st,
                                                int lane, float (&mm)[4], float (&ll)[4],
-                                               float (&acc)[G][8], float* wl, uint64_t low = 0,
+                                               float (&acc)[G][8], float* wl, uint32_t low = 0,
                                                const MAdaptive* ad = nullptr) {
   using Mg = MGeo<R, G, NT>;
   constexpr int VU = Mg::kVU, RPW = Mg::kRPW, HL = Mg::kHL;
@@ -1232,7 +1233,7 @@ __device__ __forceinline__ void softmax_values(const float (&s)[NT][4], const MS
 template <int R, int G, bool kMask, bool kAd = false, bool kCut = false>
 __device__ __forceinline__ void compute_mstep(
     const MStep<R, G>& st, int cb, int ntok, int lane, const bf16x8 (&qa)[3][MGeo<R, G>::kKC],
-    float (&mm)[4], float (&ll)[4], float (&acc)[G][8], float* wl, uint64_t low = 0,
+    float (&mm)[4], float (&ll)[4], float (&acc)[G][8], float* wl, uint32_t low = 0,
     const MAdaptive* ad = nullptr) {
   float s[MGeo<R, G>::kNT][4];
   mfma_scores<R, G, MGeo<R, G>::kNT, kMask, kAd, kCut>(st, cb, ntok, lane, qa, s, low, ad);
@@ -1364,7 +1365,7 @@ void partition_mfma_kernel(PartitionArgs a) {
   // prologue), so the loads of dropped latent pieces can be left out
   MStep<R, G> cur;
   float imp_next = 0.f;
-  uint64_t low = 0;  // the low rows of the step in `cur`
+  uint32_t low = 0;  // the low rows of the step in `cur`
   if constexpr (kAd) imp_next = load_step_imp<CH>(rimp, wave * CH, lane);
   prologue<R, G, kMfmaAfter>(a, b, hg, g, lds.base.q, lds.base.qt, [&]() {
     if constexpr (kAd) low = low_rows<CH>(imp_next, lane, ad.thr);
