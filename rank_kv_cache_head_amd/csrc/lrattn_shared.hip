@@ -12,11 +12,14 @@
 // many partitions per head: head h then uses its kv-head's factor B_K[h / G]
 // (hpf = G), and q~ is formed once per head instead of once per partition.
 //
-// Grid (Hq, sequence blocks of 8); thread (coordinate j, block row s) forms
-// q~ for sequences s, s + 256 / r, ... of the block: the factor row B_K[h][j]
-// is streamed once per thread, 256 bytes per round, and reused across those
-// sequences; the query rows sit in LDS.  Every product is exact in fp32 and
-// the sums run over i in increasing order.
+// Grid (Hq, B): one workgroup per (head, sequence).  The head's factor block
+// B_K[h] (r x d) is read as consecutive 16-byte pieces, piece t + 256 k by
+// thread t, so every load instruction of a wave covers 1 KB of consecutive
+// bytes; a factor row is d / (elements per piece) consecutive pieces, held by
+// as many consecutive lanes of one wave, and each lane's columns are the same
+// for all its pieces.  A lane forms the products of its piece with the query
+// elements of those columns (exact in fp32, summed in increasing column
+// order), and the row's lanes add their partial sums in a fixed butterfly.
 #include <float.h>
 
 #include "lrattn.h"
@@ -27,7 +30,7 @@
 namespace lrattn {
 namespace {
 
-constexpr int kAbsorbPieces = 16;  // 16-byte pieces of a factor row per round
+constexpr int kAbsorbPieces = 8;  // 16-byte factor pieces per thread and round
 
 // The elements of one 16-byte piece as fp32 (4 for fp32, 8 for 16-bit types).
 template <int DT>
@@ -54,22 +57,19 @@ __device__ __forceinline__ void stage_q_piece(const u32x4& w, float* dst) {
   for (int e = 0; e < (DT == LRATTN_F32 ? 4 : 8); ++e) dst[e] = f[e];
 }
 
-// Every load is issued before anything waits: the first round of the
-// factor row, then the block's query rows (16-byte pieces, at most two per
-// thread), so the kernel costs about one memory round trip.  Query rows
-// past the batch load zeros (buffer bounds); pieces past a factor row are
-// loaded (the next row, or zeros past the block) and never used.
+// q~[b][h][j] = qscale * sum_i q[b][h][i] * B_K[h / hpf][j][i].  Every load is
+// issued before anything waits: the first round of factor pieces, then the
+// query row (one 16-byte piece for each of the first d * size / 16 threads).
+// Pieces past the block read zeros (buffer bounds) and are not stored.
 template <int R, int FT>
 __device__ __forceinline__ void absorb_body(const AbsorbHeadsArgs& a) {
-  constexpr int SB = 8;                      // sequences per workgroup
-  constexpr int TPJ = kThreads / R;          // threads per latent coordinate
-  constexpr int KPT = (SB + TPJ - 1) / TPJ;  // sequences per thread
   constexpr int ES = FT == LRATTN_F32 ? 4 : 2;
-  constexpr int EPP = 16 / ES;  // factor elements per piece
-  const int h = blockIdx.x, b0 = blockIdx.y * SB;
-  const int tid = threadIdx.x, j = tid % R, s0 = tid / R;
-  const int d = a.d, npieces = d / EPP;
-  // the head's factor block (a wave-uniform resource); row j at j d ES bytes
+  constexpr int EPP = 16 / ES;                   // factor elements per piece
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, d = a.d;
+  const int ppr = d / EPP;                       // pieces per factor row: 8 .. 64
+  const int npieces = R * ppr;
+  const int c0 = (tid % ppr) * EPP;              // this thread's columns, every round
   const auto rb = make_rsrc(static_cast<const char*>(a.BK) + (size_t)(h / a.hpf) * R * d * ES,
                             (uint32_t)(R * d * ES));
   u32x4 w[kAbsorbPieces];
@@ -77,68 +77,48 @@ __device__ __forceinline__ void absorb_body(const AbsorbHeadsArgs& a) {
 #pragma unroll
     for (int k = 0; k < kAbsorbPieces; ++k)
       w[k] = __builtin_amdgcn_raw_buffer_load_b128(
-          rb, j * d * ES + (r0 * kAbsorbPieces + k) * 16, 0, 0);
+          rb, (int)((uint32_t)(r0 + k * kThreads + tid) * 16u), 0, 0);
   };
   load_round(0);
 
-  __shared__ float qs[SB][kMaxHeadDim];
+  __shared__ float qs[kMaxHeadDim];
   {
     const int qes = a.q_dtype == LRATTN_F32 ? 4 : 2;
-    const int qpr = d * qes / 16;  // pieces per query row
-    const int nb = min(SB, a.B - b0);
-    const uint32_t qrow = (uint32_t)a.Hq * d * qes;  // bytes between sequences
-    const auto rq = make_rsrc(static_cast<const char*>(a.q) + ((size_t)b0 * a.Hq + h) * d * qes,
-                              (uint32_t)(nb - 1) * qrow + (uint32_t)(d * qes));
-    u32x4 qw[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int e = tid + k * kThreads, sq = e / qpr, c = e - sq * qpr;
-      const uint32_t off = sq < nb ? (uint32_t)sq * qrow + (uint32_t)c * 16u : kOffNone;
-      qw[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)off, 0, 0);
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int e = tid + k * kThreads, sq = e / qpr, c = e - sq * qpr;
-      if (sq < SB) {
-        if (a.q_dtype == LRATTN_F32) stage_q_piece<LRATTN_F32>(qw[k], &qs[sq][4 * c]);
-        else if (a.q_dtype == LRATTN_BF16) stage_q_piece<LRATTN_BF16>(qw[k], &qs[sq][8 * c]);
-        else stage_q_piece<LRATTN_F16>(qw[k], &qs[sq][8 * c]);
-      }
+    const int qpr = d * qes / 16;  // pieces of the query row
+    const auto rq = make_rsrc(static_cast<const char*>(a.q) + ((size_t)b * a.Hq + h) * d * qes,
+                              (uint32_t)(d * qes));
+    const u32x4 qw = __builtin_amdgcn_raw_buffer_load_b128(
+        rq, (int)(tid < qpr ? (uint32_t)tid * 16u : kOffNone), 0, 0);
+    if (tid < qpr) {
+      if (a.q_dtype == LRATTN_F32) stage_q_piece<LRATTN_F32>(qw, &qs[4 * tid]);
+      else if (a.q_dtype == LRATTN_BF16) stage_q_piece<LRATTN_BF16>(qw, &qs[8 * tid]);
+      else stage_q_piece<LRATTN_F16>(qw, &qs[8 * tid]);
     }
   }
   __syncthreads();
-  if (s0 >= TPJ) return;  // r = 48: 16 threads without a coordinate
-
-  // acc[m] = sum_i qs[s0 + m TPJ][i] * B_K[h][j][i], i in increasing order
-  float acc[KPT];
+  float qv[EPP];
 #pragma unroll
-  for (int m = 0; m < KPT; ++m) acc[m] = 0.f;
-  for (int r0 = 0; r0 * kAbsorbPieces < npieces; ++r0) {
+  for (int e = 0; e < EPP; ++e) qv[e] = qs[c0 + e];
+
+  float* qt = a.qt + ((size_t)b * a.Hq + h) * R;
+  for (int r0 = 0; r0 < npieces; r0 += kAbsorbPieces * kThreads) {
     if (r0 > 0) {
       load_round(r0);
       __builtin_amdgcn_sched_barrier(0);  // the round's loads ahead of its arithmetic
     }
 #pragma unroll
     for (int k = 0; k < kAbsorbPieces; ++k) {
-      const int pc = r0 * kAbsorbPieces + k;
-      if (pc < npieces) {
+      const int pc = r0 + k * kThreads + tid;  // the same for the lanes of a row
+      if (r0 + k * kThreads < npieces) {     // the same in every thread (all lanes shuffle)
         float f[EPP];
         unpack_piece<FT>(w[k], f);
+        float acc = 0.f;
 #pragma unroll
-        for (int m = 0; m < KPT; ++m) {
-          const int sq = s0 + m * TPJ;
-          if (sq < SB) {
-#pragma unroll
-            for (int e = 0; e < EPP; ++e) acc[m] = fmaf(qs[sq][pc * EPP + e], f[e], acc[m]);
-          }
-        }
+        for (int e = 0; e < EPP; ++e) acc = fmaf(qv[e], f[e], acc);
+        for (int off = 1; off < ppr; off <<= 1) acc += __shfl_xor(acc, off);
+        if (tid % ppr == 0 && pc < npieces) qt[pc / ppr] = acc * a.qscale;
       }
     }
-  }
-#pragma unroll
-  for (int m = 0; m < KPT; ++m) {
-    const int sq = s0 + m * TPJ, b = b0 + sq;
-    if (sq < SB && b < a.B) a.qt[((size_t)b * a.Hq + h) * R + j] = acc[m] * a.qscale;
   }
 }
 
@@ -151,8 +131,7 @@ __global__ __launch_bounds__(kThreads) void absorb_heads_kernel(AbsorbHeadsArgs 
 
 template <int R>
 hipError_t launch_r(const AbsorbHeadsArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((absorb_heads_kernel<R>), dim3(a.Hq, (a.B + 7) / 8), dim3(kThreads), 0, s,
-                     a);
+  hipLaunchKernelGGL((absorb_heads_kernel<R>), dim3(a.Hq, a.B), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
