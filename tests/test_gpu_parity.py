@@ -639,6 +639,30 @@ def test_partition_then_combine_equals_decode(name, splits):
     assert rel_rowmax(out.cpu().numpy(), _full_oracle(w)) <= TOL[w.latent_dtype]
 
 
+@pytest.mark.parametrize("base,kw", [
+    # fp32 factors at d = 256: 64 pieces per factor row, four load rounds
+    ("gqa_vlm", dict(B=2, Hq=2, Hkv=2, r=128, d=256, T=700, seq_lens=[700, 333],
+                     q_dtype="f32", factor_dtype="f32")),
+    # 2-byte factors at r = 16, d = 64: 128 pieces, half a round
+    ("tiny", dict(B=2, T=256, seq_lens=[256, 100], q_dtype="bf16", factor_dtype="bf16")),
+    # fp16 query and factors, 4 heads per kv-head, d = 64: 8 pieces per row
+    ("gqa_vlm", dict(B=2, Hq=8, Hkv=2, r=32, d=64, T=900, seq_lens=[900, 45],
+                     q_dtype="f16", factor_dtype="f16")),
+    # the ragged workload's shape family: r = 48, one head per kv-head
+    ("ragged", dict(B=3, Hq=3, Hkv=3, T=2000, seq_lens=[2000, 1500, 64])),
+])
+def test_queries_absorbed_ahead(base, kw):
+    """With 64 or more partitions per head the queries are absorbed once per
+    query head by a kernel of their own; its factor-piece geometry depends
+    on r, d and the factor type.  Compared with the oracle at 100 splits."""
+    w = workloads.make(base, **kw)
+    say(f"absorbed ahead {base} {kw}")
+    got = run_decode(w, num_splits=100).cpu().numpy()
+    err = rel_rowmax(got, _full_oracle(w))
+    say(f"  err {err:.3e}")
+    assert err <= TOL[w.latent_dtype], err
+
+
 def test_side_stream():
     import torch
     w = workloads.make("gqa_vlm", **SMALL["gqa_vlm"])
