@@ -139,3 +139,24 @@ def test_adaptive_full_size_gqa_vlm():
         _check_update(new[sel], ref_imp, imp[sel], 0.9, w.seq_lens[sel])
     say(f"  err {err:.3e}")
     assert err <= TOL[w.latent_dtype], err
+
+
+def test_adaptive_full_size_r128_bench_setting():
+    """The benchmark's r = 128 leg at full size: gqa_vlm's batch, heads and
+    lengths over a 256-byte-row cache, low rank 64 below threshold 0.5 with
+    decay 1.0 (half the rows skip their second 128-byte line); every
+    sequence against the oracle."""
+    w = workloads.make("gqa_vlm", r=128, factor_std=1.0 / np.sqrt(128))
+    say("adaptive full gqa_vlm r=128: inputs")
+    dev = to_device(w)
+    imp = _importance(w, 5)
+    say("adaptive full gqa_vlm r=128: decode")
+    out, new = _run(w, dev, imp, 64, 0.5, 1.0)
+    assert np.array_equal(new, imp)      # decay 1.0 keeps the scores
+    err = 0.0
+    for b in range(w.batch):
+        sel = [b]
+        ref_out, _ = _ref(w, imp, 64, 0.5, 1.0, sel=sel)
+        err = max(err, rel_rowmax(out[sel], ref_out))
+    say(f"  err {err:.3e}")
+    assert err <= TOL[w.latent_dtype], err
