@@ -1005,7 +1005,32 @@ struct MAdaptive {
   int keepk;   // columns that piece keeps (1..7)
   int keepv;   // columns this lane's value piece keeps (8 when it is not cut)
   __amdgpu_buffer_rsrc_t rlg;  // the group's logits [token][G] from the partition start
+  float* lgs;  // the workgroup's LDS chunk of logits [row % lg_rows][G]
 };
+
+// Rows of logits a workgroup of the adaptive matrix-core kernel stages in LDS
+// before writing them out (a power of two, a multiple of the 128 rows of a
+// round of the four waves), sized so that the chunk does not lower the
+// kernel's occupancy: 32 or 64 KB, over the LDS of the prologue and epilogue.
+template <int R, int G>
+constexpr int lg_rows() {
+  return G == 8 ? (R == 128 ? 2048 : 1024) : (R == 128 ? 4096 : 2048);
+}
+
+// The logits of rows [c0, c1) from the LDS chunk to HBM: 16 bytes per thread
+// and instruction, every instruction of the workgroup 4 KB of consecutive
+// bytes.  Between two barriers of the whole workgroup.
+template <int G>
+__device__ __forceinline__ void flush_logits(const MAdaptive& ad, int c0, int c1) {
+  const int n4 = (c1 - c0) * G / 4;  // 16-byte pieces
+  const float4* src = reinterpret_cast<const float4*>(ad.lgs);
+  for (int i = threadIdx.x; i < n4; i += kThreads) {
+    const float4 v = src[i];
+    const u32x4 w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                     __float_as_uint(v.w)};
+    __builtin_amdgcn_raw_buffer_store_b128(w, ad.rlg, (int)((uint32_t)(c0 * G + 4 * i) * 4u), 0, 0);
+  }
+}
 
 // Latent word holding elements e0 (low half) and e0 + 1 (high half): the
 // elements at or past `keep` become zero.
@@ -1103,16 +1128,14 @@ __device__ __forceinline__ void mfma_scores(const MStep<R, G, NT>& st, int cb, i
                                                     d, 0, 0, 0);
     }
     if constexpr (kAd) {
-      // the logits, token-major per head group: lanes 0-15 hold heads 0-3 of
-      // their token, lanes 16-31 heads 4-7 (G = 8); 16 bytes a lane, one
-      // store per tile; rows past the partition are dropped (offset past
-      // the buffer)
-      const int row = cb + 16 * t + tok;
-      const bool writer = lane < (G == 8 ? 32 : 16) && row < ntok;
-      const uint32_t off = writer ? (uint32_t)(row * G + 4 * ((lane >> 4) & 1)) * 4u : kOffNone;
-      const u32x4 v = {__float_as_uint(d[0]), __float_as_uint(d[1]), __float_as_uint(d[2]),
-                       __float_as_uint(d[3])};
-      __builtin_amdgcn_raw_buffer_store_b128(v, ad->rlg, (int)off, 0, 0);
+      // the logits into the LDS chunk, token-major per head group: lanes
+      // 0-15 hold heads 0-3 of their token, lanes 16-31 heads 4-7 (G = 8);
+      // rows past the partition are staged but never written out
+      constexpr int kLg = lg_rows<R, G>();
+      const int row = (cb + 16 * t + tok) & (kLg - 1);
+      if (lane < (G == 8 ? 32 : 16))
+        *reinterpret_cast<float4*>(ad->lgs + row * G + 4 * ((lane >> 4) & 1)) =
+            make_float4(d[0], d[1], d[2], d[3]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1293,6 +1316,17 @@ struct MPartLds {
   float w[kWaves * MGeo<R, G>::kChunk * G];
 };
 
+// The adaptive form: the LDS chunk of logits overlays the query staging and
+// the merge area, which are idle while the partition streams.
+template <int R, int G>
+struct MPartLdsAd {
+  union {
+    PartLds<R, G> base;
+    float lg[lg_rows<R, G>() * G];
+  };
+  float w[kWaves * MGeo<R, G>::kChunk * G];
+};
+
 // Occupancy targets (waves per SIMD) of the attention-aware forms, each the
 // highest without spills: with 8 heads the adaptive form needs more registers
 // than three waves per SIMD allow; with 4 heads it fits the plain form's;
@@ -1325,7 +1359,7 @@ void partition_mfma_kernel(PartitionArgs a) {
   if (t0 >= t1) return;  // partition past the sequence: nothing to write
   const int ntok = t1 - t0;
 
-  __shared__ MPartLds<R, G> lds;
+  __shared__ std::conditional_t<kAd, MPartLdsAd<R, G>, MPartLds<R, G>> lds;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slot = lane / LPR, cc = lane % LPR;
 
@@ -1337,7 +1371,9 @@ void partition_mfma_kernel(PartitionArgs a) {
   // 64-byte (32-column) step; value layout: slot rows, 16 bytes per lane
   const uint32_t koff = (uint32_t)((lane & 15) * Mg::kRowBytes + (lane >> 4) * 16);
   const uint32_t voff = (uint32_t)(slot * Mg::kRowBytes + cc * 16);
-  // attention-aware rank: the partition's importance scores and logits
+  // attention-aware rank: the partition's importance scores and logits (the
+  // logits are staged in LDS and written out a chunk at a time: stores mixed
+  // into the latent stream cost far more than their bytes)
   __amdgpu_buffer_rsrc_t rimp = rk;
   MAdaptive ad{};
   if constexpr (kAd) {
@@ -1358,6 +1394,7 @@ void partition_mfma_kernel(PartitionArgs a) {
     ad.keepv = min(max(a.low_rank - cc * 8, 0), 8);
     ad.rlg = make_rsrc(a.logits + (((size_t)b * a.HG + hg) * (size_t)a.T + (size_t)t0) * G,
                        (uint32_t)ntok * G * 4u);
+    if constexpr (kAd) ad.lgs = lds.lg;
   }
 
   // attention-aware rank: the importance scores of each step's rows are
@@ -1388,6 +1425,8 @@ void partition_mfma_kernel(PartitionArgs a) {
       for (int term = 0; term < 3; ++term) qa[term][c] = t[term];
     }
   }
+  // the logits chunk overlays q~, which every wave has read above
+  if constexpr (kAd) __syncthreads();
 
   float mm[4], ll[4], acc[G][8];
 #pragma unroll
@@ -1401,14 +1440,37 @@ void partition_mfma_kernel(PartitionArgs a) {
     ll[i] = 0.f;
   }
   float* wl = lds.w + wave * CH * G;
-  for (int cb = wave * CH; cb < ntok; cb += kWaves * CH) {
-    if (cb + CH <= ntok)
-      compute_mstep<R, G, false, kAd, kCut>(cur, cb, ntok, lane, qa, mm, ll, acc, wl, low, &ad);
-    else
-      compute_mstep<R, G, true, kAd, kCut>(cur, cb, ntok, lane, qa, mm, ll, acc, wl, low, &ad);
-    if constexpr (kAd) low = low_rows<CH>(imp_next, lane, ad.thr);
-    load_mstep<R, G, Mg::kNT, kAux, kAd>(cur, cb + kWaves * CH, koff, voff, rk, rv, low, &ad);
-    if constexpr (kAd) imp_next = load_step_imp<CH>(rimp, cb + 2 * kWaves * CH, lane);
+  if constexpr (!kAd) {
+    for (int cb = wave * CH; cb < ntok; cb += kWaves * CH) {
+      if (cb + CH <= ntok)
+        compute_mstep<R, G, false>(cur, cb, ntok, lane, qa, mm, ll, acc, wl);
+      else
+        compute_mstep<R, G, true>(cur, cb, ntok, lane, qa, mm, ll, acc, wl);
+      load_mstep<R, G, Mg::kNT, kAux>(cur, cb + kWaves * CH, koff, voff, rk, rv);
+    }
+  } else {
+    // rounds of the four waves (128 rows), the same count in every wave so
+    // that the chunk flushes can synchronize the workgroup; a wave whose
+    // step lies past the partition computes nothing in that round
+    constexpr int kRound = kWaves * CH, kLg = lg_rows<R, G>(), kRPC = kLg / kRound;
+    static_assert(kLg % kRound == 0, "a chunk is whole rounds");
+    const int nround = (ntok + kRound - 1) / kRound;
+    for (int r = 0; r < nround; ++r) {
+      const int cb = wave * CH + r * kRound;
+      if (cb + CH <= ntok)
+        compute_mstep<R, G, false, kAd, kCut>(cur, cb, ntok, lane, qa, mm, ll, acc, wl, low, &ad);
+      else if (cb < ntok)
+        compute_mstep<R, G, true, kAd, kCut>(cur, cb, ntok, lane, qa, mm, ll, acc, wl, low, &ad);
+      low = low_rows<CH>(imp_next, lane, ad.thr);
+      load_mstep<R, G, Mg::kNT, kAux, kAd>(cur, cb + kRound, koff, voff, rk, rv, low, &ad);
+      imp_next = load_step_imp<CH>(rimp, cb + 2 * kRound, lane);
+      if ((r + 1) % kRPC == 0 || r + 1 == nround) {
+        const int c0 = (r / kRPC) * kLg;
+        __syncthreads();  // the chunk's rows are in LDS
+        flush_logits<G>(ad, c0, min(c0 + kLg, ntok));
+        __syncthreads();  // and read before the next chunk's rows
+      }
+    }
   }
 
   mfma_epilogue<R, G, Mg::kNT, kSeg>(a, b, hg, p, mm, ll, acc, lds.base);
