@@ -216,9 +216,28 @@ struct AdaptiveRow {
   float thr;
   int keep;
   int col;       // this lane's place in its row (it stages heads col, col + LPR, ...)
-  float* lds;    // the wave's staging tile [rows per wave per step][G]
+  float* lds;    // the workgroup's LDS chunk of logits [row % valu_lg_rows][G]
   __amdgpu_buffer_rsrc_t rlg;  // the group's logits [token][G] from the partition start
 };
+
+// Rows of logits a workgroup of the adaptive VALU kernel stages in LDS (16 KB)
+// before writing them out: stores mixed into the latent stream cost far more
+// than their bytes, so they leave a chunk at a time.
+template <int G>
+constexpr int valu_lg_rows() {
+  return 4096 / G;
+}
+
+// The logits of rows [c0, c1) from a VALU kernel's LDS chunk to HBM: 4 bytes
+// per thread and instruction, 1 KB of consecutive bytes per instruction of
+// the workgroup.  Between two barriers of the whole workgroup.
+template <int G>
+__device__ __forceinline__ void flush_valu_logits(const AdaptiveRow& ad, int c0, int c1) {
+  const int n = (c1 - c0) * G;
+  for (int i = threadIdx.x; i < n; i += kThreads)
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ad.lds[i]), ad.rlg,
+                                          (int)((uint32_t)(c0 * G + i) * 4u), 0, 0);
+}
 
 // q~ of this lane's columns: registers, or (kQtInLds) LDS rows of stride R.
 template <class LT, int R, int G>
@@ -260,7 +279,8 @@ __device__ __forceinline__ void compute_step(
       t = group_sum<Gm::kLPR>(t);
       if constexpr (kInt8) t *= st.sk[u];
       if constexpr (kAd) {
-        if (h % Gm::kLPR == ad.col) ad.lds[(u * RPW + slot) * G + h] = t;
+        constexpr int kLg = valu_lg_rows<G>();
+        if (h % Gm::kLPR == ad.col) ad.lds[((cb + u * RPW + slot) & (kLg - 1)) * G + h] = t;
       }
       if constexpr (kMask) {
         if (cb + u * RPW + slot >= ntok) t = -INFINITY;
@@ -268,28 +288,6 @@ __device__ __forceinline__ void compute_step(
       s[u][h] = t;
     }
   }
-  if constexpr (kAd) {
-    // the step's logits leave through the wave's LDS tile in the logits'
-    // token-major layout ([token][head] per head group), so each store
-    // instruction writes 256 contiguous bytes (one 4-byte store per row and
-    // head into [head][token] rows cost ~40 us of the step at gqa_vlm).
-    // Rows past the partition get an offset past the buffer and are
-    // dropped.  wave_sync: the other lanes' tile stores are visible to the
-    // reads below, and (after the loop) those reads are done before the next
-    // step's stores.
-    constexpr int NV = G * Gm::kChunk;
-    const int lane = threadIdx.x & 63;
-    wave_sync();
-#pragma unroll
-    for (int k = 0; k < (NV + 63) / 64; ++k) {
-      const int i = min(64 * k + lane, NV - 1), r = i / G;
-      const bool ok = (NV % 64 == 0 || 64 * k + lane < NV) && cb + r < ntok;
-      const uint32_t off = ok ? (uint32_t)(cb * G + i) * 4u : kOffNone;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ad.lds[i]), ad.rlg, (int)off, 0, 0);
-    }
-    wave_sync();
-  }
-
   // online softmax per slot and head, with a lazily moved reference max: the
   // running reference m only moves when a score exceeds it by more than
   // kLazyLog2 (base-2 logits), so weights 2^(s - m) stay <= 2^kLazyLog2 and
@@ -826,7 +824,7 @@ void partition_kernel(PartitionArgs a) {
   const int ntok = t1 - t0;
 
   __shared__ PartLds<R, G> lds;
-  __shared__ float lg_lds[kAd ? kWaves * G * CH : 1];  // adaptive rank: logits staging
+  __shared__ float lg_lds[kAd ? valu_lg_rows<G>() * G : 1];  // adaptive rank: logits chunk
   float* q_lds = lds.q;
   float* qt_lds = lds.qt;
 
@@ -858,7 +856,7 @@ void partition_kernel(PartitionArgs a) {
     ad.thr = a.imp_thr;
     ad.keep = min(max(a.low_rank - cc * EPL, 0), EPL);
     ad.col = cc;
-    ad.lds = lg_lds + wave * G * CH;
+    ad.lds = lg_lds;
     ad.rlg = make_rsrc(a.logits + (((size_t)b * a.HG + hg) * (size_t)a.T + (size_t)t0) * G,
                        (uint32_t)ntok * G * 4u);
   }
@@ -900,14 +898,38 @@ void partition_kernel(PartitionArgs a) {
   // one step in flight per wave: the next step's loads are issued once this
   // step's registers are free (past the partition they return zero without
   // touching memory)
-  for (int cb = cb0; cb < ntok; cb += kStride) {
-    if (cb + CH <= ntok)
-      compute_step<LT, R, G, false, kAd>(cur, cb, ntok, slot, qt, m, l, acc, ad);
-    else
-      compute_step<LT, R, G, true, kAd>(cur, cb, ntok, slot, qt, m, l, acc, ad);
-    load_step<LT, R, G, kAux, kAd>(cur, cb + kStride, slot, lane_off, rk, rv, rsk, rsv, inx,
-                                   ad.thr, drop);
-    if constexpr (kAd) load_imp<LT, R, G>(cb + 2 * kStride, slot, rimp, inx);
+  if constexpr (!kAd) {
+    for (int cb = cb0; cb < ntok; cb += kStride) {
+      if (cb + CH <= ntok)
+        compute_step<LT, R, G, false, kAd>(cur, cb, ntok, slot, qt, m, l, acc, ad);
+      else
+        compute_step<LT, R, G, true, kAd>(cur, cb, ntok, slot, qt, m, l, acc, ad);
+      load_step<LT, R, G, kAux, kAd>(cur, cb + kStride, slot, lane_off, rk, rv, rsk, rsv, inx,
+                                     ad.thr, drop);
+    }
+  } else {
+    // rounds of the four waves, the same count in every wave so that the
+    // chunk flushes can synchronize the workgroup; a wave whose step lies
+    // past the partition computes nothing in that round
+    constexpr int kLg = valu_lg_rows<G>(), kRPC = kLg / kStride;
+    static_assert(kLg % kStride == 0, "a chunk is whole rounds");
+    const int nround = (ntok + kStride - 1) / kStride;
+    for (int r = 0; r < nround; ++r) {
+      const int cb = cb0 + r * kStride;
+      if (cb + CH <= ntok)
+        compute_step<LT, R, G, false, kAd>(cur, cb, ntok, slot, qt, m, l, acc, ad);
+      else if (cb < ntok)
+        compute_step<LT, R, G, true, kAd>(cur, cb, ntok, slot, qt, m, l, acc, ad);
+      load_step<LT, R, G, kAux, kAd>(cur, cb + kStride, slot, lane_off, rk, rv, rsk, rsv, inx,
+                                     ad.thr, drop);
+      load_imp<LT, R, G>(cb + 2 * kStride, slot, rimp, inx);
+      if ((r + 1) % kRPC == 0 || r + 1 == nround) {
+        const int c0 = (r / kRPC) * kLg;
+        __syncthreads();  // the chunk's rows are in LDS
+        flush_valu_logits<G>(ad, c0, min(c0 + kLg, ntok));
+        __syncthreads();  // and read before the next chunk's rows
+      }
+    }
   }
 
   // ---- merge the slots of this wave (lanes with equal cc)
