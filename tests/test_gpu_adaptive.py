@@ -160,3 +160,30 @@ def test_adaptive_full_size_r128_bench_setting():
         err = max(err, rel_rowmax(out[sel], ref_out))
     say(f"  err {err:.3e}")
     assert err <= TOL[w.latent_dtype], err
+
+
+@pytest.mark.parametrize("base,kw", [
+    # matrix-core kernel, 4 heads at r = 64 (2048-row chunks): three chunks, the last partial
+    ("gqa_vlm", dict(B=2, Hq=8, Hkv=2, T=5000, seq_lens=[5000, 2100])),
+    # matrix-core kernel, 8 heads at r = 64 (1024-row chunks)
+    ("gqa_vlm", dict(B=1, Hq=16, Hkv=2, T=3000, seq_lens=[2999])),
+    # VALU kernel, one head per kv-head (4096-row chunks)
+    ("llm7b", dict(B=2, Hq=2, Hkv=2, T=9000, seq_lens=[9000, 4097])),
+    # VALU kernel, int8 latents, 4 heads (1024-row chunks)
+    ("int8", dict(B=1, Hq=8, Hkv=2, T=2500, seq_lens=[2500])),
+])
+def test_adaptive_logits_in_several_chunks(base, kw):
+    """One partition per sequence, longer than the LDS chunk of logits the
+    partition kernel stages: the logits leave in several chunks (the last
+    one partial) and the score update must still match the oracle."""
+    w = workloads.make(base, **kw)
+    dev = to_device(w)
+    imp = _importance(w, 7)
+    k = w.rank // 2
+    say(f"adaptive chunks {base} {kw}")
+    out, new = _run(w, dev, imp, k, 0.5, 0.6, num_splits=1)
+    ref_out, ref_imp = _ref(w, imp, k, 0.5, 0.6)
+    err = rel_rowmax(out, ref_out)
+    say(f"  err {err:.3e}")
+    assert err <= TOL[w.latent_dtype], err
+    _check_update(new, ref_imp, imp, 0.6, w.seq_lens)
