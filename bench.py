@@ -10,7 +10,10 @@ Inputs are seeded synthetic tensors with the workload's shapes and value
 distributions, resident in HBM before timing starts.  The headline workload
 is the largest, ragged long context (4 sequences x 40 heads, lengths up to
 131072, 256 partitions per head); the other workloads are timed the same way
-and reported under `other_workloads`.
+and reported under `other_workloads`.  Every workload's decode runs exactly K
+timed and W untimed steps; the side legs (dense cache, rebuilt keys, append,
+shared stream, modal factors, adaptive rank) run at least `leg_steps` and
+`leg_warmup` of each.
 
 Printed: one JSON line.  `value` = decode tokens/s = B * K / (wall time of K
 steps), bracketed by device synchronization.  `roofline` describes the
@@ -40,6 +43,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0       # MI355X published HBM3E bandwidth
 ROTATE_BYTES = 1 << 30       # rotate input copies so the 256 MB MALL cannot hold them
+LEG_MIN_STEPS = 100          # timed calls of every sub-measurement, at least
+LEG_MIN_WARMUP = 20          # untimed calls before them, at least
 WORKLOAD_TEXT = {
     "tiny": "tiny: B=1 H=4 d=64 r=16 T=256 fp32",
     "llm7b": "7B-LLM-like decode: B=8 H=32 d=128 r=32 T=4096 bf16",
@@ -334,6 +339,15 @@ def main():
     # large buffers; gqa_vlm's inputs stay resident for the legs that do
     # not apply to the headline workload (rebuilt keys need r 32 or 64,
     # separate image/text factors need an image block)
+    # The side legs below (dense cache, rebuilt keys, append, shared stream,
+    # modal factors, adaptive rank) are sub-measurements: each runs at least
+    # LEG_MIN_STEPS timed calls after LEG_MIN_WARMUP untimed ones, so that a
+    # short run (--steps 20 --warmup 5) still times them past their ramp-up
+    # (the matrix-core-heavy rebuilt-key legs lower the shader clock over
+    # their first launches); the decode of every workload uses K and W.
+    la = argparse.Namespace(**vars(args))
+    la.steps, la.warmup = max(args.steps, LEG_MIN_STEPS), max(args.warmup, LEG_MIN_WARMUP)
+    line["leg_steps"], line["leg_warmup"] = la.steps, la.warmup
     others = [x for x in args.also.split(",") if x and x != args.config]
     aux = {}
     if others:
@@ -371,7 +385,7 @@ def main():
             order = list(aux.values()) + [m]
         for mm in order:
             sp = args.num_splits or workloads.SPLITS.get(mm.w.name, 0)
-            res = fn(mm.w, torch, lr, args, sp, *[e(mm) for e in extra])
+            res = fn(mm.w, torch, lr, la, sp, *[e(mm) for e in extra])
             if res is not None:
                 res["workload"] = mm.w.name
                 return res
