@@ -158,37 +158,44 @@ struct Step {
   uint32_t v[Geo<LT, R, G>::kU][Geo<LT, R, G>::kWords];
   float sk[Geo<LT, R, G>::kU];
   float sv[Geo<LT, R, G>::kU];
-  float imp[Geo<LT, R, G>::kU];  // adaptive rank: the rows' importance scores
+  uint64_t low;  // adaptive rank: bit i set when the step's row cb + i is below the threshold
 };
 
-// Attention-aware rank: the importance scores of a step's rows (lane slot's
-// rows cb + slot + RPW u), loaded a step ahead of the rows' latents.
+// Attention-aware rank: the importance scores of a step's rows cb .. cb +
+// kChunk - 1, one per lane, loaded a step ahead of the rows' latents ...
 template <class LT, int R, int G>
-__device__ __forceinline__ void load_imp(int cb, int slot, __amdgpu_buffer_rsrc_t rimp,
-                                         float (&imp)[Geo<LT, R, G>::kU]) {
-  using Gm = Geo<LT, R, G>;
-#pragma unroll
-  for (int u = 0; u < Gm::kU; ++u) imp[u] = bload4f(rimp, (uint32_t)(cb + u * Gm::kRPW + slot) * 4u);
+__device__ __forceinline__ float load_imp(int cb, __amdgpu_buffer_rsrc_t rimp) {
+  constexpr int CH = Geo<LT, R, G>::kChunk;
+  static_assert(CH <= 64, "one score per lane");
+  const int lane = threadIdx.x & 63;
+  return bload4f(rimp, lane < CH ? (uint32_t)(cb + lane) * 4u : kOffNone);
 }
 
-// A step's latent loads.  With attention-aware rank (kAd) the rows'
-// importance scores `imp` are already in registers: a row below `thr` keeps
-// only coordinates [0, low_rank), so a lane whose whole piece lies past
-// low_rank (`drop`) gives that row's loads an offset past the buffer, which
-// fetches nothing and returns the zeros the masking would produce.
+// ... and, once they have arrived, the step's rows below the threshold as one
+// wave-uniform mask.
+template <class LT, int R, int G>
+__device__ __forceinline__ uint64_t low_mask(float imp, float thr) {
+  const int lane = threadIdx.x & 63;
+  return __builtin_amdgcn_ballot_w64(lane < Geo<LT, R, G>::kChunk && imp < thr);
+}
+
+// A step's latent loads.  With attention-aware rank (kAd) `low` marks the
+// step's rows below the threshold: such a row keeps only coordinates
+// [0, low_rank), so a lane whose whole piece lies past low_rank (`drop`)
+// gives that row's loads an offset past the buffer, which fetches nothing
+// and returns the zeros the masking would produce.
 template <class LT, int R, int G, int kAux = kNonTemporal, bool kAd = false>
 __device__ __forceinline__ void load_step(Step<LT, R, G>& st, int cb, int slot, uint32_t lane_off,
                                           __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                           __amdgpu_buffer_rsrc_t rsk, __amdgpu_buffer_rsrc_t rsv,
-                                          const float* imp = nullptr, float thr = 0.f,
-                                          bool drop = false) {
+                                          uint64_t low = 0, bool drop = false) {
   using Gm = Geo<LT, R, G>;
   constexpr int U = Gm::kU, RPW = Gm::kRPW;
   uint32_t off[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     off[u] = (uint32_t)(cb + u * RPW) * Gm::kRowBytes + lane_off;
-    if constexpr (kAd) off[u] = drop && imp[u] < thr ? kOffNone : off[u];
+    if constexpr (kAd) off[u] = drop && ((low >> (u * RPW + slot)) & 1u) ? kOffNone : off[u];
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) load_words<Gm::kWords, kAux>(st.k[u], rk, off[u]);
@@ -202,10 +209,7 @@ __device__ __forceinline__ void load_step(Step<LT, R, G>& st, int cb, int slot, 
       st.sv[u] = bload4f(rsv, so);
     }
   }
-  if constexpr (kAd) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) st.imp[u] = imp[u];
-  }
+  if constexpr (kAd) st.low = low;
 }
 
 // Attention-aware rank (AttentionPack page, section 2.B): a row whose
@@ -267,7 +271,7 @@ __device__ __forceinline__ void compute_step(
     float x[EPL];
     Unpack<LT>::run(st.k[u], x);
     if constexpr (kAd) {
-      const bool low = st.imp[u] < ad.thr;
+      const bool low = (st.low >> (u * RPW + slot)) & 1u;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) x[e] = (low && e >= ad.keep) ? 0.f : x[e];
     }
@@ -333,7 +337,7 @@ __device__ __forceinline__ void compute_step(
     float x[EPL];
     Unpack<LT>::run(st.v[u], x);
     if constexpr (kAd) {
-      const bool low = st.imp[u] < ad.thr;
+      const bool low = (st.low >> (u * RPW + slot)) & 1u;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) x[e] = (low && e >= ad.keep) ? 0.f : x[e];
     }
@@ -867,12 +871,13 @@ void partition_kernel(PartitionArgs a) {
   // ahead (the first step's before q), so the loads of dropped latent
   // pieces can be left out.
   Step<LT, R, G> cur;
-  float inx[Gm::kU];
+  float inx = 0.f;  // the next step's importance score of this lane's row
   const bool drop = kAd && ad.keep == 0;
-  if constexpr (kAd) load_imp<LT, R, G>(cb0, slot, rimp, inx);
+  if constexpr (kAd) inx = load_imp<LT, R, G>(cb0, rimp);
   prologue<R, G, kValuAfter>(a, b, hg, g, q_lds, qt_lds, [&]() {
-    load_step<LT, R, G, kAux, kAd>(cur, cb0, slot, lane_off, rk, rv, rsk, rsv, inx, ad.thr, drop);
-    if constexpr (kAd) load_imp<LT, R, G>(cb0 + kStride, slot, rimp, inx);
+    const uint64_t low = kAd ? low_mask<LT, R, G>(inx, ad.thr) : 0;
+    load_step<LT, R, G, kAux, kAd>(cur, cb0, slot, lane_off, rk, rv, rsk, rsv, low, drop);
+    if constexpr (kAd) inx = load_imp<LT, R, G>(cb0 + kStride, rimp);
   });
 
   QtView<LT, R, G> qt;
@@ -904,8 +909,8 @@ void partition_kernel(PartitionArgs a) {
         compute_step<LT, R, G, false, kAd>(cur, cb, ntok, slot, qt, m, l, acc, ad);
       else
         compute_step<LT, R, G, true, kAd>(cur, cb, ntok, slot, qt, m, l, acc, ad);
-      load_step<LT, R, G, kAux, kAd>(cur, cb + kStride, slot, lane_off, rk, rv, rsk, rsv, inx,
-                                     ad.thr, drop);
+      load_step<LT, R, G, kAux, kAd>(cur, cb + kStride, slot, lane_off, rk, rv, rsk, rsv, 0,
+                                     drop);
     }
   } else {
     // rounds of the four waves, the same count in every wave so that the
@@ -920,9 +925,10 @@ void partition_kernel(PartitionArgs a) {
         compute_step<LT, R, G, false, kAd>(cur, cb, ntok, slot, qt, m, l, acc, ad);
       else if (cb < ntok)
         compute_step<LT, R, G, true, kAd>(cur, cb, ntok, slot, qt, m, l, acc, ad);
-      load_step<LT, R, G, kAux, kAd>(cur, cb + kStride, slot, lane_off, rk, rv, rsk, rsv, inx,
-                                     ad.thr, drop);
-      load_imp<LT, R, G>(cb + 2 * kStride, slot, rimp, inx);
+      const uint64_t low = low_mask<LT, R, G>(inx, ad.thr);
+      load_step<LT, R, G, kAux, kAd>(cur, cb + kStride, slot, lane_off, rk, rv, rsk, rsv, low,
+                                     drop);
+      inx = load_imp<LT, R, G>(cb + 2 * kStride, rimp);
       if ((r + 1) % kRPC == 0 || r + 1 == nround) {
         const int c0 = (r / kRPC) * kLg;
         __syncthreads();  // the chunk's rows are in LDS
